@@ -1,0 +1,196 @@
+"""ctypes binding of libqlora.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (see
+include/qlora.h for the contract).  Tensors are torch tensors on the GPU; the
+binding checks dtype/contiguity/device, allocates missing outputs with torch,
+passes raw pointers and the current HIP stream, and raises QloraError on a
+non-zero status.  All computation happens in the HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora.so")
+_lib = None
+
+QL_F32, QL_BF16 = 0, 1
+STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_DTYPE", -4: "QL_ERR_ALIGN",
+          -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_HIP"}
+EXPORTS = ("nf4_quantize", "nf4_double_quant", "nf4_dequantize", "qlora_linear_fwd_workspace",
+           "qlora_linear_fwd", "qlora_linear_bwd_workspace", "qlora_linear_bwd", "qlora_nf4_levels",
+           "ql_status_string")
+
+
+class QloraError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({lib().ql_status_string(status).decode()})")
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m bit_quantized_lora_blockwise_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I64, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        sig = {
+            "nf4_quantize": ([P, I32, I64, I64, P, P, P], I32),
+            "nf4_double_quant": ([P, I64, P, P, P], I32),
+            "nf4_dequantize": ([P, P, P, I64, I64, P, P], I32),
+            "qlora_linear_fwd_workspace": ([I64, I64, I64, I32], SZ),
+            "qlora_linear_fwd": ([P, I64, I64, I64, P, P, P, P, P, I32, F32, P, P, P, SZ, P], I32),
+            "qlora_linear_bwd_workspace": ([I64, I64, I64, I32], SZ),
+            "qlora_linear_bwd": ([P, P, I64, I64, I64, P, P, P, P, P, I32, F32, P, P, P, P, P, SZ, P], I32),
+            "qlora_nf4_levels": ([P], I32),
+            "ql_status_string": ([I32], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes, f.restype = args, res
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    return t
+
+
+def _check(fn, status):
+    if status != 0:
+        raise QloraError(fn, status)
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def nf4_quantize(W, codes=None, absmax=None, stream=None):
+    """Packed NF4 codes [rows, cols/2] (uint8) and fp32 absmax [rows*cols/64] of W [rows, cols]."""
+    if W.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("W must be float32 or bfloat16")
+    _need(W, "W", W.dtype, 2)
+    rows, cols = W.shape
+    codes = _empty((rows, cols // 2), torch.uint8, W) if codes is None else _need(codes, "codes", torch.uint8)
+    absmax = _empty((rows * cols // 64,), torch.float32, W) if absmax is None else _need(absmax, "absmax",
+                                                                                        torch.float32)
+    _check("nf4_quantize", lib().nf4_quantize(_ptr(W), QL_BF16 if W.dtype == torch.bfloat16 else QL_F32, rows, cols,
+                                              _ptr(codes), _ptr(absmax), _stream(stream)))
+    return codes, absmax
+
+
+def nf4_double_quant(absmax, c2=None, c1=None, stream=None):
+    """E4M3FN codes c2 [n_blocks] (uint8) and fp32 group scales c1 [ceil(n_blocks/256)]."""
+    _need(absmax, "absmax", torch.float32)
+    nb = absmax.numel()
+    c2 = _empty((nb,), torch.uint8, absmax) if c2 is None else _need(c2, "c2", torch.uint8)
+    c1 = _empty(((nb + 255) // 256,), torch.float32, absmax) if c1 is None else _need(c1, "c1", torch.float32)
+    _check("nf4_double_quant", lib().nf4_double_quant(_ptr(absmax), nb, _ptr(c2), _ptr(c1), _stream(stream)))
+    return c2, c1
+
+
+def nf4_dequantize(codes, c2, c1, rows, cols, out=None, stream=None):
+    """Bit-exact bf16 doubleDequant(c1, c2, W_NF4) [rows, cols]."""
+    _need(codes, "codes", torch.uint8); _need(c2, "c2", torch.uint8); _need(c1, "c1", torch.float32)
+    out = _empty((rows, cols), torch.bfloat16, codes) if out is None else _need(out, "out", torch.bfloat16)
+    _check("nf4_dequantize", lib().nf4_dequantize(_ptr(codes), _ptr(c2), _ptr(c1), rows, cols, _ptr(out),
+                                                  _stream(stream)))
+    return out
+
+
+def qlora_linear_fwd_workspace(M, K, N, r):
+    return int(lib().qlora_linear_fwd_workspace(M, K, N, r))
+
+
+def qlora_linear_bwd_workspace(M, K, N, r):
+    return int(lib().qlora_linear_bwd_workspace(M, K, N, r))
+
+
+def _workspace(nbytes, like, workspace):
+    if workspace is not None:
+        return _need(workspace, "workspace", torch.uint8)
+    return torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=like.device)
+
+
+def qlora_linear_fwd(X, codes, c2, c1, N, L1, L2, lora_scale=1.0, Y=None, T_out=None, workspace=None,
+                     stream=None):
+    """Y = bf16(X W'^T + s T L2), T = bf16(X L1).  Returns (Y, T_out or None).
+
+    T_out: None (not returned), True (allocated here) or a bf16 [M, r] tensor."""
+    _need(X, "X", torch.bfloat16, 2); _need(L1, "L1", torch.bfloat16, 2); _need(L2, "L2", torch.bfloat16, 2)
+    _need(codes, "codes", torch.uint8); _need(c2, "c2", torch.uint8); _need(c1, "c1", torch.float32)
+    M, K = X.shape
+    r = L1.shape[1]
+    Y = _empty((M, N), torch.bfloat16, X) if Y is None else _need(Y, "Y", torch.bfloat16)
+    if T_out is True:
+        T_out = _empty((M, r), torch.bfloat16, X)
+    elif T_out is not None:
+        _need(T_out, "T_out", torch.bfloat16)
+    ws = _workspace(qlora_linear_fwd_workspace(M, K, N, r), X, workspace)
+    _check("qlora_linear_fwd", lib().qlora_linear_fwd(
+        _ptr(X), M, K, N, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(L1), _ptr(L2), r, float(lora_scale),
+        _ptr(Y), _ptr(T_out), _ptr(ws), ws.numel(), _stream(stream)))
+    return Y, T_out
+
+
+def qlora_linear_bwd(X, dY, codes, c2, c1, L1, L2, lora_scale=1.0, T=None, dX=True, dL1=None, dL2=None,
+                     workspace=None, stream=None):
+    """(dX or None, dL1 fp32 [K, r], dL2 fp32 [r, N]); the frozen base gets no gradient.
+
+    dX: True (allocated here), False/None (skipped) or a bf16 [M, K] tensor."""
+    _need(X, "X", torch.bfloat16, 2); _need(dY, "dY", torch.bfloat16, 2)
+    _need(L1, "L1", torch.bfloat16, 2); _need(L2, "L2", torch.bfloat16, 2)
+    _need(codes, "codes", torch.uint8); _need(c2, "c2", torch.uint8); _need(c1, "c1", torch.float32)
+    M, K = X.shape
+    N = dY.shape[1]
+    r = L1.shape[1]
+    if T is not None:
+        _need(T, "T", torch.bfloat16)
+    if dX is True:
+        dX = _empty((M, K), torch.bfloat16, X)
+    elif dX is False:
+        dX = None
+    elif dX is not None:
+        _need(dX, "dX", torch.bfloat16)
+    dL1 = _empty((K, r), torch.float32, X) if dL1 is None else _need(dL1, "dL1", torch.float32)
+    dL2 = _empty((r, N), torch.float32, X) if dL2 is None else _need(dL2, "dL2", torch.float32)
+    ws = _workspace(qlora_linear_bwd_workspace(M, K, N, r), X, workspace)
+    _check("qlora_linear_bwd", lib().qlora_linear_bwd(
+        _ptr(X), _ptr(dY), M, K, N, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(L1), _ptr(L2), r, float(lora_scale),
+        _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(ws), ws.numel(), _stream(stream)))
+    return dX, dL1, dL2
+
+
+def qlora_nf4_levels():
+    """The 16 fp32 NF4 levels compiled into the library (host call, no GPU)."""
+    buf = (ctypes.c_float * 16)()
+    _check("qlora_nf4_levels", lib().qlora_nf4_levels(ctypes.cast(buf, ctypes.c_void_p)))
+    return [float(v) for v in buf]
+
+
+def ql_status_string(status):
+    return lib().ql_status_string(int(status)).decode()

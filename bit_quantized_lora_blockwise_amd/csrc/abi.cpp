@@ -1,0 +1,182 @@
+// C ABI of libqlora.so: argument checks, workspace sizing and kernel dispatch.
+// Declarations and the contract of each entry point are in include/qlora.h.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/qlora.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local hipError_t g_last_hip = hipSuccess;
+thread_local char g_msg[256];
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return QL_OK;
+  g_last_hip = e;
+  return QL_ERR_HIP;
+}
+
+#define QL_TRY(expr)                       \
+  do {                                     \
+    hipError_t e_ = (expr);                \
+    if (e_ != hipSuccess) return hip_status(e_); \
+  } while (0)
+
+bool shapes_ok(int64_t M, int64_t K, int64_t N, int r) {
+  return M > 0 && K > 0 && N > 0 && (K % 64) == 0 && r >= 1 && r <= 64 &&
+         M <= (int64_t(1) << 31) && K <= (int64_t(1) << 31) && N <= (int64_t(1) << 31);
+}
+
+// Workspace layout of the forward: [T (M x r bf16) when the caller gives no T_out][fp32 partials].
+struct FwdWs {
+  size_t t_bytes, part_bytes, total;
+};
+FwdWs fwd_ws(int64_t M, int64_t K, int64_t N, int r) {
+  (void)N;
+  FwdWs w;
+  w.t_bytes = round_up((size_t)M * r * 2);
+  w.part_bytes = round_up(lora_skinny_ws(M, K, r));
+  w.total = w.t_bytes + w.part_bytes;
+  return w;
+}
+
+// Backward: [T (recomputed when NULL)][G (M x r bf16)][fp32 partials, reused by each step].
+struct BwdWs {
+  size_t t_bytes, g_bytes, part_bytes, total;
+};
+BwdWs bwd_ws(int64_t M, int64_t K, int64_t N, int r) {
+  BwdWs w;
+  w.t_bytes = round_up((size_t)M * r * 2);
+  w.g_bytes = round_up((size_t)M * r * 2);
+  size_t p = lora_skinny_ws(M, K, r);
+  p = std::max(p, lora_skinny_ws(M, N, r));
+  p = std::max(p, lora_tn_ws(M, K, r));
+  p = std::max(p, lora_tn_ws(M, N, r));
+  w.part_bytes = round_up(p);
+  w.total = w.t_bytes + w.g_bytes + w.part_bytes;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nf4_quantize(const void* W, int w_dtype, int64_t rows, int64_t cols, uint8_t* codes, float* absmax,
+                 void* stream) {
+  if (!W || !codes || !absmax) return QL_ERR_NULL;
+  if (w_dtype != QL_F32 && w_dtype != QL_BF16) return QL_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || cols % 64 != 0 || rows > (int64_t(1) << 40) / cols) return QL_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax)) return QL_ERR_ALIGN;
+  QL_TRY(launch_nf4_encode(W, w_dtype == QL_BF16, rows * cols, codes, absmax, (hipStream_t)stream));
+  return QL_OK;
+}
+
+int nf4_double_quant(const float* absmax, int64_t n_blocks, uint8_t* c2, float* c1, void* stream) {
+  if (!absmax || !c2 || !c1) return QL_ERR_NULL;
+  if (n_blocks <= 0 || n_blocks > (int64_t(1) << 36)) return QL_ERR_SHAPE;
+  if (!aligned16(absmax) || !aligned16(c2) || !aligned16(c1)) return QL_ERR_ALIGN;
+  QL_TRY(launch_double_quant(absmax, n_blocks, c2, c1, (hipStream_t)stream));
+  return QL_OK;
+}
+
+int nf4_dequantize(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t rows, int64_t cols,
+                   uint16_t* W_bf16, void* stream) {
+  if (!codes || !c2 || !c1 || !W_bf16) return QL_ERR_NULL;
+  if (rows <= 0 || cols <= 0 || cols % 64 != 0 || rows > (int64_t(1) << 40) / cols) return QL_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(c2) || !aligned16(c1) || !aligned16(W_bf16)) return QL_ERR_ALIGN;
+  QL_TRY(launch_dequant(codes, c2, c1, rows * cols, W_bf16, (hipStream_t)stream));
+  return QL_OK;
+}
+
+size_t qlora_linear_fwd_workspace(int64_t M, int64_t K, int64_t N, int r) {
+  if (!shapes_ok(M, K, N, r)) return 0;
+  return fwd_ws(M, K, N, r).total;
+}
+
+int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes, const uint8_t* c2,
+                     const float* c1, const uint16_t* L1, const uint16_t* L2, int r, float lora_scale, uint16_t* Y,
+                     uint16_t* T_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!X || !codes || !c2 || !c1 || !L1 || !L2 || !Y) return QL_ERR_NULL;
+  if (!shapes_ok(M, K, N, r)) return QL_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(codes) || !aligned16(c2) || !aligned16(c1) || !aligned16(L1) ||
+      !aligned16(L2) || !aligned16(Y) || (T_out && !aligned16(T_out)))
+    return QL_ERR_ALIGN;
+  const FwdWs w = fwd_ws(M, K, N, r);
+  if (!workspace || ws_bytes < w.total) return QL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  uint16_t* T = T_out ? T_out : (uint16_t*)ws;
+  float* part = (float*)(ws + w.t_bytes);
+  QL_TRY(launch_lora_skinny(X, M, K, L1, true, r, 1.0f, T, part, s));
+  if (M <= 16)
+    QL_TRY(launch_qgemv_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
+  else
+    QL_TRY(launch_qgemm_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
+  return QL_OK;
+}
+
+size_t qlora_linear_bwd_workspace(int64_t M, int64_t K, int64_t N, int r) {
+  if (!shapes_ok(M, K, N, r)) return 0;
+  return bwd_ws(M, K, N, r).total;
+}
+
+int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                     const uint8_t* c2, const float* c1, const uint16_t* L1, const uint16_t* L2, int r,
+                     float lora_scale, const uint16_t* T, uint16_t* dX, float* dL1, float* dL2, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  if (!X || !dY || !codes || !c2 || !c1 || !L1 || !L2 || !dL1 || !dL2) return QL_ERR_NULL;
+  if (!shapes_ok(M, K, N, r)) return QL_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(codes) || !aligned16(c2) || !aligned16(c1) ||
+      !aligned16(L1) || !aligned16(L2) || !aligned16(dL1) || !aligned16(dL2) || (T && !aligned16(T)) ||
+      (dX && !aligned16(dX)))
+    return QL_ERR_ALIGN;
+  const BwdWs w = bwd_ws(M, K, N, r);
+  if (!workspace || ws_bytes < w.total) return QL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  uint16_t* Tw = (uint16_t*)ws;
+  uint16_t* G = (uint16_t*)(ws + w.t_bytes);
+  float* part = (float*)(ws + w.t_bytes + w.g_bytes);
+  if (!T) {
+    QL_TRY(launch_lora_skinny(X, M, K, L1, true, r, 1.0f, Tw, part, s));
+    T = Tw;
+  }
+  QL_TRY(launch_lora_skinny(dY, M, N, L2, false, r, lora_scale, G, part, s));
+  if (dX) QL_TRY(launch_qgemm_dx(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s));
+  QL_TRY(launch_lora_tn(X, G, M, K, r, 1.0f, false, dL1, part, s));
+  QL_TRY(launch_lora_tn(dY, T, M, N, r, lora_scale, true, dL2, part, s));
+  return QL_OK;
+}
+
+int qlora_nf4_levels(float* out16) {
+  if (!out16) return QL_ERR_NULL;
+  std::memcpy(out16, nf4_params().q, 16 * sizeof(float));
+  return QL_OK;
+}
+
+const char* ql_status_string(int status) {
+  switch (status) {
+    case QL_OK: return "ok";
+    case QL_ERR_NULL: return "a required pointer is NULL";
+    case QL_ERR_SHAPE: return "invalid shape (sizes must be > 0, K and cols multiples of 64, 1 <= r <= 64)";
+    case QL_ERR_DTYPE: return "unsupported dtype code";
+    case QL_ERR_ALIGN: return "device pointers must be 16-byte aligned";
+    case QL_ERR_WORKSPACE: return "workspace missing or smaller than the size query returns";
+    case QL_ERR_HIP:
+      std::snprintf(g_msg, sizeof g_msg, "HIP launch failed: %s", hipGetErrorString(g_last_hip));
+      return g_msg;
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

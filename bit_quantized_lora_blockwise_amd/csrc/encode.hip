@@ -1,0 +1,170 @@
+// NF4 blockwise-absmax encoder, double quantization of the block scales and
+// the bit-exact dequantizer.
+//
+// Method: nlp-lineage milestone page on QLoRA, section "The idea" (NF4 bullet
+// and double-quantisation bullet); inferensys glossary entry "QLoRA",
+// double-quantization paragraph (scales quantised to 8-bit floats).
+#include "kernels.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t dpp_max8(uint32_t v) {
+  // max over aligned groups of 8 lanes: swap neighbours, swap pairs, mirror halves of 8
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return v;
+}
+
+// One thread encodes 8 consecutive weights; the 8 lanes of an aligned group
+// cover one block of 64 and share its absmax through DPP.  Codes of the 8
+// weights form one 32-bit word (element j in bits 4j..4j+3).
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict__ W, int64_t n_oct,
+                                                         uint32_t* __restrict__ codes,
+                                                         float* __restrict__ absmax, Nf4Params p) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t o = (int64_t)blockIdx.x * kThreads + threadIdx.x; o < n_oct; o += stride) {
+    float w[8];
+    if (kBf16) {
+      u32x4 v = __builtin_nontemporal_load((const u32x4*)W + o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[2 * j] = __uint_as_float(v[j] << 16);
+        w[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
+      }
+    } else {
+      u32x4 v0 = __builtin_nontemporal_load((const u32x4*)W + 2 * o);
+      u32x4 v1 = __builtin_nontemporal_load((const u32x4*)W + 2 * o + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[j] = __uint_as_float(v0[j]);
+        w[4 + j] = __uint_as_float(v1[j]);
+      }
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(w[j]) & 0x7FFFFFFFu);
+    m = dpp_max8(m);
+    const float a = __uint_as_float(m);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float n = (m == 0) ? 0.0f : w[j] / a;  // correctly rounded fp32 division
+      uint32_t c = 0;
+#pragma unroll
+      for (int k = 0; k < 15; ++k) c += (n >= p.thr[k]) ? 1u : 0u;
+      packed |= c << (4 * j);
+    }
+    codes[o] = packed;
+    if ((threadIdx.x & 7) == 0) absmax[o >> 3] = a;
+  }
+}
+
+// Nearest OCP E4M3FN code of t in [0, 448], ties to even.  Below 2^-6 the
+// format is fixed-point with step 2^-9, so the code is rint(t * 512); above,
+// the fp32 mantissa is rounded to 3 bits and the exponent rebased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3fn_encode(float t) {
+  if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  return (r >> 20) - (120u << 3);
+}
+
+// One wavefront per group of 256 scales; lane l owns scales 4l..4l+3.
+__global__ __launch_bounds__(kThreads) void k_double_quant(const float* __restrict__ absmax, int64_t nb,
+                                                           uint8_t* __restrict__ c2, float* __restrict__ c1,
+                                                           int64_t ngroups) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); g < ngroups; g += wstride) {
+    const int64_t base = g * qk::kGroup + 4 * lane;
+    float v[4];
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = (base + j < nb) ? absmax[base + j] : 0.0f;
+      m = max(m, __float_as_uint(v[j]));
+    }
+    m = qk::wave_max_u32(m);
+    const float cmax = __uint_as_float(m);
+    if (lane == 0) c1[g] = cmax;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float t = (m == 0) ? 0.0f : v[j] / cmax;
+      packed |= e4m3fn_encode(t) << (8 * j);
+    }
+    if (base + 4 <= nb) {
+      *(uint32_t*)(c2 + base) = packed;
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (base + j < nb) c2[base + j] = (uint8_t)(packed >> (8 * j));
+    }
+  }
+}
+
+// W'[e] = bf16(fl32(q[code_e] * s'_b)), s'_b = fl32(dec(c2_b) * c1_{b/256}).
+// One thread per 8 elements (one 32-bit word of codes -> 16 bytes of bf16).
+__global__ __launch_bounds__(kThreads) void k_dequant(const uint32_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ c2,
+                                                      const float* __restrict__ c1, int64_t n_oct,
+                                                      u32x4* __restrict__ out, Nf4Params p) {
+  __shared__ float q[16];
+  if (threadIdx.x < 16) q[threadIdx.x] = p.q[threadIdx.x];
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t o = (int64_t)blockIdx.x * kThreads + threadIdx.x; o < n_oct; o += stride) {
+    const int64_t b = o >> 3;
+    const float s = qk::e4m3fn_to_f32(c2[b]) * c1[b >> 8];
+    const uint32_t cw = codes[o];
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = q[(cw >> (8 * j)) & 15] * s;
+      const float hi = q[(cw >> (8 * j + 4)) & 15] * s;
+      r[j] = qk::pack_bf16x2(lo, hi);
+    }
+    out[o] = r;
+  }
+}
+
+int grid_for(int64_t items, int per_block) {
+  int64_t g = (items + per_block - 1) / per_block;
+  if (g > 8192) g = 8192;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_nf4_encode(const void* W, bool bf16, int64_t elems, uint8_t* codes, float* absmax,
+                             hipStream_t s) {
+  const int64_t n_oct = elems / 8;
+  const int grid = grid_for(n_oct, kThreads);
+  if (bf16)
+    hipLaunchKernelGGL(k_nf4_encode<true>, dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes, absmax,
+                       nf4_params());
+  else
+    hipLaunchKernelGGL(k_nf4_encode<false>, dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes, absmax,
+                       nf4_params());
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant(const float* absmax, int64_t n_blocks, uint8_t* c2, float* c1, hipStream_t s) {
+  const int64_t ngroups = (n_blocks + qk::kGroup - 1) / qk::kGroup;
+  const int grid = grid_for(ngroups, kThreads / 64);
+  hipLaunchKernelGGL(k_double_quant, dim3(grid), dim3(kThreads), 0, s, absmax, n_blocks, c2, c1, ngroups);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t elems, uint16_t* out,
+                          hipStream_t s) {
+  const int64_t n_oct = elems / 8;
+  const int grid = grid_for(n_oct, kThreads);
+  hipLaunchKernelGGL(k_dequant, dim3(grid), dim3(kThreads), 0, s, (const uint32_t*)codes, c2, c1, n_oct,
+                     (u32x4*)out, nf4_params());
+  return hipGetLastError();
+}

@@ -1,0 +1,53 @@
+// Internal launcher interface between the C ABI (abi.cpp) and the kernels.
+// Every launcher enqueues on `s` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+const Nf4Params& nf4_params();
+
+// --- encoder (encode.hip) ---------------------------------------------------
+hipError_t launch_nf4_encode(const void* W, bool bf16, int64_t elems, uint8_t* codes, float* absmax,
+                             hipStream_t s);
+hipError_t launch_double_quant(const float* absmax, int64_t n_blocks, uint8_t* c2, float* c1, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t elems,
+                          uint16_t* out, hipStream_t s);
+
+// --- skinny LoRA products (lora.hip) -----------------------------------------
+// Split plan of a reduction of length R over tiles of `tiles` outputs.
+struct SplitPlan {
+  int splits;      // number of reduction slices
+  int64_t chunk;   // reduction length per slice (multiple of 64)
+};
+SplitPlan plan_rowsplit(int64_t tiles, int64_t R);
+
+// C[M, r] = A[M, R] * B, B(k, c) = L1[k][c] (b_rmajor_kr = true, L1 is [R, r])
+// or B(k, c) = L2[c][k] (false, L2 is [r, R]).  Result scaled by `scale`,
+// rounded to bf16 into out[M, r].  ws holds the fp32 partials.
+size_t lora_skinny_ws(int64_t M, int64_t R, int r);
+hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, const uint16_t* B, bool b_is_kr, int r,
+                              float scale, uint16_t* out, float* ws, hipStream_t s);
+
+// C[p, c] = scale * sum_m A[m][p] * B[m][c] with A [M, P], B [M, r]; stored as
+// out[P, r] (transpose_out = false) or out[r, P] (true), fp32.
+size_t lora_tn_ws(int64_t M, int64_t P, int r);
+hipError_t launch_lora_tn(const uint16_t* A, const uint16_t* B, int64_t M, int64_t P, int r, float scale,
+                          bool transpose_out, float* out, float* ws, hipStream_t s);
+
+// --- quantised GEMMs (gemm.hip, decode.hip) ----------------------------------
+// Y[M, N] = bf16(X W'^T + scale * T L2)
+hipError_t launch_qgemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                            const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
+                            float scale, uint16_t* Y, hipStream_t s);
+// Same result for small M (M <= 16), streaming the packed weight once.
+hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                            const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
+                            float scale, uint16_t* Y, hipStream_t s);
+// dX[M, K] = bf16(dY W' + G L1^T)
+hipError_t launch_qgemm_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                           const uint8_t* c2, const float* c1, const uint16_t* G, const uint16_t* L1, int r,
+                           uint16_t* dX, hipStream_t s);

@@ -1,0 +1,141 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) QLoRA hot-path library (libqlora.so).
+ *
+ * What the library computes (sources: web pages on QLoRA, cited by page and
+ * section):
+ *   - nlp-lineage milestone page on QLoRA (2023), section "The idea": the NF4
+ *     bullet (16 levels placed at equal shares of a normal distribution, with
+ *     an exact zero), the double-quantisation bullet (blocks of 64 with a
+ *     32-bit scale each, those scales quantised again to 8 bits), and the
+ *     notation paragraph (Y = X doubleDequant(c1, c2, W_NF4) + X L1 L2, bf16
+ *     adapters, only L1 and L2 receive gradients).
+ *   - inferensys glossary entry "QLoRA": the double-quantization paragraph
+ *     (the scales become 8-bit floats) and the frozen-base paragraph (gradients
+ *     pass through the 4-bit weights but only the adapters are updated).
+ *   - examadda page "QLoRA (Quantized LoRA)", "The Core Idea" (the base is
+ *     quantised once and dequantised on the fly) and "Practical Notes" (bf16
+ *     compute).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *     The library never allocates, frees or synchronises, and keeps no mutable
+ *     global state; all work is enqueued on `stream` (a hipStream_t passed as
+ *     void*, NULL = the null stream) and completes asynchronously.
+ *   - bf16 tensors are passed as uint16_t bit patterns. All matrices are dense
+ *     row-major with no padding.
+ *   - The weight is stored out x in: W[N, K] row-major. First-level blocks are
+ *     64 consecutive elements of the flat matrix (so they run along K and K
+ *     must be a multiple of 64). Codes are packed two per byte, the element
+ *     with the even flat index in the low nibble. Code k means NF4 level k in
+ *     ascending order (code 7 is 0.0, code 0 is -1.0, code 15 is +1.0).
+ *   - Second level: groups of 256 consecutive first-level scales; c2 holds one
+ *     OCP FP8 E4M3FN byte per block, c1 one fp32 per group (the last group may
+ *     be partial).
+ *   - Device pointers must be 16-byte aligned.
+ *   - Return value: QL_OK (0) or a negative ql_status. Arguments are checked on
+ *     the host before anything is enqueued: for every status except
+ *     QL_ERR_HIP nothing has been enqueued and no output is written. QL_ERR_HIP
+ *     means a kernel launch was refused; launches of the same call that came
+ *     before it may already be enqueued, and the outputs are unspecified.
+ *     Device faults are asynchronous and surface at the caller's next
+ *     synchronisation. No C++ exception crosses this interface.
+ *   - Inputs must be finite; for non-finite weights the outputs are
+ *     unspecified.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QL_OK = 0,
+  QL_ERR_NULL = -1,      /* a required pointer is NULL                            */
+  QL_ERR_SHAPE = -2,     /* a size is <= 0, K % 64 != 0, r outside [1, 64], ...   */
+  QL_ERR_DTYPE = -3,     /* unsupported dtype code                                */
+  QL_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned               */
+  QL_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the query returns      */
+  QL_ERR_HIP = -6        /* a HIP launch failed (see ql_status_string)            */
+} ql_status;
+
+enum { QL_F32 = 0, QL_BF16 = 1 };
+
+/* First quantisation level (nlp-lineage page, "The idea", NF4 and
+ * double-quantisation bullets).
+ * W [rows, cols] (fp32 or bf16 per w_dtype), cols % 64 == 0.
+ * For every block b of 64 consecutive elements: absmax[b] = max |w| (exact, fp32);
+ * every element is normalised n = fl32(w / absmax[b]) (correctly rounded fp32
+ * division; an all-zero block gives n = 0) and replaced by the code of the
+ * nearest NF4 level (an exact tie between two levels takes the smaller code).
+ * Outputs: codes [rows * cols / 2] bytes, absmax [rows * cols / 64] fp32.      */
+int nf4_quantize(const void* W, int w_dtype, int64_t rows, int64_t cols,
+                 uint8_t* codes, float* absmax, void* stream);
+
+/* Second quantisation level ("double quantization": inferensys glossary,
+ * double-quantization paragraph; nlp-lineage page, double-quantisation bullet).
+ * absmax [n_blocks] fp32 >= 0. For every group g of 256 consecutive scales:
+ * c1[g] = max of the group; c2[b] = E4M3FN code of fl32(absmax[b] / c1[g]),
+ * rounded to nearest, ties to even (0 when c1[g] == 0).
+ * Outputs: c2 [n_blocks] bytes, c1 [ceil(n_blocks / 256)] fp32.                 */
+int nf4_double_quant(const float* absmax, int64_t n_blocks,
+                     uint8_t* c2, float* c1, void* stream);
+
+/* doubleDequant(c1, c2, W_NF4) written out as bf16 (nlp-lineage page, notation
+ * paragraph): s'_b = fl32(dec(c2[b]) * c1[b / 256]); W'[e] = bf16(fl32(q[code_e] * s'_b)),
+ * both roundings to nearest-even. Output W_bf16 [rows, cols]. This is the exact
+ * weight that the linear-layer entry points multiply with; it is provided for
+ * checking, merging and debugging (the layer kernels never store it).          */
+int nf4_dequantize(const uint8_t* codes, const uint8_t* c2, const float* c1,
+                   int64_t rows, int64_t cols, uint16_t* W_bf16, void* stream);
+
+/* Workspace (bytes) that qlora_linear_fwd needs for these sizes.               */
+size_t qlora_linear_fwd_workspace(int64_t M, int64_t K, int64_t N, int r);
+
+/* Forward of one quantised LoRA linear (nlp-lineage page, notation paragraph):
+ *   T = bf16(X L1),  Y = bf16(X W'^T + lora_scale * (T L2)),
+ * fp32 accumulation, W' as in nf4_dequantize (never materialised).
+ * X [M, K] bf16; codes/c2/c1 describe W [N, K]; L1 [K, r] bf16; L2 [r, N] bf16;
+ * 1 <= r <= 64. Outputs: Y [M, N] bf16; T_out [M, r] bf16 when non-NULL (keep it
+ * for the backward). workspace: ws_bytes >= qlora_linear_fwd_workspace(...),
+ * contents need no initialisation and are clobbered.                          */
+int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                     const uint8_t* codes, const uint8_t* c2, const float* c1,
+                     const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
+                     uint16_t* Y, uint16_t* T_out,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace (bytes) that qlora_linear_bwd needs for these sizes.               */
+size_t qlora_linear_bwd_workspace(int64_t M, int64_t K, int64_t N, int r);
+
+/* Backward of one quantised LoRA linear. The frozen 4-bit base receives no
+ * gradient: there is no dW argument (nlp-lineage page, notation paragraph;
+ * inferensys glossary, frozen-base paragraph; examadda page, "The Flow").
+ *   G   = bf16(lora_scale * dY L2^T)          [M, r]
+ *   dX  = bf16(dY W' + G L1^T)                [M, K]   (skipped when dX == NULL)
+ *   dL1 = fp32(X^T G)                         [K, r]
+ *   dL2 = fp32(lora_scale * T^T dY)           [r, N]
+ * T [M, r] bf16 is the forward's T_out; when NULL it is recomputed from X and L1
+ * (gradient-checkpointing style). dY [M, N] bf16. Shapes and workspace as in
+ * the forward; ws_bytes >= qlora_linear_bwd_workspace(...).                     */
+int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K, int64_t N,
+                     const uint8_t* codes, const uint8_t* c2, const float* c1,
+                     const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
+                     const uint16_t* T, uint16_t* dX, float* dL1, float* dL2,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Host-only helpers (no GPU needed). */
+/* The 16 NF4 levels (fp32, ascending) that the kernels use, copied to out[16].  */
+int qlora_nf4_levels(float* out16);
+/* Static description of a status code (and of the last HIP error on this
+ * thread for QL_ERR_HIP).                                                       */
+const char* ql_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

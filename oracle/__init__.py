@@ -9,5 +9,6 @@ from .qlora_oracle import (  # noqa: F401
     nf4_levels, nf4_levels_f64, nf4_midpoints, nf4_nearest_code,
     e4m3fn_decode, e4m3fn_encode,
     nf4_quantize, unpack_codes, nf4_double_quant, block_scales, nf4_dequantize,
+    dequantize_blocks, nf4_dequantize_rows, nf4_dequantize_colblock,
     qlora_forward, qlora_backward, bits_per_weight,
 )

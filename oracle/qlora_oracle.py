@@ -240,14 +240,44 @@ def block_scales(c2, c1) -> np.ndarray:
     return fp32(e4m3fn_decode(c2) * c1[g].astype(np.float64))     # product exact in float64
 
 
-def nf4_dequantize(codes, c2, c1, rows: int, cols: int) -> np.ndarray:
-    """doubleDequant(c1, c2, W_NF4) as bf16 bit patterns [rows, cols]:
-    W'_e = bf16(fl32(q[code_e] * s'_b))."""
+def dequantize_blocks(block_codes, c2_b, c1_b) -> np.ndarray:
+    """Dequantize a set of blocks: block_codes [nb, 64] unpacked codes, with each
+    block's own c2 byte and c1 group scale.  Returns bf16 bits [nb, 64]:
+    s'_b = fl32(dec(c2_b) * c1_b); W'_e = bf16(fl32(q[code_e] * s'_b))."""
     q = nf4_levels().astype(np.float64)
+    d = e4m3fn_decode(np.asarray(c2_b, dtype=np.uint8).reshape(-1))
+    s = fp32(d * np.asarray(c1_b, dtype=np.float32).reshape(-1).astype(np.float64)).astype(np.float64)
+    w = fp32(q[np.asarray(block_codes)] * s[:, None])                # exact product, one fp32 rounding
+    return bf16_bits(w)
+
+
+def nf4_dequantize(codes, c2, c1, rows: int, cols: int) -> np.ndarray:
+    """doubleDequant(c1, c2, W_NF4) as bf16 bit patterns [rows, cols]."""
     c = unpack_codes(np.asarray(codes, dtype=np.uint8).reshape(rows, cols // 2)).reshape(-1, BLOCK)
-    s = block_scales(c2, c1).astype(np.float64)
-    w = fp32(q[c] * s[:, None])                                    # exact product, one fp32 rounding
-    return bf16_bits(w).reshape(rows, cols)
+    c2 = np.asarray(c2, dtype=np.uint8).reshape(-1)
+    c1 = np.asarray(c1, dtype=np.float32).reshape(-1)
+    return dequantize_blocks(c, c2, c1[np.arange(c2.size) // GROUP]).reshape(rows, cols)
+
+
+def nf4_dequantize_rows(codes, c2, c1, cols: int, row_idx) -> np.ndarray:
+    """Rows `row_idx` of the dequantized weight, bf16 bits [len(row_idx), cols]."""
+    codes = np.asarray(codes, dtype=np.uint8).reshape(-1, cols // 2)
+    row_idx = np.asarray(row_idx, dtype=np.int64)
+    bpr = cols // BLOCK
+    b = (row_idx[:, None] * bpr + np.arange(bpr)[None, :]).reshape(-1)
+    c = unpack_codes(codes[row_idx]).reshape(-1, BLOCK)
+    c1 = np.asarray(c1, dtype=np.float32).reshape(-1)
+    return dequantize_blocks(c, np.asarray(c2).reshape(-1)[b], c1[b // GROUP]).reshape(len(row_idx), cols)
+
+
+def nf4_dequantize_colblock(codes, c2, c1, rows: int, cols: int, kb: int) -> np.ndarray:
+    """Columns [64 kb, 64 kb + 64) of the dequantized weight, bf16 bits [rows, 64]."""
+    codes = np.asarray(codes, dtype=np.uint8).reshape(rows, cols // 2)
+    bpr = cols // BLOCK
+    b = np.arange(rows, dtype=np.int64) * bpr + kb
+    c = unpack_codes(codes[:, kb * BLOCK // 2:(kb + 1) * BLOCK // 2])
+    c1 = np.asarray(c1, dtype=np.float32).reshape(-1)
+    return dequantize_blocks(c, np.asarray(c2).reshape(-1)[b], c1[b // GROUP])
 
 
 # ----------------------------------------------------------------------------
@@ -275,19 +305,22 @@ def qlora_forward(X, Wq, L1, L2, lora_scale: float = 1.0, rnd=bf16_bits):
     return Y, T
 
 
-def qlora_backward(X, dY, Wq, L1, L2, lora_scale: float = 1.0, T=None, rnd=bf16_bits):
+def qlora_backward(X, dY, Wq, L1, L2, lora_scale: float = 1.0, T=None, rnd=bf16_bits, compute_dx=True):
     """Backward of the quantized LoRA linear; the frozen base gets no gradient.
 
     Returns (dX [M, K], dL1 [K, r] fp32, dL2 [r, N] fp32, G [M, r], T [M, r]) with
       G = rnd(s dY L2^T), dX = rnd(dY Wq + G L1^T),
       dL1 = fp32(X^T G), dL2 = fp32(s T^T dY), T = rnd(X L1) when not given.
+    With compute_dx=False, dX is None and Wq is not used (as when the caller
+    passes no dX buffer).  Columns of dX/dL1 can be restricted by passing the
+    matching columns of X, Wq and rows of L1 together with the full T.
     """
-    Xf, dYf, Wf, L1f, L2f = _f64(X), _f64(dY), _f64(Wq), _f64(L1), _f64(L2)
+    Xf, dYf, L1f, L2f = _f64(X), _f64(dY), _f64(L1), _f64(L2)
     if T is None:
         T = rnd(Xf @ L1f)
     G = rnd(lora_scale * (dYf @ L2f.T))
     Gf = _f64(G)
-    dX = rnd(dYf @ Wf + Gf @ L1f.T)
+    dX = rnd(dYf @ _f64(Wq) + Gf @ L1f.T) if compute_dx else None
     dL1 = fp32(Xf.T @ Gf)
     dL2 = fp32(lora_scale * (_f64(T).T @ dYf))
     return dX, dL1, dL2, G, T

@@ -1,0 +1,107 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+declared in include/qlora.h, carries the NF4 table the oracle derives, and
+rejects bad arguments with the documented status before touching the GPU.
+Nothing here launches a kernel (every call below fails validation first)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+pytestmark = pytest.mark.skipif(
+    not os.path.exists(os.path.join(ROOT, "bit_quantized_lora_blockwise_amd", "libqlora.so")),
+    reason="libqlora.so not built (run __graft_entry__.build())")
+
+
+def _lib():
+    import bit_quantized_lora_blockwise_amd as q
+    return q, q.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    q, L = _lib()
+    names = header_functions()
+    assert {"nf4_quantize", "nf4_double_quant", "qlora_linear_fwd", "qlora_linear_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(q.EXPORTS)
+
+
+def test_nf4_table_matches_oracle_bitwise():
+    q, _ = _lib()
+    lv = np.array(q.qlora_nf4_levels(), dtype=np.float32)
+    assert np.array_equal(lv.view(np.uint32), O.nf4_levels().view(np.uint32))
+
+
+P = ctypes.c_void_p
+A = P(4096)        # a non-null, 16-byte aligned stand-in pointer (never dereferenced)
+MIS = P(4104)      # 8-byte aligned only
+
+
+def test_quantize_validation():
+    _, L = _lib()
+    assert L.nf4_quantize(None, 0, 4, 64, A, A, None) == -1
+    assert L.nf4_quantize(A, 7, 4, 64, A, A, None) == -3
+    assert L.nf4_quantize(A, 0, 4, 65, A, A, None) == -2
+    assert L.nf4_quantize(A, 0, 0, 64, A, A, None) == -2
+    assert L.nf4_quantize(A, 1, -1, 64, A, A, None) == -2
+    assert L.nf4_quantize(MIS, 1, 4, 64, A, A, None) == -4
+    assert L.nf4_double_quant(A, 0, A, A, None) == -2
+    assert L.nf4_double_quant(A, 10, None, A, None) == -1
+    assert L.nf4_double_quant(A, 10, A, MIS, None) == -4
+    assert L.nf4_dequantize(A, A, A, 2, 96, A, None) == -2
+    assert L.nf4_dequantize(A, A, None, 2, 64, A, None) == -1
+
+
+def test_linear_validation_and_workspace():
+    _, L = _lib()
+    M, K, N, r = 32, 512, 512, 8
+    ws = L.qlora_linear_fwd_workspace(M, K, N, r)
+    assert ws > 0 and ws % 256 == 0
+    assert L.qlora_linear_fwd_workspace(M, 100, N, r) == 0
+    assert L.qlora_linear_bwd_workspace(M, K, N, 65) == 0
+    assert L.qlora_linear_bwd_workspace(M, K, N, r) >= 2 * M * r * 2
+    fwd = lambda X=A, M=M, K=K, N=N, r=r, ws_p=A, ws_b=ws, T=None: L.qlora_linear_fwd(
+        X, M, K, N, A, A, A, A, A, r, 1.0, A, T, ws_p, ws_b, None)
+    assert fwd(X=None) == -1
+    assert fwd(K=100) == -2
+    assert fwd(r=0) == -2
+    assert fwd(r=65) == -2
+    assert fwd(M=0) == -2
+    assert fwd(X=MIS) == -4
+    assert fwd(T=MIS) == -4
+    assert fwd(ws_p=None) == -5
+    assert fwd(ws_b=ws - 1) == -5
+    wsb = L.qlora_linear_bwd_workspace(M, K, N, r)
+    bwd = lambda dL1=A, ws_b=wsb, dX=None, N=N: L.qlora_linear_bwd(
+        A, A, M, K, N, A, A, A, A, A, r, 1.0, None, dX, dL1, A, A, ws_b, None)
+    assert bwd(dL1=None) == -1
+    assert bwd(N=-3) == -2
+    assert bwd(dX=MIS) == -4
+    assert bwd(ws_b=wsb - 256) == -5
+
+
+def test_status_strings():
+    q, _ = _lib()
+    for s in range(0, -7, -1):
+        assert isinstance(q.ql_status_string(s), str) and q.ql_status_string(s)
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import bit_quantized_lora_blockwise_amd._lib as B
+    monkeypatch.setattr(B, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()

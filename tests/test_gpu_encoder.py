@@ -1,0 +1,122 @@
+"""GPU parity of the encoder, double quantization and dequantizer: every code,
+scale and dequantized weight must equal the CPU oracle's bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from gpu_util import assert_bitexact, bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def gpu_encode(W_cpu):
+    import bit_quantized_lora_blockwise_amd as q
+    Wd = W_cpu.to(DEV)
+    codes, absmax = q.nf4_quantize(Wd)
+    c2, c1 = q.nf4_double_quant(absmax)
+    deq = q.nf4_dequantize(codes, c2, c1, *Wd.shape)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), absmax.cpu().numpy(), c2.cpu().numpy(), c1.cpu().numpy(), bits(deq)
+
+
+def check_encode(W_cpu, name):
+    print(f"[encoder] {name} shape={tuple(W_cpu.shape)} dtype={W_cpu.dtype}", flush=True)
+    rows, cols = W_cpu.shape
+    g_codes, g_absmax, g_c2, g_c1, g_deq = gpu_encode(W_cpu)
+    Wn = W_cpu.float().numpy()
+    r_codes, r_absmax = O.nf4_quantize(Wn)
+    r_c2, r_c1 = O.nf4_double_quant(r_absmax)
+    r_deq = O.nf4_dequantize(r_codes, r_c2, r_c1, rows, cols)
+    assert_bitexact(g_absmax.view(np.uint32), r_absmax.view(np.uint32), f"{name} absmax")
+    assert_bitexact(g_codes, r_codes, f"{name} codes")
+    assert_bitexact(g_c2, r_c2, f"{name} c2")
+    assert_bitexact(g_c1.view(np.uint32), r_c1.view(np.uint32), f"{name} c1")
+    assert_bitexact(g_deq, r_deq, f"{name} dequant")
+
+
+def test_encoder_config1_fp32():
+    check_encode(WL.config1()["W"], "512x512 fp32 N(0,0.02)")
+
+
+def test_encoder_llama7b_up_outliers_bf16():
+    check_encode(WL.weight_with_outliers(11008, 4096, 0.02, 0.001, 10.0, 10), "11008x4096 bf16 outliers")
+
+
+def test_encoder_llama65b_student_t():
+    check_encode(WL.config5_weight(0, "q", "t5"), "8192x8192 bf16 0.02*t5")
+
+
+def _edge_matrix():
+    rng = np.random.default_rng(21)
+    q = O.nf4_levels()
+    mids = O.nf4_midpoints()
+    rows = []
+    rows.append(np.zeros(256, np.float32))                                        # all-zero blocks
+    for e in (-9, -1, 3):                                                         # codebook values x 2^e
+        rows.append(np.array([q[i % 16] * 2.0 ** e for i in range(256)], np.float32))
+    r = np.zeros(256, np.float32)                                                 # adversarial near midpoints
+    for blk in range(4):
+        a = np.float32(rng.uniform(0.01, 0.2))
+        vals = [a]
+        for m in mids:
+            x = np.float32(m * float(a))
+            vals += [np.nextafter(x, np.float32(-1)), x, np.nextafter(x, np.float32(1))]
+        vals = [v for v in vals if abs(v) <= a][:64]
+        r[blk * 64:blk * 64 + len(vals)] = vals
+    rows.append(r)
+    rows.append((rng.standard_normal(256) * 1e-40).astype(np.float32))          # subnormal weights
+    neg0 = np.full(256, -0.0, np.float32)
+    neg0[::7] = rng.standard_normal(37).astype(np.float32) * 0.01
+    rows.append(neg0)                                                             # signed zeros
+    rows.append((rng.standard_normal(256) * 3e4).astype(np.float32))             # large magnitudes
+    rows.append(np.where(rng.random(256) < 0.5, 1.0, -1.0).astype(np.float32))   # +-absmax only
+    return np.stack(rows)
+
+
+def test_encoder_edge_cases_fp32():
+    check_encode(torch.from_numpy(_edge_matrix()), "edge cases fp32")
+
+
+def test_encoder_edge_cases_bf16():
+    W = torch.from_numpy(_edge_matrix()).to(torch.bfloat16)
+    check_encode(W, "edge cases bf16")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (3, 320), (5, 64 * 51), (257, 64)])
+def test_encoder_ragged_groups(rows, cols):
+    W = WL.normal((rows, cols), 0.02, rows * 1000 + cols, torch.float32)
+    check_encode(W, f"{rows}x{cols}")
+
+
+def test_encoder_deterministic():
+    import bit_quantized_lora_blockwise_amd as q
+    W = WL.weight_gaussian(2048, 4096, 0.02, 77).to(DEV)
+    a = q.nf4_quantize(W)
+    b = q.nf4_quantize(W)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+def test_double_quant_sweep():
+    """Every 97th fp32 value in [0, 1] as a scale in groups whose max is 1.0: the
+    E4M3FN code of each equals the oracle's."""
+    import bit_quantized_lora_blockwise_amd as q
+    one = int(np.float32(1.0).view(np.uint32))
+    t = np.arange(0, one + 1, 97, dtype=np.uint32).view(np.float32)
+    per = 255
+    ng = (t.size + per - 1) // per
+    a = np.zeros(ng * 256, np.float32)
+    a.reshape(ng, 256)[:, 0] = 1.0
+    body = a.reshape(ng, 256)[:, 1:].reshape(-1)
+    body[:t.size] = t
+    a.reshape(ng, 256)[:, 1:] = body.reshape(ng, 255)
+    print(f"[double-quant sweep] {t.size} values in {ng} groups", flush=True)
+    ad = torch.from_numpy(a).to(DEV)
+    c2, c1 = q.nf4_double_quant(ad)
+    torch.cuda.synchronize()
+    r_c2, r_c1 = O.nf4_double_quant(a)
+    assert_bitexact(c2.cpu().numpy(), r_c2, "c2 sweep")
+    assert_bitexact(c1.cpu().numpy().view(np.uint32), r_c1.view(np.uint32), "c1 sweep")

@@ -1,0 +1,164 @@
+"""GPU parity of the quantized LoRA linear (forward and backward) against the
+CPU oracle: small and ragged shapes compared element by element, the
+decode-sized and training-sized workloads compared in full where the oracle
+can afford it and on sampled rows / columns otherwise.
+
+Tolerance (Y, dX, dL1, dL2 and T): relative L2 <= 2e-3 and
+max |err| <= 1e-2 * max |ref|, with the oracle rounding T, Y, G and dX to bf16
+at the same points as the kernels."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from gpu_util import assert_close, bits, f32np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def qlib():
+    import bit_quantized_lora_blockwise_amd as q
+    return q
+
+
+def quantize_both(W_cpu):
+    """Quantize on the GPU (kept on device) and, independently, with the oracle."""
+    q = qlib()
+    codes, absmax = q.nf4_quantize(W_cpu.to(DEV))
+    c2, c1 = q.nf4_double_quant(absmax)
+    Wn = W_cpu.float().numpy()
+    rc, ra = O.nf4_quantize(Wn)
+    rc2, rc1 = O.nf4_double_quant(ra)
+    return (codes, c2, c1), (rc, rc2, rc1)
+
+
+def run_gpu(inp, s=1.0, quant=None, keep_T=True):
+    q = qlib()
+    W = inp["W"]
+    N, K = W.shape
+    (codes, c2, c1) = quant
+    X, L1, L2, dY = (inp[k].to(DEV) for k in ("X", "L1", "L2", "dY"))
+    Y, T = q.qlora_linear_fwd(X, codes, c2, c1, N, L1, L2, s, T_out=True)
+    dX, dL1, dL2 = q.qlora_linear_bwd(X, dY, codes, c2, c1, L1, L2, s, T=T if keep_T else None)
+    torch.cuda.synchronize()
+    return {"Y": Y, "T": T, "dX": dX, "dL1": dL1, "dL2": dL2}
+
+
+def full_case(inp, s=1.0, name=""):
+    N, K = inp["W"].shape
+    M = inp["X"].shape[0]
+    r = inp["L1"].shape[1]
+    print(f"[layer] {name} M={M} K={K} N={N} r={r} s={s}", flush=True)
+    gq, rq = quantize_both(inp["W"])
+    g = run_gpu(inp, s, gq)
+    Wq = O.nf4_dequantize(*rq, N, K)
+    X, L1, L2, dY = (bits(inp[k]) for k in ("X", "L1", "L2", "dY"))
+    Y, T = O.qlora_forward(X, Wq, L1, L2, s)
+    dX, dL1, dL2, G, _ = O.qlora_backward(X, dY, Wq, L1, L2, s, T=T)
+    assert_close(bits(g["T"]), T, f"{name} T")
+    assert_close(bits(g["Y"]), Y, f"{name} Y")
+    assert_close(bits(g["dX"]), dX, f"{name} dX")
+    assert_close(f32np(g["dL1"]), dL1, f"{name} dL1")
+    assert_close(f32np(g["dL2"]), dL2, f"{name} dL2")
+    return g
+
+
+def test_config1_full():
+    full_case(WL.config1(), 1.0, "512x512 r=8 M=32")
+
+
+RAGGED = [
+    (37, 192, 200, 5), (17, 64, 33, 1), (130, 256, 136, 16), (64, 320, 96, 64), (200, 128, 260, 24),
+    (1, 128, 50, 3), (2, 64, 8, 64), (3, 192, 77, 7), (4, 256, 130, 12), (16, 512, 260, 64), (15, 64, 129, 33),
+]
+
+
+@pytest.mark.parametrize("M,K,N,r", RAGGED)
+def test_ragged_shapes(M, K, N, r):
+    inp = WL.layer_inputs(N, K, M, r, seed_base=M * 7919 + K * 31 + N + r, l2_std=0.3)
+    full_case(inp, 0.75, "ragged")
+
+
+@pytest.mark.parametrize("M", [32, 4])
+def test_lora_isolation_zero_base(M):
+    """W == 0: every code is 7 and every scale 0, so Y = bf16(s T L2) and dX = bf16(G L1^T);
+    with L2 ~ N(0, 1) the LoRA epilogues are checked on their own."""
+    inp = WL.layer_inputs(384, 256, M, 16, seed_base=500 + M, l2_std=1.0)
+    inp["W"] = torch.zeros_like(inp["W"])
+    full_case(inp, 1.5, "W=0")
+
+
+def test_zero_upstream_gradient():
+    inp = WL.layer_inputs(192, 128, 40, 8, seed_base=900)
+    inp["dY"] = torch.zeros_like(inp["dY"])
+    gq, _ = quantize_both(inp["W"])
+    g = run_gpu(inp, 1.0, gq)
+    assert not torch.any(g["dX"].float() != 0) and not torch.any(g["dL1"] != 0) and not torch.any(g["dL2"] != 0)
+
+
+def test_recompute_T_and_skip_dX_match():
+    q = qlib()
+    inp = WL.layer_inputs(320, 192, 48, 12, seed_base=1234)
+    gq, _ = quantize_both(inp["W"])
+    a = run_gpu(inp, 1.0, gq, keep_T=True)
+    b = run_gpu(inp, 1.0, gq, keep_T=False)
+    assert torch.equal(a["dX"], b["dX"]) and torch.equal(a["dL1"], b["dL1"]) and torch.equal(a["dL2"], b["dL2"])
+    X, L1, L2, dY = (inp[k].to(DEV) for k in ("X", "L1", "L2", "dY"))
+    codes, c2, c1 = gq
+    dX, dL1, dL2 = q.qlora_linear_bwd(X, dY, codes, c2, c1, L1, L2, 1.0, T=a["T"], dX=None)
+    torch.cuda.synchronize()
+    assert dX is None and torch.equal(dL1, a["dL1"]) and torch.equal(dL2, a["dL2"])
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_llama7b_up_full(M):
+    """Decode-sized forward at the full 4096 -> 11008 shape, every output compared."""
+    inp = WL.config2(M)
+    N, K = inp["W"].shape
+    print(f"[decode] M={M} K={K} N={N}", flush=True)
+    q = qlib()
+    gq, rq = quantize_both(inp["W"])
+    X, L1, L2 = (inp[k].to(DEV) for k in ("X", "L1", "L2"))
+    Y, T = q.qlora_linear_fwd(X, *gq, N, L1, L2, 1.0, T_out=True)
+    torch.cuda.synchronize()
+    Wq = O.nf4_dequantize(*rq, N, K)
+    rY, rT = O.qlora_forward(bits(inp["X"]), Wq, bits(inp["L1"]), bits(inp["L2"]), 1.0)
+    assert_close(bits(T), rT, f"decode M={M} T")
+    assert_close(bits(Y), rY, f"decode M={M} Y")
+
+
+def _sampled_case(inp, name, n_rows=48, seed=0):
+    """Full-size check: dL1, dL2 and T in full; Y and dX on sampled rows."""
+    N, K = inp["W"].shape
+    M = inp["X"].shape[0]
+    print(f"[layer sampled] {name} M={M} K={K} N={N}", flush=True)
+    gq, rq = quantize_both(inp["W"])
+    g = run_gpu(inp, 1.0, gq)
+    rows = np.sort(np.random.default_rng(seed).choice(M, n_rows, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    Wq = O.nf4_dequantize(*rq, N, K)
+    X, L1, L2, dY = (bits(inp[k]) for k in ("X", "L1", "L2", "dY"))
+    Y_s, T_s = O.qlora_forward(X[rows], Wq, L1, L2, 1.0)
+    assert_close(bits(g["Y"])[rows], Y_s, f"{name} Y rows")
+    T_full = O.bf16_bits(O.bf16_value(X) @ O.bf16_value(L1))
+    assert_close(bits(g["T"]), T_full, f"{name} T")
+    dX_s, _, _, _, _ = O.qlora_backward(X[rows], dY[rows], Wq, L1, L2, 1.0, T=T_full[rows])
+    assert_close(bits(g["dX"])[rows], dX_s, f"{name} dX rows")
+    _, dL1, dL2, _, _ = O.qlora_backward(X, dY, None, L1, L2, 1.0, T=T_full, compute_dx=False)
+    assert_close(f32np(g["dL1"]), dL1, f"{name} dL1")
+    assert_close(f32np(g["dL2"]), dL2, f"{name} dL2")
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_llama7b_mlp_m4096_sampled(which):
+    c = WL.config3()[which]
+    _sampled_case(c, f"llama7b {which} M=4096")
+
+
+@pytest.mark.parametrize("name", ["q", "gate", "down"])
+def test_llama65b_block_linear_sampled(name):
+    """One linear of each distinct shape of the 65B block (k, v, o share q's shape,
+    up shares gate's) at M = 2048."""
+    _sampled_case(WL.config4_linear(name), f"llama65b {name} M=2048", n_rows=24)
