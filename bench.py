@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA hot path on one MI355X.
+
+Timed step (the headline number): one pass of the whole path over the
+LLaMA-7B MLP pair at M = 4096 tokens, r = 64 --
+  for the up-projection (4096 -> 11008) and the down-projection (11008 -> 4096):
+  NF4 encode + double quantization of the frozen weight, forward, backward
+  (dX, dL1, dL2).
+value = algorithmic fwd+bwd FLOPs of both linears (4MKN + 6Mr(K+N) each; the
+encode adds no FLOPs) / time per step, in TFLOP/s.
+
+Also reported (not part of `value`):
+  * per-kernel roofline of the fused quantized GEMMs (forward and dX), timed with
+    HIP events on the stream they run on;
+  * decode: packed-weight GB/s of the M = 1 forward kernel at 4096 -> 11008,
+    rotating over 24 copies of the packed layer (> 512 MB) so that every call
+    streams from HBM rather than the 256 MB Infinity Cache; M = 4 and 16 too;
+  * encode throughput over the 7 linears of one LLaMA-65B block (809.5 M weights);
+  * the CPU oracle timed on a bounded sample of the headline step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "qlora_linear fwd+bwd TFLOP/s at M=4096; packed-weight HBM GB/s at M=1"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def layer_flops(M, K, N, r):
+    return 4 * M * K * N + 6 * M * r * (K + N)
+
+
+class Linear:
+    """Device buffers of one linear: weights, adapters, activations and outputs,
+    all allocated before timing so the timed region allocates nothing."""
+
+    def __init__(self, inp, dev):
+        import torch
+        import bit_quantized_lora_blockwise_amd as q
+        self.q = q
+        self.W = inp["W"].to(dev)
+        self.N, self.K = self.W.shape
+        self.X, self.L1, self.L2, self.dY = (inp[k].to(dev) for k in ("X", "L1", "L2", "dY"))
+        self.M = self.X.shape[0]
+        self.r = self.L1.shape[1]
+        E = self.N * self.K
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        self.codes = torch.empty((self.N, self.K // 2), dtype=u8, device=dev)
+        self.absmax = torch.empty((E // 64,), dtype=f32, device=dev)
+        self.c2 = torch.empty((E // 64,), dtype=u8, device=dev)
+        self.c1 = torch.empty(((E // 64 + 255) // 256,), dtype=f32, device=dev)
+        self.Y = torch.empty((self.M, self.N), dtype=bf, device=dev)
+        self.T = torch.empty((self.M, self.r), dtype=bf, device=dev)
+        self.G = torch.empty((self.M, self.r), dtype=bf, device=dev)
+        self.dX = torch.empty((self.M, self.K), dtype=bf, device=dev)
+        self.dL1 = torch.empty((self.K, self.r), dtype=f32, device=dev)
+        self.dL2 = torch.empty((self.r, self.N), dtype=f32, device=dev)
+        self.ws_f = torch.empty((max(16, q.qlora_linear_fwd_workspace(self.M, self.K, self.N, self.r)),),
+                                dtype=u8, device=dev)
+        self.ws_b = torch.empty((max(16, q.qlora_linear_bwd_workspace(self.M, self.K, self.N, self.r)),),
+                                dtype=u8, device=dev)
+
+    def encode(self):
+        self.q.nf4_quantize(self.W, self.codes, self.absmax)
+        self.q.nf4_double_quant(self.absmax, self.c2, self.c1)
+
+    def forward(self):
+        self.q.qlora_linear_fwd(self.X, self.codes, self.c2, self.c1, self.N, self.L1, self.L2, 1.0, Y=self.Y,
+                                T_out=self.T, workspace=self.ws_f)
+
+    def backward(self):
+        self.q.qlora_linear_bwd(self.X, self.dY, self.codes, self.c2, self.c1, self.L1, self.L2, 1.0, T=self.T,
+                                dX=self.dX, dL1=self.dL1, dL2=self.dL2, workspace=self.ws_b)
+
+    def step(self):
+        self.encode()
+        self.forward()
+        self.backward()
+
+    def flops(self):
+        return layer_flops(self.M, self.K, self.N, self.r)
+
+
+def time_launches(fn, reps):
+    """Average duration (ms) of `fn` over `reps` back-to-back calls, HIP events on the current stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def kernel_rooflines(lins, reps):
+    """Fused forward GEMM and fused dX GEMM, each launched alone (stage entry points)."""
+    q = lins[0].q
+    out = {}
+    for L in lins:
+        q.qlora_lora_grad_in(L.dY, L.L2, 1.0, G=L.G)
+    fwd_fns = [lambda L=L: q.qlora_linear_fwd_t(L.X, L.codes, L.c2, L.c1, L.N, L.T, L.L2, 1.0, Y=L.Y)
+               for L in lins]
+    dx_fns = [lambda L=L: q.qlora_linear_dx(L.dY, L.codes, L.c2, L.c1, L.K, L.G, L.L1, dX=L.dX) for L in lins]
+
+    def both(fns):
+        def run():
+            for f in fns:
+                f()
+        return run
+
+    for name, fns, flops in (
+            ("k_qgemm_fwd", fwd_fns, [2 * L.M * L.K * L.N + 2 * L.M * L.r * L.N for L in lins]),
+            ("k_qgemm_dx", dx_fns, [2 * L.M * L.K * L.N + 2 * L.M * L.r * L.K for L in lins])):
+        ms = time_launches(both(fns), reps) / len(fns)       # average per launch over the shape mix
+        avg_flops = sum(flops) / len(flops)
+        tf = avg_flops / (ms * 1e-3) / 1e12
+        out[name] = {"avg_ms": ms, "flops_per_launch": avg_flops, "tflops": tf}
+    return out
+
+
+def decode_bench(dev, reps=200):
+    import torch
+    import bit_quantized_lora_blockwise_amd as q
+    import workloads as WL
+    res = {}
+    inp = WL.config2(16)
+    W = inp["W"].to(dev)
+    N, K = W.shape
+    codes, absmax = q.nf4_quantize(W)
+    c2, c1 = q.nf4_double_quant(absmax)
+    packed = codes.numel() + c2.numel() + c1.numel() * 4
+    copies = max(24, (600 << 20) // packed + 1)
+    layers = [(codes.clone(), c2.clone(), c1.clone()) for _ in range(copies)]
+    del W, absmax
+    L1, L2 = inp["L1"].to(dev), inp["L2"].to(dev)
+    r = L1.shape[1]
+    for M in (1, 4, 16):
+        X = inp["X"][:M].contiguous().to(dev)
+        T = q.qlora_lora_down(X, L1)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((q.qlora_linear_fwd_workspace(M, K, N, r),), dtype=torch.uint8, device=dev)
+        it = [0]
+
+        def kern():
+            cd, cc2, cc1 = layers[it[0] % copies]
+            it[0] += 1
+            q.qlora_linear_fwd_t(X, cd, cc2, cc1, N, T, L2, 1.0, Y=Y)
+
+        def full():
+            cd, cc2, cc1 = layers[it[0] % copies]
+            it[0] += 1
+            q.qlora_linear_fwd(X, cd, cc2, cc1, N, L1, L2, 1.0, Y=Y, T_out=T, workspace=ws)
+
+        kms = time_launches(kern, reps)
+        fms = time_launches(full, reps)
+        alg = packed + r * N * 2 + M * K * 2 + M * r * 2 + M * N * 2
+        res[f"M{M}"] = {"kernel_us": kms * 1e3, "packed_gbps": packed / (kms * 1e-3) / 1e9,
+                        "alg_gbps": alg / (kms * 1e-3) / 1e9, "full_call_us": fms * 1e3,
+                        "full_call_packed_gbps": packed / (fms * 1e-3) / 1e9}
+    res["packed_bytes"] = packed
+    res["copies_rotated"] = copies
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def encode_bench(dev, reps=3):
+    import torch
+    import bit_quantized_lora_blockwise_amd as q
+    import workloads as WL
+    mats = []
+    for name in WL.LLAMA65B_BLOCK:
+        W = WL.config5_weight(0, name, "gauss", device=dev)
+        N, K = W.shape
+        E = N * K
+        bufs = (torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+                torch.empty((E // 64,), dtype=torch.float32, device=dev),
+                torch.empty((E // 64,), dtype=torch.uint8, device=dev),
+                torch.empty(((E // 64 + 255) // 256,), dtype=torch.float32, device=dev))
+        mats.append((W, bufs))
+
+    def run():
+        for W, (cd, am, c2, c1) in mats:
+            q.nf4_quantize(W, cd, am)
+            q.nf4_double_quant(am, c2, c1)
+
+    ms = time_launches(run, reps)
+    weights = sum(W.numel() for W, _ in mats)
+    alg_bytes = weights * (2 + 0.5 + 4 / 64 + 4 / 64 + 1 / 64) + 4 * weights / 16384
+    res = {"block_weights": weights, "ms_per_block": ms, "weights_per_s": weights / (ms * 1e-3),
+           "alg_gbps": alg_bytes / (ms * 1e-3) / 1e9, "est_80_blocks_ms": 80 * ms}
+    del mats
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline():
+    """The CPU oracle on a bounded sample of the headline step: the whole
+    up-projection half of it (4096 -> 11008, r = 64, M = 4096 tokens) -- encode,
+    double quant, dequant, forward and backward in float64 NumPy."""
+    import numpy as np
+    import torch
+    import oracle as O
+    import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    inp = WL.config3()["up"]
+    W = inp["W"].float().numpy()
+    b = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    X, L1, L2, dY = b(inp["X"]), b(inp["L1"]), b(inp["L2"]), b(inp["dY"])
+    N, K = W.shape
+    Ms = X.shape[0]
+    t0 = time.perf_counter()
+    codes, absmax = O.nf4_quantize(W)
+    c2, c1 = O.nf4_double_quant(absmax)
+    Wq = O.nf4_dequantize(codes, c2, c1, N, K)
+    Y, T = O.qlora_forward(X, Wq, L1, L2, 1.0)
+    O.qlora_backward(X, dY, Wq, L1, L2, 1.0, T=T)
+    dt = time.perf_counter() - t0
+    flops = layer_flops(Ms, K, N, 64)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": dt,
+            "sample": "the up-projection half of the step (4096->11008, r=64, M=4096): encode + double quant + "
+                      "dequant + fwd + bwd, float64 NumPy oracle on the host"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as WL
+    import bit_quantized_lora_blockwise_amd as q
+    q.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    c3 = WL.config3()
+    lins = [Linear(c3["up"], dev), Linear(c3["down"], dev)]
+    del c3
+
+    def step():
+        for L in lins:
+            L.step()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    flops = sum(L.flops() for L in lins)
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    # phases of the step, each timed alone
+    phases = {}
+    for name, fn in (("encode", lambda: [L.encode() for L in lins]),
+                     ("forward", lambda: [L.forward() for L in lins]),
+                     ("backward", lambda: [L.backward() for L in lins])):
+        phases[name + "_ms"] = time_launches(fn, max(3, args.kernel_reps // 4))
+    fb_ms = phases["forward_ms"] + phases["backward_ms"]
+
+    kern = kernel_rooflines(lins, args.kernel_reps)
+    dom = max(kern, key=lambda k: kern[k]["avg_ms"])
+    roof = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": kern[dom]["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+            "avg_launch_ms": kern[dom]["avg_ms"], "flops_per_launch": kern[dom]["flops_per_launch"]}
+    del lins
+    torch.cuda.empty_cache()
+
+    dec = decode_bench(dev)
+    m1 = dec["M1"]
+    dec_roof = {"kernel": "k_qgemv_fwd", "bound": "hbm", "achieved": m1["alg_gbps"], "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": m1["alg_gbps"] / PEAK_HBM_GBPS, "traffic": None,
+                "avg_launch_us": m1["kernel_us"]}
+    enc = encode_bench(dev)
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama7b MLP up 4096->11008 + down 11008->4096, M=4096 tokens, r=64: "
+                               "encode + double quant + fwd + bwd per step",
+                   "global_batch": 4096, "seq_len": 4096, "parallelism": "none (1 GPU)"},
+        "fwd_bwd_only": {"ms": round(fb_ms, 4), "tflops": round(flops / (fb_ms * 1e-3) / 1e12, 3)},
+        "phases_ms": {k: round(v, 4) for k, v in phases.items()},
+        "roofline": roof,
+        "kernels": kern,
+        "decode_m1_packed_gbps": round(m1["packed_gbps"], 1),
+        "decode": dec,
+        "roofline_decode": dec_roof,
+        "encode": enc,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

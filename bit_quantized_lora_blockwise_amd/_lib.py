@@ -21,7 +21,8 @@ STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_DTYPE",
           -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_HIP"}
 EXPORTS = ("nf4_quantize", "nf4_double_quant", "nf4_dequantize", "qlora_linear_fwd_workspace",
            "qlora_linear_fwd", "qlora_linear_bwd_workspace", "qlora_linear_bwd", "qlora_nf4_levels",
-           "ql_status_string")
+           "ql_status_string", "qlora_lora_down_workspace", "qlora_lora_down", "qlora_linear_fwd_t",
+           "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx")
 
 
 class QloraError(RuntimeError):
@@ -49,6 +50,12 @@ def lib():
             "qlora_linear_bwd": ([P, P, I64, I64, I64, P, P, P, P, P, I32, F32, P, P, P, P, P, SZ, P], I32),
             "qlora_nf4_levels": ([P], I32),
             "ql_status_string": ([I32], ctypes.c_char_p),
+            "qlora_lora_down_workspace": ([I64, I64, I32], SZ),
+            "qlora_lora_down": ([P, I64, I64, P, I32, P, P, SZ, P], I32),
+            "qlora_linear_fwd_t": ([P, I64, I64, I64, P, P, P, P, P, I32, F32, P, P], I32),
+            "qlora_lora_grad_in_workspace": ([I64, I64, I32], SZ),
+            "qlora_lora_grad_in": ([P, I64, I64, P, I32, F32, P, P, SZ, P], I32),
+            "qlora_linear_dx": ([P, I64, I64, I64, P, P, P, P, P, I32, P, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -194,3 +201,54 @@ def qlora_nf4_levels():
 
 def ql_status_string(status):
     return lib().ql_status_string(int(status)).decode()
+
+
+# --- stage entry points -------------------------------------------------------
+
+def qlora_lora_down(X, L1, T=None, workspace=None, stream=None):
+    """T = bf16(X L1) [M, r]."""
+    _need(X, "X", torch.bfloat16, 2); _need(L1, "L1", torch.bfloat16, 2)
+    M, K = X.shape
+    r = L1.shape[1]
+    T = _empty((M, r), torch.bfloat16, X) if T is None else _need(T, "T", torch.bfloat16)
+    ws = _workspace(int(lib().qlora_lora_down_workspace(M, K, r)), X, workspace)
+    _check("qlora_lora_down", lib().qlora_lora_down(_ptr(X), M, K, _ptr(L1), r, _ptr(T), _ptr(ws), ws.numel(),
+                                                    _stream(stream)))
+    return T
+
+
+def qlora_linear_fwd_t(X, codes, c2, c1, N, T, L2, lora_scale=1.0, Y=None, stream=None):
+    """Y = bf16(X W'^T + s T L2) given T (one kernel)."""
+    _need(X, "X", torch.bfloat16, 2); _need(T, "T", torch.bfloat16, 2); _need(L2, "L2", torch.bfloat16, 2)
+    _need(codes, "codes", torch.uint8); _need(c2, "c2", torch.uint8); _need(c1, "c1", torch.float32)
+    M, K = X.shape
+    r = T.shape[1]
+    Y = _empty((M, N), torch.bfloat16, X) if Y is None else _need(Y, "Y", torch.bfloat16)
+    _check("qlora_linear_fwd_t", lib().qlora_linear_fwd_t(
+        _ptr(X), M, K, N, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(T), _ptr(L2), r, float(lora_scale), _ptr(Y),
+        _stream(stream)))
+    return Y
+
+
+def qlora_lora_grad_in(dY, L2, lora_scale=1.0, G=None, workspace=None, stream=None):
+    """G = bf16(s dY L2^T) [M, r]."""
+    _need(dY, "dY", torch.bfloat16, 2); _need(L2, "L2", torch.bfloat16, 2)
+    M, N = dY.shape
+    r = L2.shape[0]
+    G = _empty((M, r), torch.bfloat16, dY) if G is None else _need(G, "G", torch.bfloat16)
+    ws = _workspace(int(lib().qlora_lora_grad_in_workspace(M, N, r)), dY, workspace)
+    _check("qlora_lora_grad_in", lib().qlora_lora_grad_in(_ptr(dY), M, N, _ptr(L2), r, float(lora_scale), _ptr(G),
+                                                          _ptr(ws), ws.numel(), _stream(stream)))
+    return G
+
+
+def qlora_linear_dx(dY, codes, c2, c1, K, G, L1, dX=None, stream=None):
+    """dX = bf16(dY W' + G L1^T) given G (one kernel)."""
+    _need(dY, "dY", torch.bfloat16, 2); _need(G, "G", torch.bfloat16, 2); _need(L1, "L1", torch.bfloat16, 2)
+    _need(codes, "codes", torch.uint8); _need(c2, "c2", torch.uint8); _need(c1, "c1", torch.float32)
+    M, N = dY.shape
+    r = G.shape[1]
+    dX = _empty((M, K), torch.bfloat16, dY) if dX is None else _need(dX, "dX", torch.bfloat16)
+    _check("qlora_linear_dx", lib().qlora_linear_dx(
+        _ptr(dY), M, K, N, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(G), _ptr(L1), r, _ptr(dX), _stream(stream)))
+    return dX

@@ -158,6 +158,66 @@ int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K
   return QL_OK;
 }
 
+size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r) {
+  if (!shapes_ok(M, K, 1, r)) return 0;
+  return round_up(lora_skinny_ws(M, K, r));
+}
+
+int qlora_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, uint16_t* T,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  if (!X || !L1 || !T) return QL_ERR_NULL;
+  if (!shapes_ok(M, K, 1, r)) return QL_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(L1) || !aligned16(T)) return QL_ERR_ALIGN;
+  if (!workspace || ws_bytes < qlora_lora_down_workspace(M, K, r)) return QL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QL_ERR_ALIGN;
+  QL_TRY(launch_lora_skinny(X, M, K, L1, true, r, 1.0f, T, (float*)workspace, (hipStream_t)stream));
+  return QL_OK;
+}
+
+int qlora_linear_fwd_t(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                       const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
+                       float lora_scale, uint16_t* Y, void* stream) {
+  if (!X || !codes || !c2 || !c1 || !T || !L2 || !Y) return QL_ERR_NULL;
+  if (!shapes_ok(M, K, N, r)) return QL_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(codes) || !aligned16(c2) || !aligned16(c1) || !aligned16(T) ||
+      !aligned16(L2) || !aligned16(Y))
+    return QL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (M <= 16)
+    QL_TRY(launch_qgemv_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
+  else
+    QL_TRY(launch_qgemm_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
+  return QL_OK;
+}
+
+size_t qlora_lora_grad_in_workspace(int64_t M, int64_t N, int r) {
+  if (!(M > 0 && N > 0 && r >= 1 && r <= 64 && M <= (int64_t(1) << 31) && N <= (int64_t(1) << 31))) return 0;
+  return round_up(lora_skinny_ws(M, N, r));
+}
+
+int qlora_lora_grad_in(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* L2, int r, float lora_scale,
+                       uint16_t* G, void* workspace, size_t ws_bytes, void* stream) {
+  if (!dY || !L2 || !G) return QL_ERR_NULL;
+  const size_t need = qlora_lora_grad_in_workspace(M, N, r);
+  if (need == 0) return QL_ERR_SHAPE;
+  if (!aligned16(dY) || !aligned16(L2) || !aligned16(G)) return QL_ERR_ALIGN;
+  if (!workspace || ws_bytes < need) return QL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QL_ERR_ALIGN;
+  QL_TRY(launch_lora_skinny(dY, M, N, L2, false, r, lora_scale, G, (float*)workspace, (hipStream_t)stream));
+  return QL_OK;
+}
+
+int qlora_linear_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint8_t* codes, const uint8_t* c2,
+                    const float* c1, const uint16_t* G, const uint16_t* L1, int r, uint16_t* dX, void* stream) {
+  if (!dY || !codes || !c2 || !c1 || !G || !L1 || !dX) return QL_ERR_NULL;
+  if (!shapes_ok(M, K, N, r)) return QL_ERR_SHAPE;
+  if (!aligned16(dY) || !aligned16(codes) || !aligned16(c2) || !aligned16(c1) || !aligned16(G) ||
+      !aligned16(L1) || !aligned16(dX))
+    return QL_ERR_ALIGN;
+  QL_TRY(launch_qgemm_dx(dY, M, K, N, codes, c2, c1, G, L1, r, dX, (hipStream_t)stream));
+  return QL_OK;
+}
+
 int qlora_nf4_levels(float* out16) {
   if (!out16) return QL_ERR_NULL;
   std::memcpy(out16, nf4_params().q, 16 * sizeof(float));

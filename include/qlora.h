@@ -127,6 +127,39 @@ int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K
                      const uint16_t* T, uint16_t* dX, float* dL1, float* dL2,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* Stage entry points: the single fused kernels of the layer, for callers that
+ * keep the LoRA intermediates themselves (activation checkpointing, graph
+ * capture of individual stages, per-kernel timing). Same formulas, layouts
+ * and rounding points as the calls above.
+ *
+ * qlora_lora_down: T = bf16(X L1) [M, r] (nlp-lineage page, notation paragraph,
+ * the X L1 factor of the adapter path). ws_bytes >= qlora_lora_down_workspace().  */
+size_t qlora_lora_down_workspace(int64_t M, int64_t K, int r);
+int qlora_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r,
+                    uint16_t* T, void* workspace, size_t ws_bytes, void* stream);
+
+/* qlora_linear_fwd_t: Y = bf16(X W'^T + lora_scale * (T L2)) given T; one kernel,
+ * no workspace (same paragraph; W' rebuilt on the fly as in qlora_linear_fwd).  */
+int qlora_linear_fwd_t(const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                       const uint8_t* codes, const uint8_t* c2, const float* c1,
+                       const uint16_t* T, const uint16_t* L2, int r, float lora_scale,
+                       uint16_t* Y, void* stream);
+
+/* qlora_lora_grad_in: G = bf16(lora_scale * dY L2^T) [M, r], the gradient that
+ * reaches the adapter's inner activation (inferensys glossary, frozen-base
+ * paragraph: gradients flow through to the adapters).
+ * ws_bytes >= qlora_lora_grad_in_workspace().                                    */
+size_t qlora_lora_grad_in_workspace(int64_t M, int64_t N, int r);
+int qlora_lora_grad_in(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* L2, int r,
+                       float lora_scale, uint16_t* G, void* workspace, size_t ws_bytes, void* stream);
+
+/* qlora_linear_dx: dX = bf16(dY W' + G L1^T) given G; one kernel, no workspace
+ * (the transposed-weight path through the frozen base: examadda page,
+ * "The Flow"; nlp-lineage page, "The idea", mechanism paragraph).               */
+int qlora_linear_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N,
+                    const uint8_t* codes, const uint8_t* c2, const float* c1,
+                    const uint16_t* G, const uint16_t* L1, int r, uint16_t* dX, void* stream);
+
 /* Host-only helpers (no GPU needed). */
 /* The 16 NF4 levels (fp32, ascending) that the kernels use, copied to out[16].  */
 int qlora_nf4_levels(float* out16);

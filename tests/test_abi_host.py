@@ -105,3 +105,19 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+def test_stage_entry_validation():
+    _, L = _lib()
+    assert L.qlora_lora_down_workspace(64, 100, 8) == 0
+    ws = L.qlora_lora_down_workspace(64, 128, 8)
+    assert ws > 0
+    assert L.qlora_lora_down(A, 64, 128, A, 8, None, A, ws, None) == -1
+    assert L.qlora_lora_down(A, 64, 128, A, 8, A, A, ws - 1, None) == -5
+    assert L.qlora_linear_fwd_t(A, 64, 128, 32, A, A, A, A, A, 0, 1.0, A, None) == -2
+    assert L.qlora_linear_fwd_t(A, 64, 128, 32, A, A, A, MIS, A, 8, 1.0, A, None) == -4
+    assert L.qlora_lora_grad_in_workspace(64, 0, 8) == 0
+    wg = L.qlora_lora_grad_in_workspace(64, 33, 8)
+    assert L.qlora_lora_grad_in(A, 64, 33, A, 8, 1.0, A, None, wg, None) == -5
+    assert L.qlora_linear_dx(A, 64, 96, 32, A, A, A, A, A, 8, A, None) == -2
+    assert L.qlora_linear_dx(A, 64, 128, 32, A, A, A, A, None, 8, A, None) == -1

@@ -162,3 +162,19 @@ def test_llama65b_block_linear_sampled(name):
     """One linear of each distinct shape of the 65B block (k, v, o share q's shape,
     up shares gate's) at M = 2048."""
     _sampled_case(WL.config4_linear(name), f"llama65b {name} M=2048", n_rows=24)
+
+
+@pytest.mark.parametrize("M", [8, 96])
+def test_stage_entry_points_match_fused_calls(M):
+    """lora_down + fwd_t == fwd; grad_in + dx == the dX of bwd (same kernels, bitwise)."""
+    q = qlib()
+    inp = WL.layer_inputs(200, 256, M, 24, seed_base=4321 + M, l2_std=0.2)
+    gq, _ = quantize_both(inp["W"])
+    a = run_gpu(inp, 0.5, gq)
+    X, L1, L2, dY = (inp[k].to(DEV) for k in ("X", "L1", "L2", "dY"))
+    T = q.qlora_lora_down(X, L1)
+    Y = q.qlora_linear_fwd_t(X, *gq, 200, T, L2, 0.5)
+    G = q.qlora_lora_grad_in(dY, L2, 0.5)
+    dX = q.qlora_linear_dx(dY, *gq, 256, G, L1)
+    torch.cuda.synchronize()
+    assert torch.equal(T, a["T"]) and torch.equal(Y, a["Y"]) and torch.equal(dX, a["dX"])
