@@ -65,6 +65,22 @@ BwdWs bwd_ws(int64_t M, int64_t K, int64_t N, int r) {
   return w;
 }
 
+// Forward product for M > 16: the large-tile kernel when the shapes qualify.
+hipError_t run_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes, const uint8_t* c2,
+                        const float* c1, const uint16_t* T, const uint16_t* L2, int r, float scale, uint16_t* Y,
+                        hipStream_t s) {
+  if (qgemm_big_ok(false, M, K, N))
+    return launch_qgemm_big(false, X, M, K, N, codes, c2, c1, T, L2, r, scale, Y, s);
+  return launch_qgemm_fwd(X, M, K, N, codes, c2, c1, T, L2, r, scale, Y, s);
+}
+
+hipError_t run_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint8_t* codes, const uint8_t* c2,
+                       const float* c1, const uint16_t* G, const uint16_t* L1, int r, uint16_t* dX, hipStream_t s) {
+  if (qgemm_big_ok(true, M, K, N))
+    return launch_qgemm_big(true, dY, M, K, N, codes, c2, c1, G, L1, r, 1.0f, dX, s);
+  return launch_qgemm_dx(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,7 +136,7 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const u
   if (M <= 16)
     QL_TRY(launch_qgemv_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
   else
-    QL_TRY(launch_qgemm_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
+    QL_TRY(run_fwd_gemm(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
   return QL_OK;
 }
 
@@ -152,7 +168,7 @@ int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K
     T = Tw;
   }
   QL_TRY(launch_lora_skinny(dY, M, N, L2, false, r, lora_scale, G, part, s));
-  if (dX) QL_TRY(launch_qgemm_dx(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s));
+  if (dX) QL_TRY(run_dx_gemm(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s));
   QL_TRY(launch_lora_tn(X, G, M, K, r, 1.0f, false, dL1, part, s));
   QL_TRY(launch_lora_tn(dY, T, M, N, r, lora_scale, true, dL2, part, s));
   return QL_OK;
@@ -186,7 +202,7 @@ int qlora_linear_fwd_t(const uint16_t* X, int64_t M, int64_t K, int64_t N, const
   if (M <= 16)
     QL_TRY(launch_qgemv_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
   else
-    QL_TRY(launch_qgemm_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
+    QL_TRY(run_fwd_gemm(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
   return QL_OK;
 }
 
@@ -214,7 +230,7 @@ int qlora_linear_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const u
   if (!aligned16(dY) || !aligned16(codes) || !aligned16(c2) || !aligned16(c1) || !aligned16(G) ||
       !aligned16(L1) || !aligned16(dX))
     return QL_ERR_ALIGN;
-  QL_TRY(launch_qgemm_dx(dY, M, K, N, codes, c2, c1, G, L1, r, dX, (hipStream_t)stream));
+  QL_TRY(run_dx_gemm(dY, M, K, N, codes, c2, c1, G, L1, r, dX, (hipStream_t)stream));
   return QL_OK;
 }
 

@@ -47,6 +47,13 @@ hipError_t launch_qgemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, 
 hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                             const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
                             float scale, uint16_t* Y, hipStream_t s);
+// Large-tile (256 x 256) versions of both GEMMs: dx = false computes the forward
+// (A = X, LA = T, LB = L2, C = Y), dx = true the dX product (A = dY, LA = G,
+// LB = L1, C = dX).  qgemm_big_ok says whether the shapes qualify.
+bool qgemm_big_ok(bool dx, int64_t M, int64_t K, int64_t N);
+hipError_t launch_qgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                            const uint8_t* c2, const float* c1, const uint16_t* LA, const uint16_t* LB, int r,
+                            float scale, uint16_t* C, hipStream_t s);
 // dX[M, K] = bf16(dY W' + G L1^T)
 hipError_t launch_qgemm_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                            const uint8_t* c2, const float* c1, const uint16_t* G, const uint16_t* L1, int r,
