@@ -27,7 +27,8 @@ constexpr int kBM = 256;          // activation rows per tile
 constexpr int kBP = 256;          // output columns per tile
 constexpr int kBR = 64;           // reduction per step
 constexpr int kPF = kBR + 8;      // pitch of the forward B tile [p][r] (elements)
-constexpr int kPD = kBP + 16;     // pitch of the dX B tile [r][p] (elements)
+constexpr int kPD = kBP + 32;     // pitch of the dX B tile [r][p] (elements): 144 dwords, so the
+                                  // 4 rows x 2 column halves of a 32-lane transposed read hit 64 banks
 constexpr int kBufElems = (kBP * kPF > kBR * kPD) ? kBP * kPF : kBR * kPD;
 constexpr int kPL = 64 + 8;       // pitch of the LoRA A tile [m][c]
 constexpr uint32_t kOOB = 0x80000000u;
@@ -237,43 +238,62 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     }
   };
 
-  // ---- main loop, two steps per iteration so the A fragments ping-pong
+  // ---- main loop.  Step st multiplies A(st) (registers) by the B tile in LDS
+  // buffer st % 2 while it dequantises block codes(st + 1) into the other
+  // buffer; the codes are loaded two steps ahead and the A fragments one step
+  // ahead.  The body has no branches (out-of-range steps load zeros), so the
+  // MFMAs, the dequantisation VALU work and the LDS traffic interleave.
   LDS_AS uint16_t* buf0 = (LDS_AS uint16_t*)lds;
   LDS_AS uint16_t* buf1 = (LDS_AS uint16_t*)lds + kBufElems;
   const int64_t nsteps = (R + kBR - 1) / kBR;
+  auto step = [&](int64_t st, const u32x4 (&acur)[2][4], u32x4 (&anext)[2][4], const LDS_AS uint16_t* bcur,
+                  LDS_AS uint16_t* bnext, const BlockCodes& bc_now, BlockCodes& bc_later) {
+    bc_later = load_codes(st + 2);
+    load_a((st + 1) * kBR, anext);
+    const BlockLut L = make_lut(qk::e4m3fn_to_f32(bc_now.c2b) * bc_now.c1v, p);
+    LDS_AS uint16_t* dst = kDx ? bnext + (t >> 2) * kPD + 64 * (t & 3) : bnext + t * kPF;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, acur[0][s]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, acur[1][s]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 b = kDx ? qk::frag_kmajor(bcur, kPD, 16 * s, 32 * j) : qk::frag_rowmajor(bcur, kPF, 32 * j, 16 * s);
+        acc[0][j] = qk::mfma32(a0, b, acc[0][j]);
+        acc[1][j] = qk::mfma32(a1, b, acc[1][j]);
+      }
+      // two of the eight 8-weight groups of the next tile per sub-step
+      const u32x4 cw = (s < 2) ? bc_now.c0 : bc_now.c1;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = 2 * (s & 1) + h;          // code word within cw
+        *(LDS_AS u32x4*)(dst + 32 * (s >> 1) + 8 * q) = dequant8(L, cw[q]);
+      }
+      // interleave: one B-fragment read, two MFMAs and VALU work, eight times
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 2 : 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);             // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);             // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);               // DS write
+    }
+    __syncthreads();
+  };
   u32x4 aA[2][4], aB[2][4];
+  BlockCodes bcA, bcB;
   {
-    BlockCodes bc = load_codes(0);
+    const BlockCodes bc0 = load_codes(0);
+    bcA = load_codes(1);
     load_a(0, aA);
-    dequant_store(bc, buf0);
+    dequant_store(bc0, buf0);
     __syncthreads();
   }
+  // bcA holds codes(st + 1) at the top of each even step
   for (int64_t st = 0; st < nsteps; st += 2) {
-    // step st: A in aA, B in buf0; prepare st + 1 into aB / buf1
-    {
-      const bool more = st + 1 < nsteps;
-      BlockCodes bc;
-      if (more) {
-        bc = load_codes(st + 1);
-        load_a((st + 1) * kBR, aB);
-      }
-      mma_step(aA, buf0);
-      if (more) dequant_store(bc, buf1);
-      __syncthreads();
-      if (!more) break;
-    }
-    // step st + 1: A in aB, B in buf1; prepare st + 2 into aA / buf0
-    {
-      const bool more = st + 2 < nsteps;
-      BlockCodes bc;
-      if (more) {
-        bc = load_codes(st + 2);
-        load_a((st + 2) * kBR, aA);
-      }
-      mma_step(aB, buf1);
-      if (more) dequant_store(bc, buf0);
-      __syncthreads();
-    }
+    step(st, aA, aB, buf0, buf1, bcA, bcB);
+    if (st + 1 >= nsteps) break;
+    step(st + 1, aB, aA, buf1, buf0, bcB, bcA);
   }
 
   // ---- store C (bf16), lane layout of the 32x32 accumulators
