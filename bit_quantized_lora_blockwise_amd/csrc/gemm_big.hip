@@ -222,22 +222,6 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) *(LDS_AS u32x4*)(dst + 32 + 8 * j) = dequant8(L, bc.c1[j]);
   };
-  auto mma_step = [&](const u32x4 (&a)[2][4], const LDS_AS uint16_t* buf) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, a[0][s]);
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, a[1][s]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bf16x8 b = kDx ? qk::frag_kmajor(buf, kPD, 16 * s, 32 * j) : qk::frag_rowmajor(buf, kPF, 32 * j, 16 * s);
-        acc[0][j] = qk::mfma32(a0, b, acc[0][j]);
-        acc[1][j] = qk::mfma32(a1, b, acc[1][j]);
-      }
-      // keep at most one sub-step of B fragments live (register pressure)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
   // ---- main loop.  Step st multiplies A(st) (registers) by the B tile in LDS
   // buffer st % 2 while it dequantises block codes(st + 1) into the other
   // buffer; the codes are loaded two steps ahead and the A fragments one step
@@ -252,15 +236,25 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     load_a((st + 1) * kBR, anext);
     const BlockLut L = make_lut(qk::e4m3fn_to_f32(bc_now.c2b) * bc_now.c1v, p);
     LDS_AS uint16_t* dst = kDx ? bnext + (t >> 2) * kPD + 64 * (t & 3) : bnext + t * kPF;
+    // B fragments of sub-step s + 1 are read from LDS while sub-step s runs
+    auto bfrag = [&](int s, int j) {
+      return kDx ? qk::frag_kmajor(bcur, kPD, 16 * s, 32 * j) : qk::frag_rowmajor(bcur, kPF, 32 * j, 16 * s);
+    };
+    bf16x8 bq[2][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[0][j] = bfrag(0, j);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bq[(s + 1) & 1][j] = bfrag(s + 1, j);
+      }
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, acur[0][s]);
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, acur[1][s]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const bf16x8 b = kDx ? qk::frag_kmajor(bcur, kPD, 16 * s, 32 * j) : qk::frag_rowmajor(bcur, kPF, 32 * j, 16 * s);
-        acc[0][j] = qk::mfma32(a0, b, acc[0][j]);
-        acc[1][j] = qk::mfma32(a1, b, acc[1][j]);
+        acc[0][j] = qk::mfma32(a0, bq[s & 1][j], acc[0][j]);
+        acc[1][j] = qk::mfma32(a1, bq[s & 1][j], acc[1][j]);
       }
       // two of the eight 8-weight groups of the next tile per sub-step
       const u32x4 cw = (s < 2) ? bc_now.c0 : bc_now.c1;
@@ -269,14 +263,15 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
         const int q = 2 * (s & 1) + h;          // code word within cw
         *(LDS_AS u32x4*)(dst + 32 * (s >> 1) + 8 * q) = dequant8(L, cw[q]);
       }
-      // interleave: one B-fragment read, two MFMAs and VALU work, eight times
+      // schedule: the next sub-step's fragment reads first, then MFMA pairs
+      // interleaved with the dequantisation VALU work, then the LDS stores
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 16 : 8, 0);   // DS read
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 2 : 1, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);             // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);             // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                        // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kDx ? 14 : 11, 0);            // VALU
       }
-      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);               // DS write
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);                          // DS write
     }
     __syncthreads();
   };
