@@ -135,7 +135,11 @@ def kernel_rooflines(lins, reps):
         ms = time_launches(both(fns), reps) / len(fns)       # average per launch over the shape mix
         avg_flops = sum(flops) / len(flops)
         tf = avg_flops / (ms * 1e-3) / 1e12
-        out[name] = {"avg_ms": ms, "flops_per_launch": avg_flops, "tflops": tf}
+        per_shape = {}
+        for L, f, fl in zip(lins, fns, flops):
+            sms = time_launches(f, reps)
+            per_shape[f"{L.K}->{L.N}"] = {"ms": sms, "tflops": fl / (sms * 1e-3) / 1e12}
+        out[name] = {"avg_ms": ms, "flops_per_launch": avg_flops, "tflops": tf, "per_shape": per_shape}
     return out
 
 

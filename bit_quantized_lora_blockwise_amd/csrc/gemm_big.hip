@@ -1,28 +1,36 @@
-// Quantised GEMMs of the layer for training-sized M, large-tile version:
+// Quantised GEMMs of the layer for training-sized M:
 //   forward  Y  = bf16(X W'^T + s T L2)       (C = Y,  P = N, reduction R = K)
 //   backward dX = bf16(dY W' + G L1^T)        (C = dX, P = K, reduction R = N)
 // Layer formula: nlp-lineage milestone page on QLoRA, "The idea", notation
 // paragraph; the frozen base is dequantised on the fly (examadda page, "The
 // Core Idea"; inferensys glossary, paragraph on the dequantising kernel).
 //
-// Tile: 256 rows of the activation x 256 output columns, reduction steps of 64.
-// Four waves; wave w owns activation rows 64 w .. 64 w + 63 and all 256 output
-// columns, i.e. 2 x 8 MFMA 32x32x16 tiles (256 fp32 accumulators per lane).
-//  * The activation (X or dY) goes straight from HBM into MFMA A fragments,
-//    one step ahead; no wave shares them.
-//  * The weight tile is rebuilt from the packed 4-bit stream once per work
-//    group: each thread dequantises one first-level block (64 weights) per step
-//    into a double-buffered LDS tile, and every wave reads its B fragments from
-//    there (directly in the forward, through ds_read_b64_tr_b16 in the dX path,
-//    where the reduction runs across the stored rows of W).
+// Tile: 256 activation rows x 256 output columns, reduction steps of 64.
+// 512 threads = eight waves, two per SIMD, so that the dequantisation VALU
+// work of one wave fills the gaps between the MFMAs of the other (a single
+// wave barely overlaps its own VALU work with its MFMAs on gfx950).  Wave w
+// owns rows 64 (w % 4) .. +64 and columns 128 (w / 4) .. +128 of the tile:
+// 2 x 4 MFMA 32x32x16 tiles, 128 fp32 accumulators per lane.
+//  * Activation tile of a step (256 x 64 bf16): each wave loads 32 of its rows
+//    with coalesced 16-byte loads (eight rows of 128 bytes per load), two steps
+//    ahead, and stores them at the end of the step before into a
+//    double-buffered LDS tile, XOR-swizzled so that fragment reads are free of
+//    bank conflicts.  The two waves of a row group both read from it.
+//  * Weight tile (256 x 64): rebuilt from the packed 4-bit stream once per work
+//    group; each pair of threads owns one first-level block (64 weights) and
+//    each thread converts half of it per step into a double-buffered LDS tile.
+//    The forward reads B fragments directly, the dX path (where the reduction
+//    runs across the stored rows of W) through ds_read_b64_tr_b16.
 //  * Dequantisation keeps the block's 16 bf16 values W'(v) = bf16(fl32(q[v] s'))
 //    in registers as two byte planes and looks each nibble up with v_perm_b32
 //    (three byte selects per four nibbles and plane), so it needs no LDS reads.
+//  * Work groups are dispatched round-robin over the 8 XCDs; the tile order is
+//    remapped so that each XCD (with its own L2) gets a contiguous run of tiles.
 #include "kernels.h"
 
 namespace {
 
-constexpr int kT = 256;           // threads per work group
+constexpr int kT = 512;           // threads per work group
 constexpr int kBM = 256;          // activation rows per tile
 constexpr int kBP = 256;          // output columns per tile
 constexpr int kBR = 64;           // reduction per step
@@ -30,7 +38,8 @@ constexpr int kPF = kBR + 8;      // pitch of the forward B tile [p][r] (element
 constexpr int kPD = kBP + 32;     // pitch of the dX B tile [r][p] (elements): 144 dwords, so the
                                   // 4 rows x 2 column halves of a 32-lane transposed read hit 64 banks
 constexpr int kBufElems = (kBP * kPF > kBR * kPD) ? kBP * kPF : kBR * kPD;
-constexpr int kPL = 64 + 8;       // pitch of the LoRA A tile [m][c]
+constexpr int kPL = 64 + 8;       // pitch of the LoRA operand tiles [row][c]
+
 constexpr uint32_t kOOB = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint64_t bytes) {
@@ -98,15 +107,17 @@ __device__ __forceinline__ u32x4 dequant8(const BlockLut& L, uint32_t c) {
   return r;
 }
 
-// A block's packed codes, scale byte and group scale, as loaded for one step.
-struct BlockCodes {
-  u32x4 c0, c1;
+// Half a block's packed codes (32 weights), its scale byte and group scale.
+struct HalfCodes {
+  u32x4 c;
   uint32_t c2b;
   float c1v;
 };
 
 // ---------------------------------------------------------------------------
-template <bool kDx>
+// kTail: dX with N not a multiple of 64 (the last step masks activation
+// columns past N).
+template <bool kDx, bool kTail>
 __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict__ A, int64_t M, int64_t K,
                                                      int64_t N, const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ c2,
@@ -115,45 +126,53 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ LB,   // L2 (fwd) / L1 (dX)
                                                      int r, float scale, uint16_t* __restrict__ C,
                                                      Nf4Params p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2 * kBufElems];   // weight tiles; LoRA operands first
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2 * kBM * kBR];   // activation tiles
   const int t = threadIdx.x;
-  const int w = t >> 6, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int rg = w & 3, ch = w >> 2;      // row group (64 rows), column half (128 columns)
   const int64_t P = kDx ? K : N;          // output columns
   const int64_t R = kDx ? N : K;          // reduction length
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int64_t p0 = (int64_t)blockIdx.x * kBP;
   const int64_t kblocks = K / qk::kBlock;
 
-  f32x16 acc[2][8];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x16{};
-
-  // ---- LoRA term first, one 32x32 tile at a time: fwd acc = s * (T L2); dX acc = G L1^T
-  //      (rank zero-padded to 64); the base product then accumulates onto it.
+  // ---- tile of this work group: XCD x = (linear id) % 8 takes a contiguous
+  // run of tiles in row-major tile order.
+  int64_t m0, p0;
   {
-    LDS_AS uint16_t* la = (LDS_AS uint16_t*)lds;                 // [256][kPL]: T / G rows
-    LDS_AS uint16_t* lb = (LDS_AS uint16_t*)lds + kBM * kPL;     // fwd: L2 [64][kPD]; dX: L1 [256][kPL]
+    const int nwg = gridDim.x * gridDim.y;
+    const int b = blockIdx.x + gridDim.x * blockIdx.y;
+    const int per = nwg / 8, extra = nwg % 8, xcd = b % 8, q = b / 8;
+    const int tile = xcd < extra ? xcd * (per + 1) + q : extra * (per + 1) + (xcd - extra) * per + q;
+    m0 = (int64_t)(tile / gridDim.x) * kBM;
+    p0 = (int64_t)(tile % gridDim.x) * kBP;
+  }
+
+  f32x16 acc[2][4];
+
+  // ---- LoRA term first: fwd acc = s * (T L2); dX acc = G L1^T (rank zero-padded
+  //      to 64); the base product then accumulates onto it.
+  {
+    LDS_AS uint16_t* la = (LDS_AS uint16_t*)lds_b;                 // [256][kPL]: T / G rows
+    LDS_AS uint16_t* lb = (LDS_AS uint16_t*)lds_b + kBM * kPL;     // fwd: L2 [64][kPD]; dX: L1 [256][kPL]
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (t >> 3) + 32 * i, cc = (t & 7) * 8;
+    for (int i = 0; i < 4; ++i) {
+      const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
       u32x4 v = {0, 0, 0, 0};
       if (m0 + row < M) v = load_row8(LA + (m0 + row) * r, cc, r);
       *(LDS_AS u32x4*)(la + row * kPL + cc) = v;
     }
     if (!kDx) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = (t >> 5) + 8 * i, pp = (t & 31) * 8;
+      for (int i = 0; i < 4; ++i) {
+        const int c = (t >> 5) + 16 * i, pp = (t & 31) * 8;
         u32x4 v = {0, 0, 0, 0};
         if (c < r) v = load_row8(LB + (int64_t)c * N, p0 + pp, N);
         *(LDS_AS u32x4*)(lb + c * kPD + pp) = v;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = (t >> 3) + 32 * i, cc = (t & 7) * 8;
+      for (int i = 0; i < 4; ++i) {
+        const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
         u32x4 v = {0, 0, 0, 0};
         if (p0 + row < K) v = load_row8(LB + (p0 + row) * r, cc, r);
         *(LDS_AS u32x4*)(lb + row * kPL + cc) = v;
@@ -165,11 +184,12 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         f32x16 z = {};
         for (int s = 0; s < ksteps; ++s) {
-          const bf16x8 a = qk::frag_rowmajor(la, kPL, 64 * w + 32 * i, 16 * s);
-          const bf16x8 b = kDx ? qk::frag_rowmajor(lb, kPL, 32 * j, 16 * s) : qk::frag_kmajor(lb, kPD, 16 * s, 32 * j);
+          const bf16x8 a = qk::frag_rowmajor(la, kPL, 64 * rg + 32 * i, 16 * s);
+          const bf16x8 b = kDx ? qk::frag_rowmajor(lb, kPL, 128 * ch + 32 * j, 16 * s)
+                               : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
           z = qk::mfma32(a, b, z);
         }
         acc[i][j] = ls * z;
@@ -177,129 +197,164 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     __syncthreads();
   }
 
-  // ---- per-thread roles
-  // A fragments: rows m0 + 64 w + 32 i + l % 32, reduction columns 16 s + 8 (l / 32).
-  const __amdgpu_buffer_rsrc_t ra = rsrc(A, (uint64_t)M * R * 2);
-  const int64_t arow0 = m0 + 64 * w + (l & 31);
-  const uint32_t aoff0 = (uint32_t)(arow0 * R * 2) + 16u * (uint32_t)(l >> 5);
-  const uint32_t aoff1 = aoff0 + (uint32_t)(32 * R * 2);
-  const bool arow0_ok = arow0 < M, arow1_ok = arow0 + 32 < M;
-  auto load_a = [&](int64_t rs, u32x4 (&a)[2][4]) {   // rs: first reduction index of the step
+  // ---- activation tiles.  Wave w loads rows 64 (w % 4) + 32 (w / 4) .. +32 of
+  // the tile, eight rows per 16-byte load (lane l: row + l / 8, slot l % 8).
+  // In LDS, row rho keeps its 16-byte chunk c in slot c ^ ((rho >> 1) & 7): the
+  // lane loads chunk (l % 8) ^ (that swizzle) and stores linearly.
+  uint32_t achunk[2], arow_off[4];
+  achunk[0] = (uint32_t)((l & 7) ^ (l >> 4));     // rows with (rho >> 1) & 7 = l / 16
+  achunk[1] = achunk[0] ^ 4u;                     // rows with (rho >> 1) & 7 = 4 + l / 16
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t col = rs + 16 * s + 8 * (l >> 5);
-      const bool cok = col < R;
-      const uint32_t d = (uint32_t)(rs * 2 + 32 * s);
-      a[0][s] = __builtin_amdgcn_raw_buffer_load_b128(ra, (arow0_ok && cok) ? aoff0 + d : kOOB, 0, 0);
-      a[1][s] = __builtin_amdgcn_raw_buffer_load_b128(ra, (arow1_ok && cok) ? aoff1 + d : kOOB, 0, 0);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int row = 64 * rg + 32 * ch + 8 * j + (l >> 3);
+    arow_off[j] = (uint32_t)((int64_t)row * R * 2) + 16u * achunk[j & 1];
+  }
+  // Step st reads through a descriptor based at column 64 st of the tile's first
+  // row whose size ends at the end of A: rows past M read as zeros, and a step
+  // past the reduction has size 0.
+  auto load_a = [&](int64_t st, u32x4 (&v)[4]) {
+    const int64_t left = R - st * kBR;
+    const int rem = __builtin_amdgcn_readfirstlane((int)(left < kBR ? left : kBR));   // columns in this step
+    const uint64_t nrec = rem > 0 ? (uint64_t)(M - m0) * R * 2 - (uint64_t)st * kBR * 2 : 0;
+    const uint64_t base = (uint64_t)(uintptr_t)(A + m0 * R + (rem > 0 ? st * kBR : 0));
+    const uint16_t* pa = (const uint16_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base));
+    const __amdgpu_buffer_rsrc_t ra = rsrc(pa, (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)nrec));
+    const bool ok0 = !kTail || 8 * (int)achunk[0] < rem;    // chunks past the reduction read as zeros
+    const bool ok1 = !kTail || 8 * (int)achunk[1] < rem;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, ((j & 1) ? ok1 : ok0) ? arow_off[j] : kOOB, 0, 0);
   };
-  // Dequantisation role: one block per thread per step.
-  //  fwd: weight row p0 + t, block = step;            tile position [t][0..64)
-  //  dX : weight row rs + t / 4, block (p0 / 64) + t % 4; tile position [t / 4][64 (t % 4) ..)
+  auto store_a = [&](const u32x4 (&v)[4], LDS_AS uint16_t* abuf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *(LDS_AS u32x4*)(abuf + (64 * rg + 32 * ch + 8 * j) * kBR + 8 * l) = v[j];
+  };
+  // A fragment of sub-step s, tile i: row 64 (w % 4) + 32 i + l % 32, chunk 2 s + l / 32.
+  uint32_t afrag_off[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    afrag_off[s] = (uint32_t)((64 * rg + (l & 31)) * kBR * 2 + 16 * ((2 * s + (l >> 5)) ^ ((l >> 1) & 7)));
+  auto afrag = [&](const LDS_AS uint16_t* abuf, int s, int i) {
+    return *(const LDS_AS bf16x8*)((const LDS_AS char*)abuf + afrag_off[s] + 32 * kBR * 2 * i);
+  };
+
+  // ---- weight tiles.  The thread pair (2 u, 2 u + 1) owns one block per step,
+  // thread 2 u + h converts its half h (32 weights):
+  //  fwd: weight row p0 + t / 2, block = step;                  tile [t / 2][32 h ..)
+  //  dX : weight row 64 step + t / 8, block p0 / 64 + (t / 2) % 4; tile [t / 8][64 ((t / 2) % 4) + 32 h ..)
   const __amdgpu_buffer_rsrc_t rc = rsrc(codes, (uint64_t)N * (K / 2));
   const __amdgpu_buffer_rsrc_t r2 = rsrc(c2, (uint64_t)N * kblocks);
   const __amdgpu_buffer_rsrc_t r1 = rsrc(c1, 4 * (((uint64_t)N * kblocks + 255) / 256));
+  const int half = t & 1;
   auto load_codes = [&](int64_t step) {
     int64_t wrow, kb;
-    if (!kDx) { wrow = p0 + t; kb = step; }
-    else { wrow = step * kBR + (t >> 2); kb = p0 / 64 + (t & 3); }
-    const bool ok = wrow < N && kb < kblocks;
-    const uint32_t co = ok ? (uint32_t)(wrow * (K / 2) + kb * 32) : kOOB;
+    if (!kDx) { wrow = p0 + (t >> 1); kb = step; }
+    else { wrow = step * kBR + (t >> 3); kb = p0 / 64 + ((t >> 1) & 3); }
+    // out-of-range blocks get bit 31 set in their offsets: past every buffer end
+    const uint32_t oob = (wrow < N && kb < kblocks) ? 0u : kOOB;
     const uint32_t b = (uint32_t)(wrow * kblocks + kb);
-    BlockCodes bc;
-    bc.c0 = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
-    bc.c1 = __builtin_amdgcn_raw_buffer_load_b128(rc, co + 16, 0, 0);
-    bc.c2b = __builtin_amdgcn_raw_buffer_load_b8(r2, ok ? b : kOOB, 0, 0);
-    bc.c1v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ok ? 4 * (b >> 8) : kOOB, 0, 0));
-    return bc;
+    HalfCodes hc;
+    hc.c = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)(wrow * (K / 2) + kb * 32 + 16 * half) | oob, 0, 0);
+    hc.c2b = __builtin_amdgcn_raw_buffer_load_b8(r2, b | oob, 0, 0);
+    hc.c1v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (4 * (b >> 8)) | oob, 0, 0));
+    return hc;
   };
-  auto dequant_store = [&](const BlockCodes& bc, LDS_AS uint16_t* buf) {
-    const BlockLut L = make_lut(qk::e4m3fn_to_f32(bc.c2b) * bc.c1v, p);
-    LDS_AS uint16_t* dst = kDx ? buf + (t >> 2) * kPD + 64 * (t & 3) : buf + t * kPF;
+  const int dq_off = kDx ? (t >> 3) * kPD + 64 * ((t >> 1) & 3) + 32 * half : (t >> 1) * kPF + 32 * half;
+  auto dequant_store = [&](const HalfCodes& hc, LDS_AS uint16_t* buf) {
+    const BlockLut L = make_lut(qk::e4m3fn_to_f32(hc.c2b) * hc.c1v, p);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(LDS_AS u32x4*)(dst + 8 * j) = dequant8(L, bc.c0[j]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(LDS_AS u32x4*)(dst + 32 + 8 * j) = dequant8(L, bc.c1[j]);
+    for (int q = 0; q < 4; ++q) *(LDS_AS u32x4*)(buf + dq_off + 8 * q) = dequant8(L, hc.c[q]);
   };
-  // ---- main loop.  Step st multiplies A(st) (registers) by the B tile in LDS
-  // buffer st % 2 while it dequantises block codes(st + 1) into the other
-  // buffer; the codes are loaded two steps ahead and the A fragments one step
-  // ahead.  The body has no branches (out-of-range steps load zeros), so the
-  // MFMAs, the dequantisation VALU work and the LDS traffic interleave.
-  LDS_AS uint16_t* buf0 = (LDS_AS uint16_t*)lds;
-  LDS_AS uint16_t* buf1 = (LDS_AS uint16_t*)lds + kBufElems;
+
+  // ---- main loop.  At the top of step st: LDS holds activation tile st and
+  // weight tile st; registers hold codes(st + 1) and activation tile st + 1.
+  // Step st multiplies, converts codes(st + 1) into the other weight buffer,
+  // loads codes(st + 2) and activation tile st + 2, and stores tile st + 1 into
+  // the other activation buffer at its end.
+  LDS_AS uint16_t* b0 = (LDS_AS uint16_t*)lds_b;
+  LDS_AS uint16_t* b1 = (LDS_AS uint16_t*)lds_b + kBufElems;
+  LDS_AS uint16_t* a0 = (LDS_AS uint16_t*)lds_a;
+  LDS_AS uint16_t* a1 = (LDS_AS uint16_t*)lds_a + kBM * kBR;
   const int64_t nsteps = (R + kBR - 1) / kBR;
-  auto step = [&](int64_t st, const u32x4 (&acur)[2][4], u32x4 (&anext)[2][4], const LDS_AS uint16_t* bcur,
-                  LDS_AS uint16_t* bnext, const BlockCodes& bc_now, BlockCodes& bc_later) {
-    bc_later = load_codes(st + 2);
-    load_a((st + 1) * kBR, anext);
-    const BlockLut L = make_lut(qk::e4m3fn_to_f32(bc_now.c2b) * bc_now.c1v, p);
-    LDS_AS uint16_t* dst = kDx ? bnext + (t >> 2) * kPD + 64 * (t & 3) : bnext + t * kPF;
-    // B fragments of sub-step s + 1 are read from LDS while sub-step s runs
+  auto step = [&](int64_t st, const LDS_AS uint16_t* acur, LDS_AS uint16_t* anext, const LDS_AS uint16_t* bcur,
+                  LDS_AS uint16_t* bnext, const HalfCodes& hc_now, HalfCodes& hc_later, const u32x4 (&av_now)[4],
+                  u32x4 (&av_later)[4]) {
+    hc_later = load_codes(st + 2);
+    load_a(st + 2, av_later);
+    __builtin_amdgcn_sched_barrier(0);
+    const BlockLut L = make_lut(qk::e4m3fn_to_f32(hc_now.c2b) * hc_now.c1v, p);
+    LDS_AS uint16_t* dst = bnext + dq_off;
+    // fragments of sub-step s + 1 are read from LDS while sub-step s runs
     auto bfrag = [&](int s, int j) {
-      return kDx ? qk::frag_kmajor(bcur, kPD, 16 * s, 32 * j) : qk::frag_rowmajor(bcur, kPF, 32 * j, 16 * s);
+      return kDx ? qk::frag_kmajor(bcur, kPD, 16 * s, 128 * ch + 32 * j)
+                 : qk::frag_rowmajor(bcur, kPF, 128 * ch + 32 * j, 16 * s);
     };
-    bf16x8 bq[2][8];
+    bf16x8 bq[2][4], aq[2][2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bq[0][j] = bfrag(0, j);
+    for (int j = 0; j < 4; ++j) bq[0][j] = bfrag(0, j);
+    aq[0][0] = afrag(acur, 0, 0);
+    aq[0][1] = afrag(acur, 0, 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s < 3) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bq[(s + 1) & 1][j] = bfrag(s + 1, j);
+        for (int j = 0; j < 4; ++j) bq[(s + 1) & 1][j] = bfrag(s + 1, j);
+        aq[(s + 1) & 1][0] = afrag(acur, s + 1, 0);
+        aq[(s + 1) & 1][1] = afrag(acur, s + 1, 1);
       }
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, acur[0][s]);
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, acur[1][s]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc[0][j] = qk::mfma32(a0, bq[s & 1][j], acc[0][j]);
-        acc[1][j] = qk::mfma32(a1, bq[s & 1][j], acc[1][j]);
+      for (int j = 0; j < 4; ++j) {
+        acc[0][j] = qk::mfma32(aq[s & 1][0], bq[s & 1][j], acc[0][j]);
+        acc[1][j] = qk::mfma32(aq[s & 1][1], bq[s & 1][j], acc[1][j]);
       }
-      // two of the eight 8-weight groups of the next tile per sub-step
-      const u32x4 cw = (s < 2) ? bc_now.c0 : bc_now.c1;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int q = 2 * (s & 1) + h;          // code word within cw
-        *(LDS_AS u32x4*)(dst + 32 * (s >> 1) + 8 * q) = dequant8(L, cw[q]);
-      }
-      // schedule: the next sub-step's fragment reads first, then MFMA pairs
-      // interleaved with the dequantisation VALU work, then the LDS stores
-      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 16 : 8, 0);   // DS read
+      // one 8-weight group of the next weight tile per sub-step
+      *(LDS_AS u32x4*)(dst + 8 * s) = dequant8(L, hc_now.c[s]);
+      // schedule: the next sub-step's fragment reads first, then one MFMA at a
+      // time interleaved with the dequantisation VALU work, then the LDS store
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 10 : 6, 0);   // DS read
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                        // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, kDx ? 14 : 11, 0);            // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                         // VALU
       }
-      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);                          // DS write
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                           // DS write
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(av_now, anext);
+    // this wave's LDS stores are done; the barrier hands both new tiles to all
+    // waves (the fragment reads of this step completed before their MFMAs)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  u32x4 aA[2][4], aB[2][4];
-  BlockCodes bcA, bcB;
+  HalfCodes hA, hB;
+  u32x4 avA[4], avB[4];
   {
-    const BlockCodes bc0 = load_codes(0);
-    bcA = load_codes(1);
-    load_a(0, aA);
-    dequant_store(bc0, buf0);
-    __syncthreads();
+    const HalfCodes h0 = load_codes(0);
+    hA = load_codes(1);
+    u32x4 av0[4];
+    load_a(0, av0);
+    load_a(1, avA);
+    dequant_store(h0, b0);
+    store_a(av0, a0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  // bcA holds codes(st + 1) at the top of each even step
+  // Steps in pairs with no exit between them, so that the loop body is one
+  // basic block and the early loads stay where they are issued; an odd step
+  // count runs one more step over zeros (codes and activations past the end).
   for (int64_t st = 0; st < nsteps; st += 2) {
-    step(st, aA, aB, buf0, buf1, bcA, bcB);
-    if (st + 1 >= nsteps) break;
-    step(st + 1, aB, aA, buf1, buf0, bcB, bcA);
+    step(st, a0, a1, b0, b1, hA, hB, avA, avB);
+    step(st + 1, a1, a0, b1, b0, hB, hA, avB, avA);
   }
 
   // ---- store C (bf16), lane layout of the 32x32 accumulators
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t pc = p0 + 32 * j + qk::acc_col();
+    for (int j = 0; j < 4; ++j) {
+      const int64_t pc = p0 + 128 * ch + 32 * j + qk::acc_col();
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + 64 * w + 32 * i + qk::acc_row(e);
+        const int64_t m = m0 + 64 * rg + 32 * i + qk::acc_row(e);
         if (m < M && pc < P) C[m * P + pc] = qk::f32_to_bf16(acc[i][j][e]);
       }
     }
@@ -318,11 +373,14 @@ hipError_t launch_qgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, in
                             float scale, uint16_t* C, hipStream_t s) {
   const int64_t P = dx ? K : N;
   dim3 grid((unsigned)((P + kBP - 1) / kBP), (unsigned)((M + kBM - 1) / kBM));
-  if (dx)
-    hipLaunchKernelGGL(k_qgemm_big<true>, grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r, scale, C,
-                       nf4_params());
+  if (!dx)
+    hipLaunchKernelGGL((k_qgemm_big<false, false>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
+                       scale, C, nf4_params());
+  else if (N % kBR == 0)
+    hipLaunchKernelGGL((k_qgemm_big<true, false>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
+                       scale, C, nf4_params());
   else
-    hipLaunchKernelGGL(k_qgemm_big<false>, grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r, scale, C,
-                       nf4_params());
+    hipLaunchKernelGGL((k_qgemm_big<true, true>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
+                       scale, C, nf4_params());
   return hipGetLastError();
 }
