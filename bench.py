@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="only launch each fused GEMM a few times on the headline shapes, then a plain "
+                         "512 MiB device copy (the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -97,6 +100,29 @@ class Linear:
 
     def flops(self):
         return layer_flops(self.M, self.K, self.N, self.r)
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_qgemm_llama7b_m4096.md")
+GEMM_SOURCE = os.path.join(ROOT, "bit_quantized_lora_blockwise_amd", "csrc", "gemm_big.hip")
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None when the GEMM source has changed since those counters were
+    taken (the summary records the source's sha256)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if f"gemm_big.hip sha256 {sha}" not in text:
+        return None
+    for line in text.splitlines():
+        parts = line.split()
+        if len(parts) == 3 and parts[0] == "traffic_bytes_per_launch" and parts[1] == kernel:
+            return float(parts[2])
+    return None
 
 
 def time_launches(fn, reps):
@@ -252,6 +278,28 @@ def cpu_baseline():
                       "dequant + fwd + bwd, float64 NumPy oracle on the host"}
 
 
+def pmc_probe(lins, reps=3):
+    """Launches for hardware-counter runs: fused forward and dX GEMMs of both
+    headline linears, then one copy of 512 MiB (bytes read = bytes written =
+    2^29), the known-size reference for the traffic counters."""
+    import torch
+    q = lins[0].q
+    for L in lins:
+        q.qlora_lora_down(L.X, L.L1, T=L.T)
+        q.qlora_lora_grad_in(L.dY, L.L2, 1.0, G=L.G)
+    for _ in range(reps):
+        for L in lins:
+            q.qlora_linear_fwd_t(L.X, L.codes, L.c2, L.c1, L.N, L.T, L.L2, 1.0, Y=L.Y)
+            q.qlora_linear_dx(L.dY, L.codes, L.c2, L.c1, L.K, L.G, L.L1, dX=L.dX)
+    torch.cuda.synchronize()
+    src = torch.empty((1 << 28,), dtype=torch.int16, device=lins[0].X.device).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_probe": "done", "gemm_launches_per_kind": reps * len(lins), "copy_bytes": 1 << 29}))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -269,6 +317,11 @@ def main():
     c3 = WL.config3()
     lins = [Linear(c3["up"], dev), Linear(c3["down"], dev)]
     del c3
+    if args.pmc_probe:
+        for L in lins:
+            L.encode()
+        pmc_probe(lins)
+        return
 
     def step():
         for L in lins:
@@ -300,7 +353,7 @@ def main():
     kern = kernel_rooflines(lins, args.kernel_reps)
     dom = max(kern, key=lambda k: kern[k]["avg_ms"])
     roof = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": kern[dom]["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": kern[dom]["tflops"] / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(dom),
             "avg_launch_ms": kern[dom]["avg_ms"], "flops_per_launch": kern[dom]["flops_per_launch"]}
     del lins
     torch.cuda.empty_cache()
