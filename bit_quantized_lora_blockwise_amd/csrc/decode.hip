@@ -142,25 +142,21 @@ __global__ __launch_bounds__(kThreads) void k_qgemv_fwd(const uint16_t* __restri
   const __amdgpu_buffer_rsrc_t r1 = rsrc(c1, 4 * (((uint64_t)N * kblocks + 255) / 256));
   const __amdgpu_buffer_rsrc_t rx = rsrc(X, (uint64_t)M * K * 2);
 
-  // ---- X into LDS first (small X): every 16-byte group of eight columns is
-  // stored as (0, 2, 4, 6, 1, 3, 5, 7); the staging completes before any code
-  // load is issued.
+  // ---- small X: its loads are issued first, then the first chunk of the code
+  // stream, then X is written to LDS (waiting for the X loads only).  Every
+  // 16-byte group of eight columns is stored as (0, 2, 4, 6, 1, 3, 5, 7).
   LDS_AS uint8_t* xl = (LDS_AS uint8_t*)lds;
+  constexpr int kXPer = kXBytes / (16 * kThreads);       // 16-byte X loads per thread
+  u32x4 xr[kXLds ? kXPer : 1];
+  const uint32_t xbytes = kXLds ? (uint32_t)(M * K * 2) : 0u;
   if (kXLds) {
-    const uint32_t xbytes = (uint32_t)(M * K * 2);
-    for (uint32_t o = 16u * (uint32_t)t; o < xbytes; o += 16u * kThreads) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
-      u32x4 e;
-      e[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
-      e[1] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
-      e[2] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
-      e[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
-      *(LDS_AS u32x4*)(xl + o) = e;
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j) {
+      const uint32_t o = 16u * (uint32_t)(t + j * kThreads);
+      xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, o < xbytes ? o : kOOB, 0, 0);
     }
-    if (t < kZeroBytes / 16) *(LDS_AS u32x4*)(xl + kXBytes + 16 * t) = u32x4{0, 0, 0, 0};
-    __syncthreads();
   }
-
+  __builtin_amdgcn_sched_barrier(0);
   // ---- code stream: chunk c covers steps 4c .. 4c + 3 of the lane
   const uint32_t code_row = (uint32_t)(nrow * (K / 2));
   const uint32_t blk_row = (uint32_t)(nrow * kblocks);
@@ -202,6 +198,22 @@ __global__ __launch_bounds__(kThreads) void k_qgemv_fwd(const uint16_t* __restri
       ll[j] = vl[2 * j] | (vl[2 * j + 1] << 16);
       lt[j] = vt[2 * j] | (vt[2 * j + 1] << 16);
     }
+  }
+
+  if (kXLds) {
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j) {
+      const uint32_t o = 16u * (uint32_t)(t + j * kThreads);
+      const u32x4 v = xr[j];
+      u32x4 e;
+      e[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+      e[1] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+      e[2] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+      e[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+      if (o < xbytes) *(LDS_AS u32x4*)(xl + o) = e;
+    }
+    if (t < kZeroBytes / 16) *(LDS_AS u32x4*)(xl + kXBytes + 16 * t) = u32x4{0, 0, 0, 0};
+    __syncthreads();
   }
 
   f32x4 acc = {0, 0, 0, 0};
