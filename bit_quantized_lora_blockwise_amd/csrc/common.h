@@ -26,6 +26,18 @@ struct Nf4Params {
   float thr[15];
 };
 
+// Encoder lookup over 34 buckets of width 1/16 in n (index floor(16 n) + 17,
+// n in [-1, 1]); each bucket holds at most one threshold.  For bucket i:
+// t16[i] = 16 * (its threshold), or +inf when it has none; mb[i] = bits of a
+// power-of-two margin m (|16 n' - t16| <= m marks an approximate n' as too
+// close to decide), whose low 4 bits hold the number of thresholds at or below
+// the bucket's lower end.  Built on the host (see nf4_table.cpp).
+struct Nf4Buckets {
+  float t16[34];
+  uint32_t mb[34];
+  int ok;   // 1 when the construction's assumptions held
+};
+
 namespace qk {
 
 static constexpr int kBlock = 64;   // weights per first-level scale

@@ -21,10 +21,27 @@ __device__ __forceinline__ uint32_t dpp_max8(uint32_t v) {
 // One thread encodes 8 consecutive weights; the 8 lanes of an aligned group
 // cover one block of 64 and share its absmax through DPP.  Codes of the 8
 // weights form one 32-bit word (element j in bits 4j..4j+3).
+//
+// The code of n = fl32(w / a) is #{k : n >= thr[k]}.  Instead of dividing and
+// comparing with all 15 thresholds, each weight takes n' = w * (16 / a) from
+// one reciprocal per block (within a few ulp of 16 n), finds its 1/16-wide
+// bucket in a 34-entry LDS table (one 8-byte read: the bucket's threshold, a
+// margin and the count of thresholds below the bucket), and compares once.
+// Weights whose n' lies within the margin of the bucket's threshold -- and
+// all weights of blocks whose absmax is not a normal number -- are redone
+// with the correctly rounded division, so the codes are exactly those of the
+// definition.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict__ W, int64_t n_oct,
                                                          uint32_t* __restrict__ codes,
-                                                         float* __restrict__ absmax, Nf4Params p) {
+                                                         float* __restrict__ absmax, Nf4Buckets bk) {
+  __shared__ __attribute__((aligned(8))) uint32_t tab[34 * 2];
+  if (threadIdx.x < 34) {
+    tab[2 * threadIdx.x] = __float_as_uint(bk.t16[threadIdx.x]);
+    tab[2 * threadIdx.x + 1] = bk.mb[threadIdx.x];
+  }
+  __syncthreads();
+  const uint32_t tab_base = (uint32_t)(uintptr_t)(LDS_AS uint32_t*)tab;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t o = (int64_t)blockIdx.x * kThreads + threadIdx.x; o < n_oct; o += stride) {
     float w[8];
@@ -49,14 +66,34 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict_
     for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(w[j]) & 0x7FFFFFFFu);
     m = dpp_max8(m);
     const float a = __uint_as_float(m);
-    uint32_t packed = 0;
+    // 16 / a for a normal absmax; an all-zero block gives n' = 0 (codes 7)
+    const bool a_normal = m >= 0x00800000u;
+    const float y16 = a_normal ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
+    uint32_t packed = 0, redo = (m != 0 && !a_normal) ? 0xFFu : 0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float n = (m == 0) ? 0.0f : w[j] / a;  // correctly rounded fp32 division
-      uint32_t c = 0;
-#pragma unroll
-      for (int k = 0; k < 15; ++k) c += (n >= p.thr[k]) ? 1u : 0u;
+      const float n16 = w[j] * y16;
+      const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);   // bucket (clamped: non-finite input)
+      const uint32_t addr = tab_base + 8u * (uint32_t)bi;
+      const float t16 = __uint_as_float(*(const LDS_AS uint32_t*)(uintptr_t)addr);
+      const uint32_t mb = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
+      const uint32_t c = (mb & 15u) + (n16 >= t16 ? 1u : 0u);
+      redo |= (__builtin_fabsf(n16 - t16) <= __uint_as_float(mb) ? 1u : 0u) << j;
       packed |= c << (4 * j);
+    }
+    if (redo) {
+      // correctly rounded quotient for the undecided weights
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if ((redo >> j) & 1u) {
+          const float n = (m == 0) ? 0.0f : w[j] / a;
+          const float n16 = 16.0f * n;                            // exact
+          const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);
+          const float t16 = __uint_as_float(tab[2 * bi]);
+          const uint32_t c = (tab[2 * bi + 1] & 15u) + (n16 >= t16 ? 1u : 0u);
+          packed = (packed & ~(15u << (4 * j))) | (c << (4 * j));
+        }
+      }
     }
     codes[o] = packed;
     if ((threadIdx.x & 7) == 0) absmax[o >> 3] = a;
@@ -144,12 +181,13 @@ hipError_t launch_nf4_encode(const void* W, bool bf16, int64_t elems, uint8_t* c
                              hipStream_t s) {
   const int64_t n_oct = elems / 8;
   const int grid = grid_for(n_oct, kThreads);
+  if (!nf4_buckets().ok) return hipErrorInvalidValue;   // table assumptions (checked once on the host)
   if (bf16)
     hipLaunchKernelGGL(k_nf4_encode<true>, dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes, absmax,
-                       nf4_params());
+                       nf4_buckets());
   else
     hipLaunchKernelGGL(k_nf4_encode<false>, dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes, absmax,
-                       nf4_params());
+                       nf4_buckets());
   return hipGetLastError();
 }
 

@@ -9,6 +9,7 @@
 #include "common.h"
 
 const Nf4Params& nf4_params();
+const Nf4Buckets& nf4_buckets();
 
 // --- encoder (encode.hip) ---------------------------------------------------
 hipError_t launch_nf4_encode(const void* W, bool bf16, int64_t elems, uint8_t* codes, float* absmax,

@@ -50,9 +50,48 @@ Nf4Params build() {
   return p;
 }
 
+// Bucket table of the encoder.  The approximate quotient n' it is used with
+// is within 2 ulp of the correctly rounded n = w / a (one reciprocal of at most
+// 1 ulp error and one rounded product); the margin is 2^-18 |t16| rounded up to
+// a power of two, far above that, and every threshold must lie farther than
+// the margin from its bucket's ends, so that a quotient placed in a
+// neighbouring bucket still gets the right count.
+Nf4Buckets build_buckets(const Nf4Params& p) {
+  Nf4Buckets b;
+  b.ok = 1;
+  for (int i = 0; i < 34; ++i) {
+    const double lo = i - 17, hi = i - 16;      // bucket covers 16 n in [lo, hi)
+    int base = 0, inside = 0;
+    float t = INFINITY;
+    for (int k = 0; k < 15; ++k) {
+      const double t16 = 16.0 * (double)p.thr[k];
+      if (t16 <= lo) ++base;
+      else if (t16 < hi) { ++inside; t = (float)t16; }
+    }
+    if (inside > 1) b.ok = 0;
+    float m = 1.0f / 65536.0f;                   // margin for buckets without a threshold
+    if (inside == 1) {
+      int e;
+      std::frexp(std::fabs((double)t), &e);      // |t| < 2^e
+      m = std::ldexp(1.0f, e - 18);
+      if ((double)t - lo <= 4.0 * m || hi - (double)t <= 4.0 * m) b.ok = 0;
+    }
+    uint32_t mbits;
+    std::memcpy(&mbits, &m, 4);
+    b.t16[i] = t;
+    b.mb[i] = mbits | (uint32_t)base;            // margin's low mantissa bits are zero
+  }
+  return b;
+}
+
 }  // namespace
 
 const Nf4Params& nf4_params() {
   static const Nf4Params p = build();
   return p;
+}
+
+const Nf4Buckets& nf4_buckets() {
+  static const Nf4Buckets b = build_buckets(nf4_params());
+  return b;
 }
