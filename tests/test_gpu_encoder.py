@@ -120,3 +120,53 @@ def test_double_quant_sweep():
     r_c2, r_c1 = O.nf4_double_quant(a)
     assert_bitexact(c2.cpu().numpy(), r_c2, "c2 sweep")
     assert_bitexact(c1.cpu().numpy().view(np.uint32), r_c1.view(np.uint32), "c1 sweep")
+
+
+def _blocks_with_absmax(vals, a):
+    """Rows of 64 weights: a first, then 63 of `vals` (|v| <= a), zero padded."""
+    per = 63
+    nb = (vals.size + per - 1) // per
+    W = np.zeros((nb, 64), np.float32)
+    W[:, 0] = a
+    body = np.zeros(nb * per, np.float32)
+    body[:vals.size] = vals
+    W[:, 1:] = body.reshape(nb, per)
+    return W
+
+
+def test_nearest_code_sweep():
+    """Codes of weights w with block absmax a = 1 (so n = w exactly), for every
+    fp32 within 2^16 ulp of each code midpoint and of each multiple of 1/16 in
+    [-1, 1], and every 997th fp32 of [-1, 1]; then the same neighbourhoods of
+    the midpoints scaled by a non-power-of-two absmax.  Every code must equal
+    the oracle's nearest-level rule."""
+    one = int(np.float32(1.0).view(np.uint32))
+    pts = [float(m) for m in O.nf4_midpoints()] + [k / 16.0 for k in range(-16, 17)]
+    chunks = []
+    for p in pts:
+        c = int(np.float32(abs(p)).view(np.uint32))
+        lo, hi = max(c - 65536, 0), min(c + 65536, one)
+        v = np.arange(lo, hi + 1, dtype=np.uint32).view(np.float32)
+        chunks.append(v if p >= 0 else -v)
+    stride = np.arange(0, one + 1, 997, dtype=np.uint32).view(np.float32)
+    chunks += [stride, -stride]
+    vals = np.concatenate(chunks)
+    W1 = _blocks_with_absmax(vals, np.float32(1.0))
+    a = np.float32(0.0371)
+    near = []
+    for m in O.nf4_midpoints():
+        x = np.float32(float(m) * float(a))
+        c = int(np.abs(x).view(np.uint32))
+        v = np.arange(c - 64, c + 65, dtype=np.uint32).view(np.float32)
+        near.append(v if x >= 0 else -v)
+    near = np.concatenate(near)
+    near = near[np.abs(near) <= a]
+    Wa = _blocks_with_absmax(near, a)
+    W = np.concatenate([W1, Wa])
+    print(f"[nearest sweep] {vals.size + near.size} weights in {W.shape[0]} blocks", flush=True)
+    import bit_quantized_lora_blockwise_amd as q
+    codes, absmax = q.nf4_quantize(torch.from_numpy(W).to(DEV))
+    torch.cuda.synchronize()
+    r_codes, r_absmax = O.nf4_quantize(W)
+    assert_bitexact(absmax.cpu().numpy().view(np.uint32), r_absmax.view(np.uint32), "sweep absmax")
+    assert_bitexact(codes.cpu().numpy(), r_codes, "sweep codes")
