@@ -9,7 +9,9 @@
 // All four are memory-bound passes over an [M, R] bf16 activation.  Each work
 // group owns a 64-row tile of the long dimension and one slice of the
 // reduction; slices write fp32 partials that a second kernel sums in a fixed
-// order, so results are deterministic.
+// order, so results are deterministic.  Within a slice the 64-wide steps are
+// pipelined: the tiles of step st + 2 are loaded into registers while step st
+// multiplies out of one LDS buffer and step st + 1's tiles go into the other.
 #include "kernels.h"
 
 namespace {
@@ -17,6 +19,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
 constexpr int kPitch = 72;  // 64 + 8 elements of padding per LDS row
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)(bytes < 0x7FFFFFFFull ? bytes : 0x7FFFFFFFull),
+                                           0x00020000);
+}
 
 // 8 consecutive bf16 of a row starting at column `col`, zero past `ncols`.
 __device__ __forceinline__ u32x4 load_row8(const uint16_t* __restrict__ row, int64_t col, int64_t ncols) {
@@ -31,21 +39,44 @@ __device__ __forceinline__ u32x4 load_row8(const uint16_t* __restrict__ row, int
   return v;
 }
 
-__device__ __forceinline__ void store8(LDS_AS uint16_t* dst, u32x4 v) { *(LDS_AS u32x4*)dst = v; }
+// A 64 x 64 bf16 tile of a row-major matrix held in registers: thread t holds
+// rows (t / 8) + 32 i, columns 8 (t % 8) .. +8.
+struct Tile {
+  u32x4 v[2];
+};
 
-// Stage a 64 x 64 tile of a row-major [rows, cols] matrix (rows from r0, cols
-// from c0) into LDS [64][kPitch]; out-of-range entries are zero.
-__device__ __forceinline__ void stage_tile(LDS_AS uint16_t* dst, const uint16_t* __restrict__ src, int64_t ld,
-                                           int64_t rows, int64_t cols, int64_t r0, int64_t c0) {
+// Tile at `base` (its element (0, 0)) of a matrix with `ld` elements per row;
+// rows at or past `rows` and columns at or past `cols` read as zero.  With
+// `vec` (ld and cols multiples of 8) each thread issues two 16-byte buffer
+// loads; otherwise it reads element by element.  `bytes`: extent of the
+// matrix from `base`.
+__device__ __forceinline__ Tile load_tile(const uint16_t* base, int64_t ld, int64_t rows, int64_t cols,
+                                          uint64_t bytes, bool vec) {
+  const int t = threadIdx.x;
+  const int cc = (t & 7) * 8;
+  Tile tl;
+  if (vec) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(base, bytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (t >> 3) + 32 * i;
+      const bool ok = row < rows && cc < cols;
+      tl.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? (uint32_t)((row * ld + cc) * 2) : kOOB, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (t >> 3) + 32 * i;
+      tl.v[i] = (row < rows) ? load_row8(base + row * ld, cc, cols) : u32x4{0, 0, 0, 0};
+    }
+  }
+  return tl;
+}
+
+__device__ __forceinline__ void store_tile(const Tile& tl, LDS_AS uint16_t* dst) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = (t >> 3) + 32 * i;
-    const int cc = (t & 7) * 8;
-    u32x4 v = {0, 0, 0, 0};
-    if (r0 + row < rows) v = load_row8(src + (r0 + row) * ld, c0 + cc, cols);
-    store8(dst + row * kPitch + cc, v);
-  }
+  for (int i = 0; i < 2; ++i) *(LDS_AS u32x4*)(dst + ((t >> 3) + 32 * i) * kPitch + (t & 7) * 8) = tl.v[i];
 }
 
 // C[M, r] partial over one reduction slice: A [M, R] row-major times B, where
@@ -53,36 +84,50 @@ __device__ __forceinline__ void stage_tile(LDS_AS uint16_t* dst, const uint16_t*
 template <bool kBkr>
 __global__ __launch_bounds__(kThreads) void k_lora_skinny(const uint16_t* __restrict__ A, int64_t M, int64_t R,
                                                           const uint16_t* __restrict__ Bm, int r, int64_t chunk,
-                                                          float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kTile * kPitch];
+                                                          float* __restrict__ part, int avec, int bvec) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * kPitch];
   const int w = threadIdx.x >> 6;
   const int wm = w & 1, wc = w >> 1;
   const int64_t m0 = (int64_t)blockIdx.x * kTile;
   const int split = blockIdx.y;
   const int64_t k_beg = split * chunk;
   const int64_t k_end = min(R, k_beg + chunk);
+  const int64_t nsteps = (k_end - k_beg + kTile - 1) / kTile;
+  auto tiles = [&](int64_t st, Tile& ta, Tile& tb) {
+    const int64_t k0 = k_beg + st * kTile;
+    const int64_t kl = k_end - k0;                     // columns of the slice left (<= 0: zeros)
+    const int64_t k0c = kl > 0 ? k0 : 0;
+    ta = load_tile(A + m0 * R + k0c, R, M - m0, kl, (uint64_t)((M - m0) * R - k0c) * 2, avec);
+    if (kBkr) tb = load_tile(Bm + k0c * r, r, kl, r, (uint64_t)((R - k0c) * r) * 2, bvec);
+    else tb = load_tile(Bm + k0c, R, r, kl, (uint64_t)(r * R - k0c) * 2, bvec);
+  };
   f32x16 acc = {};
-  for (int64_t k0 = k_beg; k0 < k_end; k0 += kTile) {
-    stage_tile((LDS_AS uint16_t*)As, A, R, M, k_end, m0, k0);
-    if (kBkr) {
-      // Bs[k][c] = L1[k0 + k][c]
-      stage_tile((LDS_AS uint16_t*)Bs, Bm, r, k_end, r, k0, 0);
-    } else {
-      // Bs[c][k] = L2[c][k0 + k]
-      stage_tile((LDS_AS uint16_t*)Bs, Bm, R, r, k_end, 0, k0);
-    }
-    __syncthreads();
+  auto step = [&](int64_t st, const Tile& na, const Tile& nb, Tile& la, Tile& lb) {
+    tiles(st + 2, la, lb);
+    const LDS_AS uint16_t* as = (const LDS_AS uint16_t*)As[st & 1];
+    const LDS_AS uint16_t* bs = (const LDS_AS uint16_t*)Bs[st & 1];
     if (wc * 32 < r) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bf16x8 a = qk::frag_rowmajor((const LDS_AS uint16_t*)As, kPitch, 32 * wm, 16 * s);
-        bf16x8 b = kBkr ? qk::frag_kmajor((const LDS_AS uint16_t*)Bs, kPitch, 16 * s, 32 * wc)
-                        : qk::frag_rowmajor((const LDS_AS uint16_t*)Bs, kPitch, 32 * wc, 16 * s);
+        bf16x8 a = qk::frag_rowmajor(as, kPitch, 32 * wm, 16 * s);
+        bf16x8 b = kBkr ? qk::frag_kmajor(bs, kPitch, 16 * s, 32 * wc) : qk::frag_rowmajor(bs, kPitch, 32 * wc, 16 * s);
         acc = qk::mfma32(a, b, acc);
       }
     }
+    store_tile(na, (LDS_AS uint16_t*)As[(st + 1) & 1]);
+    store_tile(nb, (LDS_AS uint16_t*)Bs[(st + 1) & 1]);
     __syncthreads();
+  };
+  Tile a0, b0, aA, bA, aB, bB;
+  tiles(0, a0, b0);
+  tiles(1, aA, bA);
+  store_tile(a0, (LDS_AS uint16_t*)As[0]);
+  store_tile(b0, (LDS_AS uint16_t*)Bs[0]);
+  __syncthreads();
+  for (int64_t st = 0; st < nsteps; st += 2) {   // an odd count runs one more step over zeros
+    step(st, aA, bA, aB, bB);
+    step(st + 1, aB, bB, aA, bA);
   }
   if (wc * 32 < r) {
     const int c = 32 * wc + qk::acc_col();
@@ -107,29 +152,49 @@ __global__ __launch_bounds__(kThreads) void k_skinny_reduce(const float* __restr
 // C[p, c] partial over one slice of m: sum_m A[m][p] * B[m][c], A [M, P], B [M, r].
 __global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                       int64_t M, int64_t P, int r, int64_t chunk,
-                                                      float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kTile * kPitch];
+                                                      float* __restrict__ part, int avec, int bvec) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * kPitch];
   const int w = threadIdx.x >> 6;
   const int wp = w & 1, wc = w >> 1;
   const int64_t p0 = (int64_t)blockIdx.x * kTile;
   const int split = blockIdx.y;
   const int64_t m_beg = split * chunk;
   const int64_t m_end = min(M, m_beg + chunk);
+  const int64_t nsteps = (m_end - m_beg + kTile - 1) / kTile;
+  auto tiles = [&](int64_t st, Tile& ta, Tile& tb) {
+    const int64_t mm = m_beg + st * kTile;
+    const int64_t ml = m_end - mm;                     // rows of the slice left (<= 0: zeros)
+    const int64_t mmc = ml > 0 ? mm : 0;
+    ta = load_tile(A + mmc * P + p0, P, ml, P - p0, (uint64_t)((M - mmc) * P - p0) * 2, avec);   // [m][p]
+    tb = load_tile(B + mmc * r, r, ml, r, (uint64_t)((M - mmc) * r) * 2, bvec);                // [m][c]
+  };
   f32x16 acc = {};
-  for (int64_t mm = m_beg; mm < m_end; mm += kTile) {
-    stage_tile((LDS_AS uint16_t*)As, A, P, m_end, P, mm, p0);   // As[m][p]
-    stage_tile((LDS_AS uint16_t*)Bs, B, r, m_end, r, mm, 0);    // Bs[m][c]
-    __syncthreads();
+  auto step = [&](int64_t st, const Tile& na, const Tile& nb, Tile& la, Tile& lb) {
+    tiles(st + 2, la, lb);
+    const LDS_AS uint16_t* as = (const LDS_AS uint16_t*)As[st & 1];
+    const LDS_AS uint16_t* bs = (const LDS_AS uint16_t*)Bs[st & 1];
     if (wc * 32 < r) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bf16x8 a = qk::frag_kmajor((const LDS_AS uint16_t*)As, kPitch, 16 * s, 32 * wp);
-        bf16x8 b = qk::frag_kmajor((const LDS_AS uint16_t*)Bs, kPitch, 16 * s, 32 * wc);
+        bf16x8 a = qk::frag_kmajor(as, kPitch, 16 * s, 32 * wp);
+        bf16x8 b = qk::frag_kmajor(bs, kPitch, 16 * s, 32 * wc);
         acc = qk::mfma32(a, b, acc);
       }
     }
+    store_tile(na, (LDS_AS uint16_t*)As[(st + 1) & 1]);
+    store_tile(nb, (LDS_AS uint16_t*)Bs[(st + 1) & 1]);
     __syncthreads();
+  };
+  Tile a0, b0, aA, bA, aB, bB;
+  tiles(0, a0, b0);
+  tiles(1, aA, bA);
+  store_tile(a0, (LDS_AS uint16_t*)As[0]);
+  store_tile(b0, (LDS_AS uint16_t*)Bs[0]);
+  __syncthreads();
+  for (int64_t st = 0; st < nsteps; st += 2) {
+    step(st, aA, bA, aB, bB);
+    step(st + 1, aB, bB, aA, bA);
   }
   if (wc * 32 < r) {
     const int c = 32 * wc + qk::acc_col();
@@ -165,10 +230,12 @@ int grid_for(int64_t items) {
 
 }  // namespace
 
+// Split of a reduction of length R over `tiles` output tiles: about 384 work
+// groups in all, but at most one slice per 1024 of reduction, so that the fp32
+// partials stay small next to the activation pass.
 SplitPlan plan_rowsplit(int64_t tiles, int64_t R) {
-  const int64_t want = (1024 + tiles - 1) / tiles;
-  const int64_t max_splits = (R + 255) / 256;
-  int64_t splits = want < 1 ? 1 : want;
+  int64_t splits = (384 + tiles - 1) / tiles;
+  const int64_t max_splits = R / 1024;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int64_t chunk = (R + splits - 1) / splits;
@@ -187,10 +254,12 @@ hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, const uin
   const int64_t tiles = (M + kTile - 1) / kTile;
   const SplitPlan sp = plan_rowsplit(tiles, R);
   dim3 grid((unsigned)tiles, (unsigned)sp.splits);
+  const int avec = (R % 8) == 0;
+  const int bvec = b_is_kr ? (r % 8) == 0 : (R % 8) == 0;
   if (b_is_kr)
-    hipLaunchKernelGGL(k_lora_skinny<true>, grid, dim3(kThreads), 0, s, A, M, R, B, r, sp.chunk, ws);
+    hipLaunchKernelGGL(k_lora_skinny<true>, grid, dim3(kThreads), 0, s, A, M, R, B, r, sp.chunk, ws, avec, bvec);
   else
-    hipLaunchKernelGGL(k_lora_skinny<false>, grid, dim3(kThreads), 0, s, A, M, R, B, r, sp.chunk, ws);
+    hipLaunchKernelGGL(k_lora_skinny<false>, grid, dim3(kThreads), 0, s, A, M, R, B, r, sp.chunk, ws, avec, bvec);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_skinny_reduce, dim3(grid_for(M * r)), dim3(kThreads), 0, s, ws, sp.splits, M * (int64_t)r,
@@ -208,7 +277,8 @@ hipError_t launch_lora_tn(const uint16_t* A, const uint16_t* B, int64_t M, int64
   const int64_t tiles = (P + kTile - 1) / kTile;
   const SplitPlan sp = plan_rowsplit(tiles, M);
   dim3 grid((unsigned)tiles, (unsigned)sp.splits);
-  hipLaunchKernelGGL(k_lora_tn, grid, dim3(kThreads), 0, s, A, B, M, P, r, sp.chunk, ws);
+  hipLaunchKernelGGL(k_lora_tn, grid, dim3(kThreads), 0, s, A, B, M, P, r, sp.chunk, ws, (int)((P % 8) == 0),
+                     (int)((r % 8) == 0));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_tn_reduce, dim3(grid_for(P * r)), dim3(kThreads), 0, s, ws, sp.splits, P, r, scale,
