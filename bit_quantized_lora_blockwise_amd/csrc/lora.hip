@@ -230,12 +230,12 @@ int grid_for(int64_t items) {
 
 }  // namespace
 
-// Split of a reduction of length R over `tiles` output tiles: about 384 work
-// groups in all, but at most one slice per 1024 of reduction, so that the fp32
+// Split of a reduction of length R over `tiles` output tiles: about 768 work
+// groups in all, but at most one slice per 512 of reduction, so that the fp32
 // partials stay small next to the activation pass.
 SplitPlan plan_rowsplit(int64_t tiles, int64_t R) {
-  int64_t splits = (384 + tiles - 1) / tiles;
-  const int64_t max_splits = R / 1024;
+  int64_t splits = (768 + tiles - 1) / tiles;
+  const int64_t max_splits = R / 512;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int64_t chunk = (R + splits - 1) / splits;
