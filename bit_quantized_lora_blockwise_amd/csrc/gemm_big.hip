@@ -37,7 +37,10 @@ constexpr int kBR = 64;           // reduction per step
 constexpr int kPF = kBR + 8;      // pitch of the forward B tile [p][r] (elements)
 constexpr int kPD = kBP + 32;     // pitch of the dX B tile [r][p] (elements): 144 dwords, so the
                                   // 4 rows x 2 column halves of a 32-lane transposed read hit 64 banks
+constexpr int kPlane = kBP + 32;  // dX B tile: bytes per byte-plane row (72 dwords: the 8 rows x 32 columns
+                                  // of a 32-lane transposed byte read hit 64 banks)
 constexpr int kBufElems = (kBP * kPF > kBR * kPD) ? kBP * kPF : kBR * kPD;
+static_assert(2 * kBR * kPlane <= 2 * kBufElems, "dX byte-plane tile fits the B buffer");
 constexpr int kPL = 64 + 8;       // pitch of the LoRA operand tiles [row][c]
 
 constexpr uint32_t kOOB = 0x80000000u;
@@ -105,6 +108,40 @@ __device__ __forceinline__ u32x4 dequant8(const BlockLut& L, uint32_t c) {
   r[2] = __builtin_amdgcn_perm(o57, e46, 0x05040100u);   // e4, e5
   r[3] = __builtin_amdgcn_perm(o57, e46, 0x07060302u);   // e6, e7
   return r;
+}
+
+// Eight nibbles -> the low and high bytes of their bf16 values, each as eight
+// bytes in the element order (0, 2, 4, 6, 1, 3, 5, 7).
+__device__ __forceinline__ void dequant8_planes(const BlockLut& L, uint32_t c, u32x2& lo8, u32x2& hi8) {
+  const uint32_t xe = c & 0x0F0F0F0Fu;
+  const uint32_t xo = (c >> 4) & 0x0F0F0F0Fu;
+  const uint32_t se = ((xe >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t so = ((xo >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t xe7 = xe & 0x07070707u, xo7 = xo & 0x07070707u;
+  lo8 = u32x2{lut16(L.lo, xe, xe7, se), lut16(L.lo, xo, xo7, so)};
+  hi8 = u32x2{lut16(L.hi, xe, xe7, se), lut16(L.hi, xo, xo7, so)};
+}
+
+// Column held in slot `s` of a dX weight tile: within each group of eight the
+// slots hold columns (0, 2, 4, 6, 1, 3, 5, 7).
+__device__ __forceinline__ int dx_slot_col(int s) {
+  const int u = s & 7;
+  return (s & ~7) + (u < 4 ? 2 * u : 2 * u - 7);
+}
+
+// dX B fragment from the byte-plane tile (plane row 2 k + {0: low, 1: high}
+// bytes, kPlane bytes per row): two ds_read_b64_tr_b8, each returning for the
+// lane's column the low and high bytes of four consecutive k, i.e. four bf16.
+__device__ __forceinline__ bf16x8 frag_planes(const LDS_AS uint8_t* base, int k0, int col0) {
+  const int l = threadIdx.x & 63;
+  const int g = l >> 4, i = l & 15;
+  const int row = 2 * (k0 + 8 * (g >> 1)) + (i >> 1);
+  const LDS_AS uint8_t* p = base + row * kPlane + col0 + 16 * (g & 1) + 8 * (i & 1);
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)p);
+  const v2i b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 8 * kPlane));
+  const u32x4 v = {(uint32_t)a[0], (uint32_t)a[1], (uint32_t)b[0], (uint32_t)b[1]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // Half a block's packed codes (32 weights), its scale byte and group scale.
@@ -188,8 +225,11 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
         f32x16 z = {};
         for (int s = 0; s < ksteps; ++s) {
           const bf16x8 a = qk::frag_rowmajor(la, kPL, 64 * rg + 32 * i, 16 * s);
-          const bf16x8 b = kDx ? qk::frag_rowmajor(lb, kPL, 128 * ch + 32 * j, 16 * s)
-                               : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
+          // dX: the column of accumulator slot (l % 32) is dx_slot_col(l % 32)
+          const bf16x8 b =
+              kDx ? *(const LDS_AS bf16x8*)(lb + (128 * ch + 32 * j + dx_slot_col(l & 31)) * kPL + 16 * s +
+                                            8 * (l >> 5))
+                  : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
           z = qk::mfma32(a, b, z);
         }
         acc[i][j] = ls * z;
@@ -260,11 +300,24 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     hc.c1v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (4 * (b >> 8)) | oob, 0, 0));
     return hc;
   };
-  const int dq_off = kDx ? (t >> 3) * kPD + 64 * ((t >> 1) & 3) + 32 * half : (t >> 1) * kPF + 32 * half;
+  // fwd: element offset of the thread's 32 weights; dX: byte offset of their
+  // low-byte plane row (the high bytes follow one plane row later)
+  const int dq_off = kDx ? 2 * (t >> 3) * kPlane + 64 * ((t >> 1) & 3) + 32 * half : (t >> 1) * kPF + 32 * half;
+  auto store8 = [&](const BlockLut& L, uint32_t c, LDS_AS uint16_t* buf, int q) {
+    if (kDx) {
+      u32x2 lo8, hi8;
+      dequant8_planes(L, c, lo8, hi8);
+      LDS_AS uint8_t* d = (LDS_AS uint8_t*)buf + dq_off + 8 * q;
+      *(LDS_AS u32x2*)d = lo8;
+      *(LDS_AS u32x2*)(d + kPlane) = hi8;
+    } else {
+      *(LDS_AS u32x4*)(buf + dq_off + 8 * q) = dequant8(L, c);
+    }
+  };
   auto dequant_store = [&](const HalfCodes& hc, LDS_AS uint16_t* buf) {
     const BlockLut L = make_lut(qk::e4m3fn_to_f32(hc.c2b) * hc.c1v, p);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *(LDS_AS u32x4*)(buf + dq_off + 8 * q) = dequant8(L, hc.c[q]);
+    for (int q = 0; q < 4; ++q) store8(L, hc.c[q], buf, q);
   };
 
   // ---- main loop.  At the top of step st: LDS holds activation tile st and
@@ -284,10 +337,9 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     load_a(st + 2, av_later);
     __builtin_amdgcn_sched_barrier(0);
     const BlockLut L = make_lut(qk::e4m3fn_to_f32(hc_now.c2b) * hc_now.c1v, p);
-    LDS_AS uint16_t* dst = bnext + dq_off;
     // fragments of sub-step s + 1 are read from LDS while sub-step s runs
     auto bfrag = [&](int s, int j) {
-      return kDx ? qk::frag_kmajor(bcur, kPD, 16 * s, 128 * ch + 32 * j)
+      return kDx ? frag_planes((const LDS_AS uint8_t*)bcur, 16 * s, 128 * ch + 32 * j)
                  : qk::frag_rowmajor(bcur, kPF, 128 * ch + 32 * j, 16 * s);
     };
     bf16x8 bq[2][4], aq[2][2];
@@ -309,7 +361,7 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
         acc[1][j] = qk::mfma32(aq[s & 1][1], bq[s & 1][j], acc[1][j]);
       }
       // one 8-weight group of the next weight tile per sub-step
-      *(LDS_AS u32x4*)(dst + 8 * s) = dequant8(L, hc_now.c[s]);
+      store8(L, hc_now.c[s], bnext, s);
       // schedule: the next sub-step's fragment reads first, then one MFMA at a
       // time interleaved with the dequantisation VALU work, then the LDS store
       if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 10 : 6, 0);   // DS read
@@ -318,7 +370,7 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                         // VALU
       }
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                           // DS write
+      __builtin_amdgcn_sched_group_barrier(0x200, kDx ? 2 : 1, 0);                 // DS write
     }
     __builtin_amdgcn_sched_barrier(0);
     store_a(av_now, anext);
@@ -351,7 +403,7 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t pc = p0 + 128 * ch + 32 * j + qk::acc_col();
+      const int64_t pc = p0 + 128 * ch + 32 * j + (kDx ? dx_slot_col(qk::acc_col()) : qk::acc_col());
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + 64 * rg + 32 * i + qk::acc_row(e);
