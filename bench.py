@@ -169,6 +169,45 @@ def kernel_rooflines(lins, reps):
     return out
 
 
+def comparators(lins, reps):
+    """Same fwd + bwd of both linears by two other strategies, for context (the
+    headline is the fused 4-bit path).  The bf16 GEMMs are torch's (hipBLASLt).
+      lora_bf16_base: LoRA over a bf16 base (the dequantised weights kept in HBM):
+        torch GEMMs for the base, this library's kernels for the adapter products;
+      dequant_then_gemm: the 4-bit base dequantised to bf16 in HBM each step
+        (nf4_dequantize), then the same torch GEMMs."""
+    import torch
+    q = lins[0].q
+    prep = []
+    for L in lins:
+        Wd = q.nf4_dequantize(L.codes, L.c2, L.c1, L.N, L.K)           # [N, K] bf16
+        prep.append({"L": L, "W": Wd, "Wbuf": torch.empty_like(Wd)})
+
+    def lora_step(p, dequant):
+        L = p["L"]
+        W = p["Wbuf"] if dequant else p["W"]
+        if dequant:
+            q.nf4_dequantize(L.codes, L.c2, L.c1, L.N, L.K, out=W)
+        # two-dimensional products only (transposed operands are plain views)
+        T = q.qlora_lora_down(L.X, L.L1, T=L.T)
+        Y = torch.mm(L.X, W.t())
+        Y.add_(torch.mm(T, L.L2))
+        G = q.qlora_lora_grad_in(L.dY, L.L2, 1.0, G=L.G)
+        dX = torch.mm(L.dY, W)
+        dX.add_(torch.mm(G, L.L1.t()))
+        torch.mm(L.X.t(), G)                                             # dL1
+        torch.mm(T.t(), L.dY)                                            # dL2
+
+    out = {}
+    flops = sum(L.flops() for L in lins)
+    for name, dq in (("lora_bf16_base", False), ("dequant_then_gemm", True)):
+        ms = time_launches(lambda: [lora_step(p, dq) for p in prep], reps)
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+    del prep
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_bench(dev, reps=200):
     import torch
     import bit_quantized_lora_blockwise_amd as q
@@ -351,6 +390,7 @@ def main():
     fb_ms = phases["forward_ms"] + phases["backward_ms"]
 
     kern = kernel_rooflines(lins, args.kernel_reps)
+    comp = comparators(lins, max(3, args.kernel_reps // 4))
     dom = max(kern, key=lambda k: kern[k]["avg_ms"])
     roof = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": kern[dom]["tflops"] / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(dom),
@@ -374,6 +414,7 @@ def main():
                    "global_batch": 4096, "seq_len": 4096, "parallelism": "none (1 GPU)"},
         "fwd_bwd_only": {"ms": round(fb_ms, 4), "tflops": round(flops / (fb_ms * 1e-3) / 1e12, 3)},
         "phases_ms": {k: round(v, 4) for k, v in phases.items()},
+        "comparators": comp,
         "roofline": roof,
         "kernels": kern,
         "decode_m1_packed_gbps": round(m1["packed_gbps"], 1),
