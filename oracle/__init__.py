@@ -10,5 +10,5 @@ from .qlora_oracle import (  # noqa: F401
     e4m3fn_decode, e4m3fn_encode,
     nf4_quantize, unpack_codes, nf4_double_quant, block_scales, nf4_dequantize,
     dequantize_blocks, nf4_dequantize_rows, nf4_dequantize_colblock,
-    qlora_forward, qlora_backward, bits_per_weight,
+    qlora_forward, qlora_backward, qlora_merge, bits_per_weight,
 )

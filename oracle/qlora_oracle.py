@@ -326,6 +326,20 @@ def qlora_backward(X, dY, Wq, L1, L2, lora_scale: float = 1.0, T=None, rnd=bf16_
     return dX, dL1, dL2, G, T
 
 
+def qlora_merge(codes, c2, c1, rows: int, cols: int, L1, L2, lora_scale: float = 1.0) -> np.ndarray:
+    """Adapter merged into a bf16 copy of the base, for export after training:
+    W_m = bf16(W' + s (L1 L2)^T), [rows = N, cols = K] bf16 bits.
+
+    [examadda] "Practical Notes": merging an adapter into the 4-bit base is
+    lossy, so the base is dequantised first.  The layer's output with the
+    merged weight is X W_m^T = X W'^T + s X L1 L2 up to the one bf16 rounding of
+    W_m ([lineage] notation paragraph).  W' is exact (nf4_dequantize), the
+    low-rank term is float64, and the sum is rounded once."""
+    Wd = bf16_value(nf4_dequantize(codes, c2, c1, rows, cols)).astype(np.float64)
+    low = _f64(L1) @ _f64(L2)                       # [K, N]
+    return bf16_bits(Wd + lora_scale * low.T)
+
+
 def bits_per_weight(rows: int, cols: int) -> float:
     """Storage of the quantized base in bits per weight, from the buffer sizes
     that nf4_quantize / nf4_double_quant produce."""

@@ -433,6 +433,65 @@ def test_special_cases_reduce_to_library_gemm():
     assert not np.any(O.bf16_value(dX)) and not np.any(dL1) and not np.any(dL2) and not np.any(O.bf16_value(G))
 
 
+def _quantized(N, K, seed, wstd=0.02):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * wstd).astype(np.float32)
+    codes, absmax = O.nf4_quantize(W)
+    c2, c1 = O.nf4_double_quant(absmax)
+    return codes, c2, c1
+
+
+def test_merge_zero_adapter_is_the_dequantized_base():
+    """qlora_merge with L2 = 0 is exactly W' (the sum adds +0 before one
+    rounding of an already-bf16 value)."""
+    N, K, r = 48, 128, 4
+    codes, c2, c1 = _quantized(N, K, 31)
+    rng = np.random.default_rng(32)
+    L1 = O.bf16_bits(rng.standard_normal((K, r)))
+    Wm = O.qlora_merge(codes, c2, c1, N, K, L1, np.zeros((r, N), np.uint16), 0.75)
+    assert np.array_equal(Wm, O.nf4_dequantize(codes, c2, c1, N, K))
+
+
+def test_merge_zero_base_is_the_library_product():
+    """An all-zero weight quantizes to W' = 0, so the merge is bf16(s L2^T L1^T),
+    here from torch's float64 matmul."""
+    N, K, r, s = 40, 192, 8, 1.5
+    codes, absmax = O.nf4_quantize(np.zeros((N, K), np.float32))
+    c2, c1 = O.nf4_double_quant(absmax)
+    rng = np.random.default_rng(33)
+    L1 = O.bf16_bits(rng.standard_normal((K, r)))
+    L2 = O.bf16_bits(rng.standard_normal((r, N)))
+    Wm = O.qlora_merge(codes, c2, c1, N, K, L1, L2, s)
+    ref = s * (torch.tensor(O.bf16_value(L2)).T @ torch.tensor(O.bf16_value(L1)).T)
+    assert np.array_equal(Wm, ref.to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def _merge_identity_err(Wm_bits, codes, c2, c1, N, K, L1, L2, s, X):
+    Wq = O.nf4_dequantize(codes, c2, c1, N, K)
+    Xf = O.bf16_value(X)
+    exact = Xf @ O.bf16_value(Wq).T + s * (Xf @ O.bf16_value(L1)) @ O.bf16_value(L2)
+    merged = Xf @ O.bf16_value(Wm_bits).T
+    return np.linalg.norm(merged - exact) / np.linalg.norm(exact)
+
+
+def test_merge_layer_identity():
+    """The layer with the merged weight, X W_m^T, reproduces X W'^T + s X L1 L2
+    up to the one bf16 rounding of W_m (relative error about 2^-9); the adapter
+    applied untransposed (square case) is caught."""
+    N = K = 128
+    r, s = 8, 1.0
+    codes, c2, c1 = _quantized(N, K, 34)
+    rng = np.random.default_rng(35)
+    L1 = O.bf16_bits(rng.standard_normal((K, r)) * 0.05)
+    L2 = O.bf16_bits(rng.standard_normal((r, N)) * 0.05)
+    X = O.bf16_bits(rng.standard_normal((16, K)))
+    Wm = O.qlora_merge(codes, c2, c1, N, K, L1, L2, s)
+    assert _merge_identity_err(Wm, codes, c2, c1, N, K, L1, L2, s, X) < 2.0 ** -8
+    Wq = O.bf16_value(O.nf4_dequantize(codes, c2, c1, N, K))
+    wrong = O.bf16_bits(Wq + s * (O.bf16_value(L1) @ O.bf16_value(L2)))      # (L1 L2) not transposed
+    assert _merge_identity_err(wrong, codes, c2, c1, N, K, L1, L2, s, X) > 1e-2
+
+
 def test_rounding_points():
     """T, Y, G and dX are bf16-rounded once; dL1/dL2 are fp32."""
     X, Wq, L1, L2, dY = _layer(seed=7)
