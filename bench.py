@@ -284,6 +284,35 @@ def encode_bench(dev, reps=3):
     return res
 
 
+def merge_bench(dev, reps=20):
+    """Adapter merge (W' + s (L1 L2)^T to bf16) of the LLaMA-7B up and down
+    projections at r = 64: one launch per matrix, HBM-bound."""
+    import torch
+    import bit_quantized_lora_blockwise_amd as q
+    import workloads as WL
+    mats = []
+    for i, (N, K) in enumerate((WL.LLAMA7B_UP, WL.LLAMA7B_DOWN)):
+        codes, absmax = q.nf4_quantize(WL.weight_gaussian(N, K, 0.02, 90 + 10 * i, device=dev))
+        c2, c1 = q.nf4_double_quant(absmax)
+        L1, L2 = (t.to(dev) for t in WL.lora_pair(K, N, 64, 91 + 10 * i, 92 + 10 * i, 0.01))
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        mats.append((codes, c2, c1, N, K, L1, L2, out))
+
+    def run():
+        for codes, c2, c1, N, K, L1, L2, out in mats:
+            q.qlora_merge(codes, c2, c1, N, K, L1, L2, 2.0, out=out)
+
+    ms = time_launches(run, reps)
+    elems = sum(m[3] * m[4] for m in mats)
+    alg_bytes = sum(N * K * (0.5 + 2 + 1 / 64) + 4 * (N * K // 16384) + 2 * 64 * (N + K)
+                    for _, _, _, N, K, _, _, _ in mats)
+    gbps = alg_bytes / (ms * 1e-3) / 1e9
+    del mats
+    torch.cuda.empty_cache()
+    return {"kernel": "k_merge", "weights": elems, "ms_two_launches": ms, "alg_bytes": alg_bytes,
+            "alg_gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS}
+
+
 def cpu_baseline():
     """The CPU oracle on a bounded sample of the headline step: the whole
     up-projection half of it (4096 -> 11008, r = 64, M = 4096 tokens) -- encode,
@@ -404,6 +433,7 @@ def main():
                 "unit": "GB/s", "frac": m1["alg_gbps"] / PEAK_HBM_GBPS, "traffic": None,
                 "avg_launch_us": m1["kernel_us"]}
     enc = encode_bench(dev)
+    mrg = merge_bench(dev)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -421,6 +451,7 @@ def main():
         "decode": dec,
         "roofline_decode": dec_roof,
         "encode": enc,
+        "merge": mrg,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

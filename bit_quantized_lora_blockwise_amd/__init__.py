@@ -9,4 +9,5 @@ from ._lib import (  # noqa: F401
     qlora_linear_bwd_workspace, qlora_linear_bwd,
     qlora_nf4_levels, ql_status_string,
     qlora_lora_down, qlora_linear_fwd_t, qlora_lora_grad_in, qlora_linear_dx,
+    qlora_merge,
 )

@@ -22,7 +22,7 @@ STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_DTYPE",
 EXPORTS = ("nf4_quantize", "nf4_double_quant", "nf4_dequantize", "qlora_linear_fwd_workspace",
            "qlora_linear_fwd", "qlora_linear_bwd_workspace", "qlora_linear_bwd", "qlora_nf4_levels",
            "ql_status_string", "qlora_lora_down_workspace", "qlora_lora_down", "qlora_linear_fwd_t",
-           "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx")
+           "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx", "qlora_merge")
 
 
 class QloraError(RuntimeError):
@@ -56,6 +56,7 @@ def lib():
             "qlora_lora_grad_in_workspace": ([I64, I64, I32], SZ),
             "qlora_lora_grad_in": ([P, I64, I64, P, I32, F32, P, P, SZ, P], I32),
             "qlora_linear_dx": ([P, I64, I64, I64, P, P, P, P, P, I32, P, P], I32),
+            "qlora_merge": ([P, P, P, I64, I64, P, P, I32, F32, P, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -126,6 +127,19 @@ def nf4_dequantize(codes, c2, c1, rows, cols, out=None, stream=None):
     out = _empty((rows, cols), torch.bfloat16, codes) if out is None else _need(out, "out", torch.bfloat16)
     _check("nf4_dequantize", lib().nf4_dequantize(_ptr(codes), _ptr(c2), _ptr(c1), rows, cols, _ptr(out),
                                                   _stream(stream)))
+    return out
+
+
+def qlora_merge(codes, c2, c1, N, K, L1, L2, lora_scale=1.0, out=None, stream=None):
+    """Merged bf16 weight W' + lora_scale (L1 L2)^T [N, K], rounded once."""
+    _need(codes, "codes", torch.uint8); _need(c2, "c2", torch.uint8); _need(c1, "c1", torch.float32)
+    _need(L1, "L1", torch.bfloat16); _need(L2, "L2", torch.bfloat16)
+    r = L1.shape[1]
+    if tuple(L1.shape) != (K, r) or tuple(L2.shape) != (r, N):
+        raise ValueError(f"qlora_merge: L1 {tuple(L1.shape)} / L2 {tuple(L2.shape)} do not match N={N}, K={K}")
+    out = _empty((N, K), torch.bfloat16, codes) if out is None else _need(out, "out", torch.bfloat16)
+    _check("qlora_merge", lib().qlora_merge(_ptr(codes), _ptr(c2), _ptr(c1), N, K, _ptr(L1), _ptr(L2), r,
+                                            float(lora_scale), _ptr(out), _stream(stream)))
     return out
 
 

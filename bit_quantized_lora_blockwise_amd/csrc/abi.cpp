@@ -112,6 +112,19 @@ int nf4_dequantize(const uint8_t* codes, const uint8_t* c2, const float* c1, int
   return QL_OK;
 }
 
+int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t N, int64_t K, const uint16_t* L1,
+                const uint16_t* L2, int r, float lora_scale, uint16_t* W_out, void* stream) {
+  if (!codes || !c2 || !c1 || !L1 || !L2 || !W_out) return QL_ERR_NULL;
+  if (N <= 0 || K <= 0 || K % 64 != 0 || r < 1 || r > 64 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31) ||
+      N > (int64_t(1) << 36) / K)
+    return QL_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(c2) || !aligned16(c1) || !aligned16(L1) || !aligned16(L2) ||
+      !aligned16(W_out))
+    return QL_ERR_ALIGN;
+  QL_TRY(launch_merge(codes, c2, c1, N, K, L1, L2, r, lora_scale, W_out, (hipStream_t)stream));
+  return QL_OK;
+}
+
 size_t qlora_linear_fwd_workspace(int64_t M, int64_t K, int64_t N, int r) {
   if (!shapes_ok(M, K, N, r)) return 0;
   return fwd_ws(M, K, N, r).total;

@@ -39,6 +39,12 @@ size_t lora_tn_ws(int64_t M, int64_t P, int r);
 hipError_t launch_lora_tn(const uint16_t* A, const uint16_t* B, int64_t M, int64_t P, int r, float scale,
                           bool transpose_out, float* out, float* ws, hipStream_t s);
 
+// --- adapter merge (merge.hip) ---------------------------------------------
+// W[n][k] = bf16(W'[n][k] + scale * sum_c L1[k][c] L2[c][n]), W' the bf16
+// dequantised base; W [N, K], K a multiple of 64.
+hipError_t launch_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t N, int64_t K,
+                        const uint16_t* L1, const uint16_t* L2, int r, float scale, uint16_t* W, hipStream_t s);
+
 // --- quantised GEMMs (gemm.hip, decode.hip) ----------------------------------
 // Y[M, N] = bf16(X W'^T + scale * T L2)
 hipError_t launch_qgemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,

@@ -160,6 +160,21 @@ int qlora_linear_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N,
                     const uint8_t* codes, const uint8_t* c2, const float* c1,
                     const uint16_t* G, const uint16_t* L1, int r, uint16_t* dX, void* stream);
 
+/* Adapter merge for export (examadda page, "Practical Notes": to merge, the
+ * base is dequantised first and the adapter product is added to it):
+ *   W_m = bf16(W' + lora_scale * (L1 L2)^T)                [N, K]
+ * W' as in nf4_dequantize; (L1 L2)^T in fp32 accumulation, added to W' in fp32
+ * and rounded once to bf16 (nearest-even). codes/c2/c1 describe W [N, K];
+ * L1 [K, r] bf16; L2 [r, N] bf16; 1 <= r <= 64; K % 64 == 0; N * K <= 2^36.
+ * Output W_out [N, K] bf16, owned by the caller, must not overlap the inputs.
+ * With L1 or L2 all zero the result equals nf4_dequantize's in value (a zero
+ * may change sign). The merged weight is bf16: re-quantising it to NF4 is
+ * lossy and is left to the caller (nf4_quantize). Errors: QL_ERR_NULL,
+ * QL_ERR_SHAPE, QL_ERR_ALIGN before anything is enqueued; QL_ERR_HIP.          */
+int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t N, int64_t K,
+                const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
+                uint16_t* W_out, void* stream);
+
 /* Host-only helpers (no GPU needed). */
 /* The 16 NF4 levels (fp32, ascending) that the kernels use, copied to out[16].  */
 int qlora_nf4_levels(float* out16);

@@ -121,3 +121,18 @@ def test_stage_entry_validation():
     assert L.qlora_lora_grad_in(A, 64, 33, A, 8, 1.0, A, None, wg, None) == -5
     assert L.qlora_linear_dx(A, 64, 96, 32, A, A, A, A, A, 8, A, None) == -2
     assert L.qlora_linear_dx(A, 64, 128, 32, A, A, A, A, None, 8, A, None) == -1
+
+
+def test_merge_validation():
+    _, L = _lib()
+    mrg = lambda codes=A, N=48, K=128, L1=A, r=8, out=A: L.qlora_merge(codes, A, A, N, K, L1, A, r, 1.0, out, None)
+    assert mrg(codes=None) == -1
+    assert mrg(out=None) == -1
+    assert mrg(K=96) == -2
+    assert mrg(N=0) == -2
+    assert mrg(r=0) == -2
+    assert mrg(r=65) == -2
+    assert mrg(N=1 << 32) == -2
+    assert mrg(N=1 << 26, K=1 << 11) == -2   # N K above 2^36
+    assert mrg(L1=MIS) == -4
+    assert mrg(out=MIS) == -4

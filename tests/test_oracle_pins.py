@@ -546,3 +546,18 @@ def test_mutation_wrong_delta_is_caught():
     ref = np.array(sorted([-inv_norm_bisect(d - j * (d - 0.5) / 7) / t2 for j in range(7)] + [0.0] +
                           [inv_norm_bisect(d - j * (d - 0.5) / 8) / t2 for j in range(8)])).astype(np.float32)
     assert not np.array_equal(wrong, ref)
+
+
+def test_requantizing_the_dequantized_base_keeps_its_codes():
+    """Re-quantizing W' (a merge with a zero adapter) reproduces the NF4 codes:
+    W'/absmax(W') lands within bf16 rounding of the original level, far from
+    any midpoint; a lossy re-quantization therefore loses only what the adapter
+    added.  A wrong level order, nibble order or scale in the chain fails it."""
+    N, K = 64, 256
+    codes, c2, c1 = _quantized(N, K, 41)
+    Wd = O.bf16_value(O.nf4_dequantize(codes, c2, c1, N, K)).astype(np.float32)
+    codes2, absmax2 = O.nf4_quantize(Wd)
+    assert np.array_equal(codes2, codes)
+    # and the block scales come back to within the bf16 rounding of s'
+    sprime = O.e4m3fn_decode(c2).astype(np.float64) * np.repeat(np.asarray(c1, np.float64), 256)[: c2.size]
+    assert np.allclose(absmax2, sprime, rtol=2.0 ** -8, atol=0)
