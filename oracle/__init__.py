@@ -12,3 +12,4 @@ from .qlora_oracle import (  # noqa: F401
     dequantize_blocks, nf4_dequantize_rows, nf4_dequantize_colblock,
     qlora_forward, qlora_backward, qlora_merge, bits_per_weight,
 )
+from . import variants  # noqa: F401,E402  (code-book and second-level-scale variants)
