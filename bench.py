@@ -313,6 +313,56 @@ def merge_bench(dev, reps=20):
             "alg_gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS}
 
 
+def quant_study(dev, n=4096, reps=10):
+    """Quantization error of the 4-bit formats the pages rank (NF4 with double
+    quantization against a 4-bit float and 4-bit integers) under the four ways
+    of coding the block scales, on n x n N(0, 1) and Student-t (5 d.o.f.)
+    weights: normalised MSE sum (W' - W)^2 / sum W^2 and the entropy of the code
+    histogram, plus the time of the table encoder and dequantizer."""
+    import torch
+    import bit_quantized_lora_blockwise_amd as q
+    g = torch.Generator(device=dev).manual_seed(1234)
+    mats = {"normal": torch.randn((n, n), generator=g, device=dev)}
+    z = torch.randn((n, n), generator=g, device=dev)
+    chi = sum(torch.randn((n, n), generator=g, device=dev) ** 2 for _ in range(5))
+    mats["t5"] = z / torch.sqrt(chi / 5)
+    del z, chi
+    out = {"weights": n * n, "nmse": {}, "code_entropy_bits": {}}
+    for dist, W in mats.items():
+        Wb = W.to(torch.bfloat16)
+        Wf = Wb.float()
+        den = (Wf.double() ** 2).sum()
+        for book in ("nf4", "fp4", "int4"):
+            codes, absmax = q.q4_quantize(Wb, book)
+            h = torch.bincount(torch.cat([(codes & 15).flatten(), (codes >> 4).flatten()]).long(), minlength=16)
+            p = h.double() / h.sum()
+            p = p[p > 0]
+            out["code_entropy_bits"][f"{dist}/{book}"] = round(float(-(p * torch.log2(p)).sum()), 4)
+            for sc in ("absmax", "groupmax", "fullrange", "mean"):
+                if sc == "absmax":
+                    Wd = q.q4_dequantize(codes, n, n, book, sc, absmax=absmax)
+                else:
+                    c2, c1, mu = q.q4_double_quant(absmax, sc)
+                    Wd = q.q4_dequantize(codes, n, n, book, sc, c2=c2, c1=c1, mu=mu)
+                out["nmse"][f"{dist}/{book}/{sc}"] = round(float(((Wd.float() - Wf).double() ** 2).sum() / den), 6)
+    Wb = mats["normal"].to(torch.bfloat16)
+    codes, absmax = q.q4_quantize(Wb, "fp4")
+    c2, c1, mu = q.q4_double_quant(absmax, "mean")
+    Wd = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    t_enc = time_launches(lambda: q.q4_quantize(Wb, "fp4", codes=codes, absmax=absmax), reps)
+    t_nf4 = time_launches(lambda: q.nf4_quantize(Wb, codes=codes, absmax=absmax), reps)
+    t_deq = time_launches(lambda: q.q4_dequantize(codes, n, n, "fp4", "mean", c2=c2, c1=c1, mu=mu, out=Wd), reps)
+    e = n * n
+    out["encode_table_us"] = round(t_enc * 1e3, 2)
+    out["encode_table_gbps"] = round(e * (2 + 0.5 + 4 / 64) / (t_enc * 1e-3) / 1e9, 1)
+    out["encode_nf4_bucketed_us"] = round(t_nf4 * 1e3, 2)
+    out["dequant_mean_us"] = round(t_deq * 1e3, 2)
+    out["dequant_mean_gbps"] = round(e * (0.5 + 1 / 64 + 2) / (t_deq * 1e-3) / 1e9, 1)
+    del mats
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline():
     """The CPU oracle on a bounded sample of the headline step: the whole
     up-projection half of it (4096 -> 11008, r = 64, M = 4096 tokens) -- encode,
@@ -434,6 +484,7 @@ def main():
                 "avg_launch_us": m1["kernel_us"]}
     enc = encode_bench(dev)
     mrg = merge_bench(dev)
+    study = quant_study(dev)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -452,6 +503,7 @@ def main():
         "roofline_decode": dec_roof,
         "encode": enc,
         "merge": mrg,
+        "quant_study": study,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

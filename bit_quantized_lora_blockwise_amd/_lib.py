@@ -17,12 +17,15 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora.s
 _lib = None
 
 QL_F32, QL_BF16 = 0, 1
+CODEBOOKS = {"nf4": 0, "fp4": 1, "int4": 2}
+SCALE_CODES = {"groupmax": 0, "fullrange": 1, "mean": 2, "absmax": 3}
 STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_DTYPE", -4: "QL_ERR_ALIGN",
           -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_HIP"}
 EXPORTS = ("nf4_quantize", "nf4_double_quant", "nf4_dequantize", "qlora_linear_fwd_workspace",
            "qlora_linear_fwd", "qlora_linear_bwd_workspace", "qlora_linear_bwd", "qlora_nf4_levels",
            "ql_status_string", "qlora_lora_down_workspace", "qlora_lora_down", "qlora_linear_fwd_t",
-           "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx", "qlora_merge")
+           "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx", "qlora_merge",
+           "q4_quantize", "q4_double_quant", "q4_dequantize", "q4_levels")
 
 
 class QloraError(RuntimeError):
@@ -57,6 +60,10 @@ def lib():
             "qlora_lora_grad_in": ([P, I64, I64, P, I32, F32, P, P, SZ, P], I32),
             "qlora_linear_dx": ([P, I64, I64, I64, P, P, P, P, P, I32, P, P], I32),
             "qlora_merge": ([P, P, P, I64, I64, P, P, I32, F32, P, P], I32),
+            "q4_quantize": ([P, I32, I64, I64, I32, P, P, P], I32),
+            "q4_double_quant": ([P, I64, I32, P, P, P, P], I32),
+            "q4_dequantize": ([P, I64, I64, I32, I32, P, P, P, P, P, P], I32),
+            "q4_levels": ([I32, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -128,6 +135,70 @@ def nf4_dequantize(codes, c2, c1, rows, cols, out=None, stream=None):
     _check("nf4_dequantize", lib().nf4_dequantize(_ptr(codes), _ptr(c2), _ptr(c1), rows, cols, _ptr(out),
                                                   _stream(stream)))
     return out
+
+
+def _codebook(name):
+    if name not in CODEBOOKS:
+        raise ValueError(f"unknown code book {name!r} (one of {sorted(CODEBOOKS)})")
+    return CODEBOOKS[name]
+
+
+def _scale_code(name):
+    if name not in SCALE_CODES:
+        raise ValueError(f"unknown scale code {name!r} (one of {sorted(SCALE_CODES)})")
+    return SCALE_CODES[name]
+
+
+def q4_quantize(W, codebook="nf4", codes=None, absmax=None, stream=None):
+    """Packed 4-bit codes [rows, cols/2] and fp32 absmax [rows*cols/64] with the given code book."""
+    if W.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("W must be float32 or bfloat16")
+    _need(W, "W", W.dtype, 2)
+    rows, cols = W.shape
+    codes = _empty((rows, cols // 2), torch.uint8, W) if codes is None else _need(codes, "codes", torch.uint8)
+    absmax = _empty((rows * cols // 64,), torch.float32, W) if absmax is None else _need(absmax, "absmax",
+                                                                                        torch.float32)
+    _check("q4_quantize", lib().q4_quantize(_ptr(W), QL_BF16 if W.dtype == torch.bfloat16 else QL_F32, rows, cols,
+                                            _codebook(codebook), _ptr(codes), _ptr(absmax), _stream(stream)))
+    return codes, absmax
+
+
+def q4_double_quant(absmax, scale_code="groupmax", stream=None):
+    """(c2 [n_blocks] uint8, c1 [groups] fp32, mu [groups] fp32 or None) for a scale code."""
+    _need(absmax, "absmax", torch.float32)
+    sc = _scale_code(scale_code)
+    if sc == SCALE_CODES["absmax"]:
+        raise ValueError("absmax scales need no second level")
+    nb = absmax.numel()
+    ng = (nb + 255) // 256
+    c2 = _empty((nb,), torch.uint8, absmax)
+    c1 = _empty((ng,), torch.float32, absmax)
+    mu = _empty((ng,), torch.float32, absmax) if scale_code == "mean" else None
+    _check("q4_double_quant", lib().q4_double_quant(_ptr(absmax), nb, sc, _ptr(c2), _ptr(c1),
+                                                    _ptr(mu) if mu is not None else None, _stream(stream)))
+    return c2, c1, mu
+
+
+def q4_dequantize(codes, rows, cols, codebook="nf4", scale_code="groupmax", absmax=None, c2=None, c1=None, mu=None,
+                  out=None, stream=None):
+    """bf16 W' [rows, cols] from codes and the block scales of `scale_code`."""
+    _need(codes, "codes", torch.uint8)
+    for t, n, d in ((absmax, "absmax", torch.float32), (c2, "c2", torch.uint8), (c1, "c1", torch.float32),
+                    (mu, "mu", torch.float32)):
+        if t is not None:
+            _need(t, n, d)
+    out = _empty((rows, cols), torch.bfloat16, codes) if out is None else _need(out, "out", torch.bfloat16)
+    p = lambda t: _ptr(t) if t is not None else None
+    _check("q4_dequantize", lib().q4_dequantize(_ptr(codes), rows, cols, _codebook(codebook), _scale_code(scale_code),
+                                                p(absmax), p(c2), p(c1), p(mu), _ptr(out), _stream(stream)))
+    return out
+
+
+def q4_levels(codebook="nf4"):
+    """The 16 fp32 levels of a code book compiled into the library (host call)."""
+    buf = (ctypes.c_float * 16)()
+    _check("q4_levels", lib().q4_levels(_codebook(codebook), ctypes.cast(buf, ctypes.c_void_p)))
+    return list(buf)
 
 
 def qlora_merge(codes, c2, c1, N, K, L1, L2, lora_scale=1.0, out=None, stream=None):

@@ -125,6 +125,57 @@ int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_
   return QL_OK;
 }
 
+int q4_quantize(const void* W, int w_dtype, int64_t rows, int64_t cols, int codebook, uint8_t* codes,
+                float* absmax, void* stream) {
+  if (!W || !codes || !absmax) return QL_ERR_NULL;
+  const Nf4Params* p = codebook_params(codebook);
+  if ((w_dtype != QL_F32 && w_dtype != QL_BF16) || !p) return QL_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || cols % 64 != 0 || rows > (int64_t(1) << 40) / cols) return QL_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax)) return QL_ERR_ALIGN;
+  QL_TRY(launch_q4_encode(W, w_dtype == QL_BF16, rows * cols, *p, codes, absmax, (hipStream_t)stream));
+  return QL_OK;
+}
+
+int q4_double_quant(const float* absmax, int64_t n_blocks, int scale_code, uint8_t* c2, float* c1, float* mu,
+                    void* stream) {
+  if (scale_code != QL_SC_GROUPMAX && scale_code != QL_SC_FULLRANGE && scale_code != QL_SC_MEAN)
+    return QL_ERR_DTYPE;
+  if (!absmax || !c2 || !c1 || (scale_code == QL_SC_MEAN && !mu)) return QL_ERR_NULL;
+  if (n_blocks <= 0 || n_blocks > (int64_t(1) << 36)) return QL_ERR_SHAPE;
+  if (!aligned16(absmax) || !aligned16(c2) || !aligned16(c1) || (scale_code == QL_SC_MEAN && !aligned16(mu)))
+    return QL_ERR_ALIGN;
+  if (scale_code == QL_SC_GROUPMAX) {
+    QL_TRY(launch_double_quant(absmax, n_blocks, c2, c1, (hipStream_t)stream));
+  } else {
+    QL_TRY(launch_double_quant_full(absmax, n_blocks, scale_code == QL_SC_MEAN, c2, c1, mu, (hipStream_t)stream));
+  }
+  return QL_OK;
+}
+
+int q4_dequantize(const uint8_t* codes, int64_t rows, int64_t cols, int codebook, int scale_code,
+                  const float* absmax, const uint8_t* c2, const float* c1, const float* mu, uint16_t* W_bf16,
+                  void* stream) {
+  const Nf4Params* p = codebook_params(codebook);
+  if (!p || scale_code < QL_SC_GROUPMAX || scale_code > QL_SC_ABSMAX) return QL_ERR_DTYPE;
+  const bool single = scale_code == QL_SC_ABSMAX, mean = scale_code == QL_SC_MEAN;
+  if (!codes || !W_bf16 || (single && !absmax) || (!single && (!c2 || !c1)) || (mean && !mu)) return QL_ERR_NULL;
+  if (rows <= 0 || cols <= 0 || cols % 64 != 0 || rows > (int64_t(1) << 40) / cols) return QL_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(W_bf16) || (single && !aligned16(absmax)) ||
+      (!single && (!aligned16(c2) || !aligned16(c1))) || (mean && !aligned16(mu)))
+    return QL_ERR_ALIGN;
+  const int mode = single ? 1 : (mean ? 2 : 0);
+  QL_TRY(launch_q4_dequant(codes, mode, absmax, c2, c1, mu, rows * cols, *p, W_bf16, (hipStream_t)stream));
+  return QL_OK;
+}
+
+int q4_levels(int codebook, float* out16) {
+  const Nf4Params* p = codebook_params(codebook);
+  if (!p) return QL_ERR_DTYPE;
+  if (!out16) return QL_ERR_NULL;
+  std::memcpy(out16, p->q, 16 * sizeof(float));
+  return QL_OK;
+}
+
 size_t qlora_linear_fwd_workspace(int64_t M, int64_t K, int64_t N, int r) {
   if (!shapes_ok(M, K, N, r)) return 0;
   return fwd_ws(M, K, N, r).total;
@@ -258,7 +309,7 @@ const char* ql_status_string(int status) {
     case QL_OK: return "ok";
     case QL_ERR_NULL: return "a required pointer is NULL";
     case QL_ERR_SHAPE: return "invalid shape (sizes must be > 0, K and cols multiples of 64, 1 <= r <= 64)";
-    case QL_ERR_DTYPE: return "unsupported dtype code";
+    case QL_ERR_DTYPE: return "unsupported dtype, code book or scale code";
     case QL_ERR_ALIGN: return "device pointers must be 16-byte aligned";
     case QL_ERR_WORKSPACE: return "workspace missing or smaller than the size query returns";
     case QL_ERR_HIP:

@@ -101,6 +101,25 @@ __device__ __forceinline__ int acc_row(int j) {
 }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 31; }
 
+// max over aligned groups of 8 lanes: swap neighbours, swap pairs, mirror halves of 8
+__device__ __forceinline__ uint32_t dpp_max8(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return v;
+}
+
+// Nearest OCP E4M3FN magnitude code of t in [0, 464) (past 448 the nearest
+// finite value is 448), ties to even.  Below 2^-6 the format is fixed-point
+// with step 2^-9, so the code is rint(t * 512); above, the fp32 mantissa is
+// rounded to 3 bits and the exponent rebased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3fn_encode(float t) {
+  if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  return (r >> 20) - (120u << 3);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
   return v;

@@ -10,14 +10,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ uint32_t dpp_max8(uint32_t v) {
-  // max over aligned groups of 8 lanes: swap neighbours, swap pairs, mirror halves of 8
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
-  return v;
-}
-
 // One thread encodes 8 consecutive weights; the 8 lanes of an aligned group
 // cover one block of 64 and share its absmax through DPP.  Codes of the 8
 // weights form one 32-bit word (element j in bits 4j..4j+3).
@@ -64,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict_
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(w[j]) & 0x7FFFFFFFu);
-    m = dpp_max8(m);
+    m = qk::dpp_max8(m);
     const float a = __uint_as_float(m);
     // 16 / a for a normal absmax; an all-zero block gives n' = 0 (codes 7)
     const bool a_normal = m >= 0x00800000u;
@@ -100,16 +92,6 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict_
   }
 }
 
-// Nearest OCP E4M3FN code of t in [0, 448], ties to even.  Below 2^-6 the
-// format is fixed-point with step 2^-9, so the code is rint(t * 512); above,
-// the fp32 mantissa is rounded to 3 bits and the exponent rebased from 127 to 7.
-__device__ __forceinline__ uint32_t e4m3fn_encode(float t) {
-  if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);
-  const uint32_t u = __float_as_uint(t);
-  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
-  return (r >> 20) - (120u << 3);
-}
-
 // One wavefront per group of 256 scales; lane l owns scales 4l..4l+3.
 __global__ __launch_bounds__(kThreads) void k_double_quant(const float* __restrict__ absmax, int64_t nb,
                                                            uint8_t* __restrict__ c2, float* __restrict__ c1,
@@ -132,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void k_double_quant(const float* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float t = (m == 0) ? 0.0f : v[j] / cmax;
-      packed |= e4m3fn_encode(t) << (8 * j);
+      packed |= qk::e4m3fn_encode(t) << (8 * j);
     }
     if (base + 4 <= nb) {
       *(uint32_t*)(c2 + base) = packed;

@@ -10,6 +10,9 @@
 
 const Nf4Params& nf4_params();
 const Nf4Buckets& nf4_buckets();
+// Level table of a 4-bit code book: 0 NF4, 1 4-bit float (E2M1 / 6), 2 4-bit
+// integer (k / 7); nullptr for any other id.
+const Nf4Params* codebook_params(int codebook);
 
 // --- encoder (encode.hip) ---------------------------------------------------
 hipError_t launch_nf4_encode(const void* W, bool bf16, int64_t elems, uint8_t* codes, float* absmax,
@@ -17,6 +20,19 @@ hipError_t launch_nf4_encode(const void* W, bool bf16, int64_t elems, uint8_t* c
 hipError_t launch_double_quant(const float* absmax, int64_t n_blocks, uint8_t* c2, float* c1, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t elems,
                           uint16_t* out, hipStream_t s);
+
+// --- code-book and scale-code variants (variants.hip) ------------------------
+// Blockwise absmax encoder with level table p (exact division, threshold count).
+hipError_t launch_q4_encode(const void* W, bool bf16, int64_t elems, const Nf4Params& p, uint8_t* codes,
+                            float* absmax, hipStream_t s);
+// Second-level codes over the full E4M3FN range; mean = true codes the signed
+// differences from the group mean (mu[g] written), else the scales themselves.
+hipError_t launch_double_quant_full(const float* absmax, int64_t n_blocks, bool mean, uint8_t* c2, float* c1,
+                                    float* mu, hipStream_t s);
+// Table dequantizer; mode 0: s = dec(c2) c1, 1: s = absmax, 2: s = mu + dec(c2) c1.
+hipError_t launch_q4_dequant(const uint8_t* codes, int mode, const float* absmax, const uint8_t* c2,
+                             const float* c1, const float* mu, int64_t elems, const Nf4Params& p, uint16_t* out,
+                             hipStream_t s);
 
 // --- skinny LoRA products (lora.hip) -----------------------------------------
 // Split plan of a reduction of length R over tiles of `tiles` outputs.

@@ -29,8 +29,21 @@ long double phi_inv(long double p) {
   return 0.5L * (lo + hi);
 }
 
-Nf4Params build() {
+// Levels and the encoder thresholds: thr[k] is the smallest fp32 strictly
+// above the midpoint of q[k] and q[k + 1] (exact in double).
+Nf4Params from_levels(const float* q) {
   Nf4Params p;
+  for (int k = 0; k < 16; ++k) p.q[k] = q[k];
+  for (int k = 0; k < 15; ++k) {
+    const double m = ((double)p.q[k] + (double)p.q[k + 1]) * 0.5;
+    float f = (float)m;
+    if ((double)f <= m) f = std::nextafter(f, 2.0f);
+    p.thr[k] = f;
+  }
+  return p;
+}
+
+Nf4Params build() {
   const long double delta = 1.0L - 0.5L * (1.0L / 32.0L + 1.0L / 30.0L);
   const long double top = phi_inv(delta);
   long double v[16];
@@ -39,15 +52,36 @@ Nf4Params build() {
   for (int j = 0; j < 7; ++j) v[n++] = -phi_inv(delta - j * (delta - 0.5L) / 7.0L) / top;
   v[n++] = 0.0L;
   std::sort(v, v + 16);
-  for (int k = 0; k < 16; ++k) p.q[k] = (float)v[k];
-  for (int k = 0; k < 15; ++k) {
-    // midpoint of two fp32 levels: exact in double
-    double m = ((double)p.q[k] + (double)p.q[k + 1]) * 0.5;
-    float f = (float)m;
-    if ((double)f <= m) f = std::nextafter(f, 2.0f);
-    p.thr[k] = f;
+  float q[16];
+  for (int k = 0; k < 16; ++k) q[k] = (float)v[k];
+  return from_levels(q);
+}
+
+// 4-bit float: OCP E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit,
+// exponent 0 subnormal) divided by its largest value 6.  4-bit integer: k / 7
+// for k = -7..7.  Both have 15 distinct values; code 15 repeats +1 and is
+// never the nearest (ties go to the smaller code).
+Nf4Params build_fp4() {
+  double v[16];
+  int n = 0;
+  for (int c = 0; c < 8; ++c) {               // non-negative patterns; the sign bit mirrors them
+    const int e = (c >> 1) & 3, m = c & 1;
+    const double mag = e == 0 ? 0.5 * m : (1.0 + 0.5 * m) * std::ldexp(1.0, e - 1);
+    v[n++] = mag / 6.0;
+    if (c) v[n++] = -mag / 6.0;
   }
-  return p;
+  std::sort(v, v + 15);
+  float q[16];
+  for (int k = 0; k < 15; ++k) q[k] = (float)v[k];
+  q[15] = 1.0f;
+  return from_levels(q);
+}
+
+Nf4Params build_int4() {
+  float q[16];
+  for (int k = 0; k < 15; ++k) q[k] = (float)((k - 7) / 7.0);
+  q[15] = 1.0f;
+  return from_levels(q);
 }
 
 // Bucket table of the encoder.  The approximate quotient n' it is used with
@@ -94,4 +128,14 @@ const Nf4Params& nf4_params() {
 const Nf4Buckets& nf4_buckets() {
   static const Nf4Buckets b = build_buckets(nf4_params());
   return b;
+}
+
+const Nf4Params* codebook_params(int codebook) {
+  static const Nf4Params fp4 = build_fp4(), int4 = build_int4();
+  switch (codebook) {
+    case 0: return &nf4_params();
+    case 1: return &fp4;
+    case 2: return &int4;
+    default: return nullptr;
+  }
 }

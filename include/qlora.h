@@ -56,13 +56,18 @@ typedef enum {
   QL_OK = 0,
   QL_ERR_NULL = -1,      /* a required pointer is NULL                            */
   QL_ERR_SHAPE = -2,     /* a size is <= 0, K % 64 != 0, r outside [1, 64], ...   */
-  QL_ERR_DTYPE = -3,     /* unsupported dtype code                                */
+  QL_ERR_DTYPE = -3,     /* unsupported dtype, code book or scale code            */
   QL_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned               */
   QL_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the query returns      */
   QL_ERR_HIP = -6        /* a HIP launch failed (see ql_status_string)            */
 } ql_status;
 
 enum { QL_F32 = 0, QL_BF16 = 1 };
+
+/* 4-bit code books of the q4_* calls (QL_CB_NF4 is the layer's format). */
+enum { QL_CB_NF4 = 0, QL_CB_FP4 = 1, QL_CB_INT4 = 2 };
+/* Block-scale codes of the q4_* calls: QL_SC_GROUPMAX is nf4_double_quant's. */
+enum { QL_SC_GROUPMAX = 0, QL_SC_FULLRANGE = 1, QL_SC_MEAN = 2, QL_SC_ABSMAX = 3 };
 
 /* First quantisation level (nlp-lineage page, "The idea", NF4 and
  * double-quantisation bullets).
@@ -174,6 +179,49 @@ int qlora_linear_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N,
 int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t N, int64_t K,
                 const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
                 uint16_t* W_out, void* stream);
+
+/* The 4-bit baselines the pages rank NF4 against (nlp-lineage page, "What it
+ * showed": NF4 with double quantization against a standard 4-bit float and
+ * 4-bit integers; inferensys glossary, NF4 paragraph), run through the same
+ * blockwise-absmax encoder and table dequantizer, and two further ways to
+ * code the block scales. Code books (16 fp32 levels, ascending; code 7 is 0):
+ *   QL_CB_NF4   the layer's NF4 table,
+ *   QL_CB_FP4   OCP E2M1 values / 6 (the block absmax maps to the largest, 6),
+ *   QL_CB_INT4  k / 7 for k = -7..7;
+ * FP4 and INT4 have 15 distinct values and code 15 repeats +1 (never produced:
+ * ties go to the smaller code).
+ *
+ * q4_quantize: as nf4_quantize with the chosen table: absmax a per 64, n =
+ * fl32(w / a) correctly rounded (0 for an all-zero block), code = nearest
+ * level. Same layouts and errors as nf4_quantize; QL_ERR_DTYPE for an unknown
+ * code book.                                                                    */
+int q4_quantize(const void* W, int w_dtype, int64_t rows, int64_t cols, int codebook,
+                uint8_t* codes, float* absmax, void* stream);
+
+/* q4_double_quant: block scales absmax [n_blocks] to one E4M3FN byte each plus
+ * per-group fp32 values (groups of 256, the last may be partial):
+ *   QL_SC_GROUPMAX   exactly nf4_double_quant (mu unused, may be NULL);
+ *   QL_SC_FULLRANGE  c1 = fl32(max / 448), c2 = E4M3FN(fl32(a / c1)) (0 if c1 = 0);
+ *   QL_SC_MEAN       mu = fl32(S / count), S the fp32 sum over the zero-padded
+ *                    group taken pairwise (i with i + h, h = 128, 64, ..., 1);
+ *                    d = fl32(a - mu); c1 = fl32(max |d| / 448);
+ *                    c2 = signed E4M3FN of fl32(d / c1) (0 if c1 = 0).
+ * Outputs c2 [n_blocks], c1 [groups], mu [groups] (QL_SC_MEAN only; required).  */
+int q4_double_quant(const float* absmax, int64_t n_blocks, int scale_code,
+                    uint8_t* c2, float* c1, float* mu, void* stream);
+
+/* q4_dequantize: W'[e] = bf16(fl32(q[code_e] * s_b)) for the chosen table, with
+ *   QL_SC_ABSMAX               s_b = absmax[b] (c2, c1, mu unused);
+ *   QL_SC_GROUPMAX, _FULLRANGE s_b = fl32(dec(c2[b]) * c1[b / 256]);
+ *   QL_SC_MEAN                 s_b = fl32(mu[b / 256] + fl32(dec(c2[b]) * c1[b / 256])).
+ * With QL_CB_NF4 and QL_SC_GROUPMAX this is nf4_dequantize.                    */
+int q4_dequantize(const uint8_t* codes, int64_t rows, int64_t cols, int codebook, int scale_code,
+                  const float* absmax, const uint8_t* c2, const float* c1, const float* mu,
+                  uint16_t* W_bf16, void* stream);
+
+/* Host helper: the 16 levels of a code book, copied to out16 (QL_ERR_DTYPE for
+ * an unknown id).                                                               */
+int q4_levels(int codebook, float* out16);
 
 /* Host-only helpers (no GPU needed). */
 /* The 16 NF4 levels (fp32, ascending) that the kernels use, copied to out[16].  */

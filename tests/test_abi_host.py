@@ -136,3 +136,36 @@ def test_merge_validation():
     assert mrg(N=1 << 26, K=1 << 11) == -2   # N K above 2^36
     assert mrg(L1=MIS) == -4
     assert mrg(out=MIS) == -4
+
+
+def test_q4_levels_match_oracle_bitwise():
+    q, _ = _lib()
+    for name in ("nf4", "fp4", "int4"):
+        lv = np.array(q.q4_levels(name), dtype=np.float32)
+        assert np.array_equal(lv.view(np.uint32), O.variants.codebook_levels(name).view(np.uint32)), name
+
+
+def test_q4_validation():
+    _, L = _lib()
+    assert L.q4_quantize(A, 0, 4, 64, 3, A, A, None) == -3
+    assert L.q4_quantize(A, 0, 4, 64, -1, A, A, None) == -3
+    assert L.q4_quantize(A, 0, 4, 96, 1, A, A, None) == -2
+    assert L.q4_quantize(A, 0, 4, 64, 1, None, A, None) == -1
+    assert L.q4_quantize(MIS, 1, 4, 64, 2, A, A, None) == -4
+    assert L.q4_double_quant(A, 10, 4, A, A, A, None) == -3
+    assert L.q4_double_quant(A, 10, 3, A, A, A, None) == -3       # absmax scales have no second level
+    assert L.q4_double_quant(A, 10, 2, A, A, None, None) == -1    # mean-centred needs mu
+    assert L.q4_double_quant(A, 0, 1, A, A, None, None) == -2
+    assert L.q4_double_quant(A, 10, 2, A, A, MIS, None) == -4
+    deq = lambda cb=0, sc=0, am=None, c2=A, c1=A, mu=None, cols=64: L.q4_dequantize(
+        A, 4, cols, cb, sc, am, c2, c1, mu, A, None)
+    assert deq(cb=5) == -3
+    assert deq(sc=4) == -3
+    assert deq(sc=3) == -1                                          # absmax missing
+    assert deq(sc=2) == -1                                          # mu missing
+    assert deq(c2=None) == -1
+    assert deq(cols=100) == -2
+    assert deq(sc=3, am=MIS) == -4
+    buf = (ctypes.c_float * 16)()
+    assert L.q4_levels(3, ctypes.cast(buf, ctypes.c_void_p)) == -3
+    assert L.q4_levels(1, None) == -1
