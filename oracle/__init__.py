@@ -13,3 +13,4 @@ from .qlora_oracle import (  # noqa: F401
     qlora_forward, qlora_backward, qlora_merge, bits_per_weight,
 )
 from . import variants  # noqa: F401,E402  (code-book and second-level-scale variants)
+from . import block  # noqa: F401,E402  (stacked linears and the adapter-only optimizer step)
