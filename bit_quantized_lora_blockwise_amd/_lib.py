@@ -20,12 +20,14 @@ QL_F32, QL_BF16 = 0, 1
 CODEBOOKS = {"nf4": 0, "fp4": 1, "int4": 2}
 SCALE_CODES = {"groupmax": 0, "fullrange": 1, "mean": 2, "absmax": 3}
 STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_DTYPE", -4: "QL_ERR_ALIGN",
-          -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_HIP"}
+          -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_HIP", -7: "QL_ERR_VALUE"}
 EXPORTS = ("nf4_quantize", "nf4_double_quant", "nf4_dequantize", "qlora_linear_fwd_workspace",
            "qlora_linear_fwd", "qlora_linear_bwd_workspace", "qlora_linear_bwd", "qlora_nf4_levels",
            "ql_status_string", "qlora_lora_down_workspace", "qlora_lora_down", "qlora_linear_fwd_t",
            "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx", "qlora_merge",
-           "q4_quantize", "q4_double_quant", "q4_dequantize", "q4_levels")
+           "q4_quantize", "q4_double_quant", "q4_dequantize", "q4_levels",
+           "qlora_group_fwd_workspace", "qlora_group_fwd", "qlora_group_bwd_workspace", "qlora_group_bwd",
+           "qlora_adamw_step")
 
 
 class QloraError(RuntimeError):
@@ -64,6 +66,11 @@ def lib():
             "q4_double_quant": ([P, I64, I32, P, P, P, P], I32),
             "q4_dequantize": ([P, I64, I64, I32, I32, P, P, P, P, P, P], I32),
             "q4_levels": ([I32, P], I32),
+            "qlora_group_fwd_workspace": ([I64, I64, I64, I32, I32], SZ),
+            "qlora_group_fwd": ([P, I64, I64, I64, I32, P, P, P, P, P, I32, F32, P, P, P, SZ, P], I32),
+            "qlora_group_bwd_workspace": ([I64, I64, I64, I32, I32], SZ),
+            "qlora_group_bwd": ([P, P, I64, I64, I64, I32, P, P, P, P, P, I32, F32, P, P, P, P, P, SZ, P], I32),
+            "qlora_adamw_step": ([P, P, P, P, P, I64, F32, F32, F32, F32, F32, I64, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -275,6 +282,71 @@ def qlora_linear_bwd(X, dY, codes, c2, c1, L1, L2, lora_scale=1.0, T=None, dX=Tr
         _ptr(X), _ptr(dY), M, K, N, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(L1), _ptr(L2), r, float(lora_scale),
         _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(ws), ws.numel(), _stream(stream)))
     return dX, dL1, dL2
+
+
+def qlora_group_fwd(X, codes, c2, c1, N, G, L1, L2, lora_scale=1.0, Y=None, T_out=None, workspace=None,
+                    stream=None):
+    """G stacked linears sharing X (W [G N, K] quantized as one; L1 [G, K, r], L2 [G, r, N]):
+    Y [M, G N] = [Y_0 | ... | Y_{G-1}].  Returns (Y, T_out [G, M, r] or None)."""
+    _need(X, "X", torch.bfloat16, 2); _need(L1, "L1", torch.bfloat16, 3); _need(L2, "L2", torch.bfloat16, 3)
+    _need(codes, "codes", torch.uint8); _need(c2, "c2", torch.uint8); _need(c1, "c1", torch.float32)
+    M, K = X.shape
+    r = L1.shape[2]
+    if tuple(L1.shape) != (G, K, r) or tuple(L2.shape) != (G, r, N):
+        raise ValueError(f"qlora_group_fwd: L1 {tuple(L1.shape)} / L2 {tuple(L2.shape)} vs G={G}, K={K}, N={N}")
+    Y = _empty((M, G * N), torch.bfloat16, X) if Y is None else _need(Y, "Y", torch.bfloat16)
+    if T_out is True:
+        T_out = _empty((G, M, r), torch.bfloat16, X)
+    elif T_out is not None:
+        _need(T_out, "T_out", torch.bfloat16)
+    ws = _workspace(int(lib().qlora_group_fwd_workspace(M, K, N, G, r)), X, workspace)
+    _check("qlora_group_fwd", lib().qlora_group_fwd(
+        _ptr(X), M, K, N, G, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(L1), _ptr(L2), r, float(lora_scale),
+        _ptr(Y), _ptr(T_out), _ptr(ws), ws.numel(), _stream(stream)))
+    return Y, T_out
+
+
+def qlora_group_bwd(X, dY, codes, c2, c1, G, L1, L2, lora_scale=1.0, T=None, dX=True, dL1=None, dL2=None,
+                    workspace=None, stream=None):
+    """(dX or None, dL1 [G, K, r], dL2 [G, r, N]) of G stacked linears; dX sums the segments, rounded once."""
+    _need(X, "X", torch.bfloat16, 2); _need(dY, "dY", torch.bfloat16, 2)
+    _need(L1, "L1", torch.bfloat16, 3); _need(L2, "L2", torch.bfloat16, 3)
+    _need(codes, "codes", torch.uint8); _need(c2, "c2", torch.uint8); _need(c1, "c1", torch.float32)
+    M, K = X.shape
+    N = dY.shape[1] // G
+    r = L1.shape[2]
+    if T is not None:
+        _need(T, "T", torch.bfloat16)
+    if dX is True:
+        dX = _empty((M, K), torch.bfloat16, X)
+    elif dX is False:
+        dX = None
+    elif dX is not None:
+        _need(dX, "dX", torch.bfloat16)
+    dL1 = _empty((G, K, r), torch.float32, X) if dL1 is None else _need(dL1, "dL1", torch.float32)
+    dL2 = _empty((G, r, N), torch.float32, X) if dL2 is None else _need(dL2, "dL2", torch.float32)
+    ws = _workspace(int(lib().qlora_group_bwd_workspace(M, K, N, G, r)), X, workspace)
+    _check("qlora_group_bwd", lib().qlora_group_bwd(
+        _ptr(X), _ptr(dY), M, K, N, G, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(L1), _ptr(L2), r, float(lora_scale),
+        _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(ws), ws.numel(), _stream(stream)))
+    return dX, dL1, dL2
+
+
+def qlora_adamw_step(param, exp_avg, exp_avg_sq, grad, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                     weight_decay=0.0, param_bf16=None, stream=None):
+    """One AdamW step over flat fp32 tensors (in place); param_bf16 (optional) gets bf16(param)."""
+    for t, n in ((param, "param"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad")):
+        _need(t, n, torch.float32)
+    n = param.numel()
+    if any(t.numel() != n for t in (exp_avg, exp_avg_sq, grad)):
+        raise ValueError("qlora_adamw_step: all state tensors must have the parameter's size")
+    if param_bf16 is not None:
+        _need(param_bf16, "param_bf16", torch.bfloat16)
+        if param_bf16.numel() != n:
+            raise ValueError("qlora_adamw_step: param_bf16 must have the parameter's size")
+    _check("qlora_adamw_step", lib().qlora_adamw_step(
+        _ptr(param), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad), _ptr(param_bf16), n, float(lr), float(beta1),
+        float(beta2), float(eps), float(weight_decay), int(step), _stream(stream)))
 
 
 def qlora_nf4_levels():

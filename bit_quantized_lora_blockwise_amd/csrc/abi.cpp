@@ -1,6 +1,7 @@
 // C ABI of libqlora.so: argument checks, workspace sizing and kernel dispatch.
 // Declarations and the contract of each entry point are in include/qlora.h.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 
@@ -79,6 +80,30 @@ hipError_t run_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, cons
   if (qgemm_big_ok(true, M, K, N))
     return launch_qgemm_big(true, dY, M, K, N, codes, c2, c1, G, L1, r, 1.0f, dX, s);
   return launch_qgemm_dx(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s);
+}
+
+// ---- stacked linears -------------------------------------------------------
+bool group_ok(int64_t M, int64_t K, int64_t N, int G, int r) {
+  if (G < 1 || G > 16 || N <= 0 || N > (int64_t(1) << 31) / G) return false;
+  if (!shapes_ok(M, K, N * G, r)) return false;
+  if (G == 1) return true;
+  return N % 256 == 0 && M > 16 && qgemm_big_ok(false, M, K, N * G) && qgemm_big_ok(true, M, K, N * G);
+}
+
+struct GroupWs {
+  size_t t_bytes, g_bytes, part_bytes, total;
+};
+GroupWs group_ws(int64_t M, int64_t K, int64_t N, int G, int r) {
+  GroupWs w;
+  w.t_bytes = round_up((size_t)G * M * r * 2);
+  w.g_bytes = round_up((size_t)G * M * r * 2);
+  size_t p = lora_skinny_ws(M, K, r);
+  p = std::max(p, lora_skinny_ws(M, N, r));
+  p = std::max(p, lora_tn_ws(M, K, r));
+  p = std::max(p, lora_tn_ws(M, N, r));
+  w.part_bytes = round_up(p);
+  w.total = w.t_bytes + w.g_bytes + w.part_bytes;
+  return w;
 }
 
 }  // namespace
@@ -176,6 +201,97 @@ int q4_levels(int codebook, float* out16) {
   return QL_OK;
 }
 
+
+size_t qlora_group_fwd_workspace(int64_t M, int64_t K, int64_t N, int G, int r) {
+  if (!group_ok(M, K, N, G, r)) return 0;
+  const GroupWs w = group_ws(M, K, N, G, r);
+  return w.t_bytes + w.part_bytes;
+}
+
+int qlora_group_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, int G, const uint8_t* codes,
+                    const uint8_t* c2, const float* c1, const uint16_t* L1, const uint16_t* L2, int r,
+                    float lora_scale, uint16_t* Y, uint16_t* T_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!X || !codes || !c2 || !c1 || !L1 || !L2 || !Y) return QL_ERR_NULL;
+  if (!group_ok(M, K, N, G, r)) return QL_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(codes) || !aligned16(c2) || !aligned16(c1) || !aligned16(L1) ||
+      !aligned16(L2) || !aligned16(Y) || (T_out && !aligned16(T_out)))
+    return QL_ERR_ALIGN;
+  if (G == 1)
+    return qlora_linear_fwd(X, M, K, N, codes, c2, c1, L1, L2, r, lora_scale, Y, T_out, workspace, ws_bytes,
+                            stream);
+  const GroupWs w = group_ws(M, K, N, G, r);
+  if (!workspace || ws_bytes < w.t_bytes + w.part_bytes) return QL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  uint16_t* T = T_out ? T_out : (uint16_t*)ws;
+  float* part = (float*)(ws + w.t_bytes);
+  for (int g = 0; g < G; ++g)
+    QL_TRY(launch_lora_skinny(X, M, K, K, L1 + (int64_t)g * K * r, true, r, 1.0f, T + (int64_t)g * M * r, part, s));
+  QL_TRY(launch_qgemm_big(false, X, M, K, N * G, codes, c2, c1, T, L2, r, lora_scale, Y, s, G));
+  return QL_OK;
+}
+
+size_t qlora_group_bwd_workspace(int64_t M, int64_t K, int64_t N, int G, int r) {
+  if (!group_ok(M, K, N, G, r)) return 0;
+  return group_ws(M, K, N, G, r).total;
+}
+
+int qlora_group_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K, int64_t N, int G,
+                    const uint8_t* codes, const uint8_t* c2, const float* c1, const uint16_t* L1, const uint16_t* L2,
+                    int r, float lora_scale, const uint16_t* T, uint16_t* dX, float* dL1, float* dL2,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  if (!X || !dY || !codes || !c2 || !c1 || !L1 || !L2 || !dL1 || !dL2) return QL_ERR_NULL;
+  if (!group_ok(M, K, N, G, r)) return QL_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(codes) || !aligned16(c2) || !aligned16(c1) ||
+      !aligned16(L1) || !aligned16(L2) || !aligned16(dL1) || !aligned16(dL2) || (T && !aligned16(T)) ||
+      (dX && !aligned16(dX)))
+    return QL_ERR_ALIGN;
+  if (G == 1)
+    return qlora_linear_bwd(X, dY, M, K, N, codes, c2, c1, L1, L2, r, lora_scale, T, dX, dL1, dL2, workspace,
+                            ws_bytes, stream);
+  const GroupWs w = group_ws(M, K, N, G, r);
+  if (!workspace || ws_bytes < w.total) return QL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  uint16_t* Tw = (uint16_t*)ws;
+  uint16_t* Gm = (uint16_t*)(ws + w.t_bytes);
+  float* part = (float*)(ws + w.t_bytes + w.g_bytes);
+  const int64_t ldy = N * G;
+  for (int g = 0; g < G; ++g) {
+    const int64_t mr = (int64_t)g * M * r;
+    if (!T) QL_TRY(launch_lora_skinny(X, M, K, K, L1 + (int64_t)g * K * r, true, r, 1.0f, Tw + mr, part, s));
+    QL_TRY(launch_lora_skinny(dY + (int64_t)g * N, M, N, ldy, L2 + (int64_t)g * r * N, false, r, lora_scale, Gm + mr,
+                              part, s));
+  }
+  const uint16_t* Tg = T ? T : Tw;
+  if (dX) QL_TRY(launch_qgemm_big(true, dY, M, K, N * G, codes, c2, c1, Gm, L1, r, 1.0f, dX, s, G));
+  for (int g = 0; g < G; ++g) {
+    const int64_t mr = (int64_t)g * M * r;
+    QL_TRY(launch_lora_tn(X, K, Gm + mr, M, K, r, 1.0f, false, dL1 + (int64_t)g * K * r, part, s));
+    QL_TRY(launch_lora_tn(dY + (int64_t)g * N, ldy, Tg + mr, M, N, r, lora_scale, true, dL2 + (int64_t)g * r * N,
+                          part, s));
+  }
+  return QL_OK;
+}
+
+int qlora_adamw_step(float* param, float* exp_avg, float* exp_avg_sq, const float* grad, uint16_t* param_bf16,
+                     int64_t n, float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                     void* stream) {
+  if (!param || !exp_avg || !exp_avg_sq || !grad) return QL_ERR_NULL;
+  if (n <= 0 || n > (int64_t(1) << 40) || step < 1) return QL_ERR_SHAPE;
+  if (!(lr >= 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) ||
+      !(weight_decay >= 0.0f) || !std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(weight_decay))
+    return QL_ERR_VALUE;
+  if (!aligned16(param) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) || !aligned16(grad) ||
+      (param_bf16 && !aligned16(param_bf16)))
+    return QL_ERR_ALIGN;
+  QL_TRY(launch_adamw(param, exp_avg, exp_avg_sq, grad, param_bf16, n, lr, beta1, beta2, eps, weight_decay, step,
+                      (hipStream_t)stream));
+  return QL_OK;
+}
+
 size_t qlora_linear_fwd_workspace(int64_t M, int64_t K, int64_t N, int r) {
   if (!shapes_ok(M, K, N, r)) return 0;
   return fwd_ws(M, K, N, r).total;
@@ -196,7 +312,7 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const u
   char* ws = (char*)workspace;
   uint16_t* T = T_out ? T_out : (uint16_t*)ws;
   float* part = (float*)(ws + w.t_bytes);
-  QL_TRY(launch_lora_skinny(X, M, K, L1, true, r, 1.0f, T, part, s));
+  QL_TRY(launch_lora_skinny(X, M, K, K, L1, true, r, 1.0f, T, part, s));
   if (M <= 16)
     QL_TRY(launch_qgemv_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));
   else
@@ -228,13 +344,13 @@ int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K
   uint16_t* G = (uint16_t*)(ws + w.t_bytes);
   float* part = (float*)(ws + w.t_bytes + w.g_bytes);
   if (!T) {
-    QL_TRY(launch_lora_skinny(X, M, K, L1, true, r, 1.0f, Tw, part, s));
+    QL_TRY(launch_lora_skinny(X, M, K, K, L1, true, r, 1.0f, Tw, part, s));
     T = Tw;
   }
-  QL_TRY(launch_lora_skinny(dY, M, N, L2, false, r, lora_scale, G, part, s));
+  QL_TRY(launch_lora_skinny(dY, M, N, N, L2, false, r, lora_scale, G, part, s));
   if (dX) QL_TRY(run_dx_gemm(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s));
-  QL_TRY(launch_lora_tn(X, G, M, K, r, 1.0f, false, dL1, part, s));
-  QL_TRY(launch_lora_tn(dY, T, M, N, r, lora_scale, true, dL2, part, s));
+  QL_TRY(launch_lora_tn(X, K, G, M, K, r, 1.0f, false, dL1, part, s));
+  QL_TRY(launch_lora_tn(dY, N, T, M, N, r, lora_scale, true, dL2, part, s));
   return QL_OK;
 }
 
@@ -250,7 +366,7 @@ int qlora_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1,
   if (!aligned16(X) || !aligned16(L1) || !aligned16(T)) return QL_ERR_ALIGN;
   if (!workspace || ws_bytes < qlora_lora_down_workspace(M, K, r)) return QL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return QL_ERR_ALIGN;
-  QL_TRY(launch_lora_skinny(X, M, K, L1, true, r, 1.0f, T, (float*)workspace, (hipStream_t)stream));
+  QL_TRY(launch_lora_skinny(X, M, K, K, L1, true, r, 1.0f, T, (float*)workspace, (hipStream_t)stream));
   return QL_OK;
 }
 
@@ -283,7 +399,7 @@ int qlora_lora_grad_in(const uint16_t* dY, int64_t M, int64_t N, const uint16_t*
   if (!aligned16(dY) || !aligned16(L2) || !aligned16(G)) return QL_ERR_ALIGN;
   if (!workspace || ws_bytes < need) return QL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return QL_ERR_ALIGN;
-  QL_TRY(launch_lora_skinny(dY, M, N, L2, false, r, lora_scale, G, (float*)workspace, (hipStream_t)stream));
+  QL_TRY(launch_lora_skinny(dY, M, N, N, L2, false, r, lora_scale, G, (float*)workspace, (hipStream_t)stream));
   return QL_OK;
 }
 
@@ -310,6 +426,7 @@ const char* ql_status_string(int status) {
     case QL_ERR_NULL: return "a required pointer is NULL";
     case QL_ERR_SHAPE: return "invalid shape (sizes must be > 0, K and cols multiples of 64, 1 <= r <= 64)";
     case QL_ERR_DTYPE: return "unsupported dtype, code book or scale code";
+    case QL_ERR_VALUE: return "hyper-parameter out of range";
     case QL_ERR_ALIGN: return "device pointers must be 16-byte aligned";
     case QL_ERR_WORKSPACE: return "workspace missing or smaller than the size query returns";
     case QL_ERR_HIP:

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ LA,   // T (fwd) / G (dX)
                                                      const uint16_t* __restrict__ LB,   // L2 (fwd) / L1 (dX)
                                                      int r, float scale, uint16_t* __restrict__ C,
-                                                     Nf4Params p) {
+                                                     Nf4Params p, int nseg, int64_t seg) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_b[2 * kBufElems];   // weight tiles; LoRA operands first
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[2 * kBM * kBR];   // activation tiles
   const int t = threadIdx.x;
@@ -187,54 +187,76 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   f32x16 acc[2][4];
 
   // ---- LoRA term first: fwd acc = s * (T L2); dX acc = G L1^T (rank zero-padded
-  //      to 64); the base product then accumulates onto it.
+  //      to 64); the base product then accumulates onto it.  With nseg > 1
+  //      segments of seg output columns (fwd) or reduction columns (dX), each
+  //      segment g has its own T_g / G_g [M, r] (at LA + g M r) and L2_g [r, seg]
+  //      (at LB + g r seg) / L1_g [K, r] (at LB + g K r): the forward tile uses
+  //      its own segment's pair (tiles never straddle segments), the dX tile
+  //      sums the products of all segments.
   {
     LDS_AS uint16_t* la = (LDS_AS uint16_t*)lds_b;                 // [256][kPL]: T / G rows
     LDS_AS uint16_t* lb = (LDS_AS uint16_t*)lds_b + kBM * kPL;     // fwd: L2 [64][kPD]; dX: L1 [256][kPL]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
-      u32x4 v = {0, 0, 0, 0};
-      if (m0 + row < M) v = load_row8(LA + (m0 + row) * r, cc, r);
-      *(LDS_AS u32x4*)(la + row * kPL + cc) = v;
-    }
-    if (!kDx) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = (t >> 5) + 16 * i, pp = (t & 31) * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (c < r) v = load_row8(LB + (int64_t)c * N, p0 + pp, N);
-        *(LDS_AS u32x4*)(lb + c * kPD + pp) = v;
-      }
-    } else {
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    const int ng = kDx ? nseg : 1;
+    for (int g = 0; g < ng; ++g) {
+      const int64_t gs = kDx ? g : p0 / seg;
+      const uint16_t* la_src = LA + gs * M * r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
         u32x4 v = {0, 0, 0, 0};
-        if (p0 + row < K) v = load_row8(LB + (p0 + row) * r, cc, r);
-        *(LDS_AS u32x4*)(lb + row * kPL + cc) = v;
+        if (m0 + row < M) v = load_row8(la_src + (m0 + row) * r, cc, r);
+        *(LDS_AS u32x4*)(la + row * kPL + cc) = v;
       }
-    }
-    __syncthreads();
-    const int ksteps = (r + 15) / 16;
-    const float ls = kDx ? 1.0f : scale;
+      if (!kDx) {
+        const uint16_t* lb_src = LB + gs * r * seg;
+        const int64_t pc = p0 - gs * seg;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x16 z = {};
-        for (int s = 0; s < ksteps; ++s) {
-          const bf16x8 a = qk::frag_rowmajor(la, kPL, 64 * rg + 32 * i, 16 * s);
-          // dX: the column of accumulator slot (l % 32) is dx_slot_col(l % 32)
-          const bf16x8 b =
-              kDx ? *(const LDS_AS bf16x8*)(lb + (128 * ch + 32 * j + dx_slot_col(l & 31)) * kPL + 16 * s +
-                                            8 * (l >> 5))
-                  : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
-          z = qk::mfma32(a, b, z);
+        for (int i = 0; i < 4; ++i) {
+          const int c = (t >> 5) + 16 * i, pp = (t & 31) * 8;
+          u32x4 v = {0, 0, 0, 0};
+          if (c < r) v = load_row8(lb_src + (int64_t)c * seg, pc + pp, seg);
+          *(LDS_AS u32x4*)(lb + c * kPD + pp) = v;
         }
-        acc[i][j] = ls * z;
+      } else {
+        const uint16_t* lb_src = LB + gs * K * r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
+          u32x4 v = {0, 0, 0, 0};
+          if (p0 + row < K) v = load_row8(lb_src + (p0 + row) * r, cc, r);
+          *(LDS_AS u32x4*)(lb + row * kPL + cc) = v;
+        }
       }
-    __syncthreads();
+      __syncthreads();
+      const int ksteps = (r + 15) / 16;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x16 z = acc[i][j];
+          for (int s = 0; s < ksteps; ++s) {
+            const bf16x8 a = qk::frag_rowmajor(la, kPL, 64 * rg + 32 * i, 16 * s);
+            // dX: the column of accumulator slot (l % 32) is dx_slot_col(l % 32)
+            const bf16x8 b =
+                kDx ? *(const LDS_AS bf16x8*)(lb + (128 * ch + 32 * j + dx_slot_col(l & 31)) * kPL + 16 * s +
+                                              8 * (l >> 5))
+                    : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
+            z = qk::mfma32(a, b, z);
+          }
+          acc[i][j] = z;
+        }
+      __syncthreads();
+    }
+    if (!kDx) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = scale * acc[i][j];
+    }
   }
 
   // ---- activation tiles.  Wave w loads rows 64 (w % 4) + 32 (w / 4) .. +32 of
@@ -422,17 +444,18 @@ bool qgemm_big_ok(bool dx, int64_t M, int64_t K, int64_t N) {
 
 hipError_t launch_qgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                             const uint8_t* c2, const float* c1, const uint16_t* LA, const uint16_t* LB, int r,
-                            float scale, uint16_t* C, hipStream_t s) {
+                            float scale, uint16_t* C, hipStream_t s, int nseg) {
   const int64_t P = dx ? K : N;
+  const int64_t seg = N / nseg;   // columns of W per segment (a multiple of 256 when nseg > 1)
   dim3 grid((unsigned)((P + kBP - 1) / kBP), (unsigned)((M + kBM - 1) / kBM));
   if (!dx)
     hipLaunchKernelGGL((k_qgemm_big<false, false>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
-                       scale, C, nf4_params());
+                       scale, C, nf4_params(), nseg, seg);
   else if (N % kBR == 0)
     hipLaunchKernelGGL((k_qgemm_big<true, false>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
-                       scale, C, nf4_params());
+                       scale, C, nf4_params(), nseg, seg);
   else
     hipLaunchKernelGGL((k_qgemm_big<true, true>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
-                       scale, C, nf4_params());
+                       scale, C, nf4_params(), nseg, seg);
   return hipGetLastError();
 }

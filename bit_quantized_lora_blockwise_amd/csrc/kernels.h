@@ -42,24 +42,30 @@ struct SplitPlan {
 };
 SplitPlan plan_rowsplit(int64_t tiles, int64_t R);
 
-// C[M, r] = A[M, R] * B, B(k, c) = L1[k][c] (b_rmajor_kr = true, L1 is [R, r])
-// or B(k, c) = L2[c][k] (false, L2 is [r, R]).  Result scaled by `scale`,
-// rounded to bf16 into out[M, r].  ws holds the fp32 partials.
+// C[M, r] = A[M, R] * B, A with row stride lda, B(k, c) = L1[k][c] (b_is_kr =
+// true, L1 is [R, r]) or B(k, c) = L2[c][k] (false, L2 is [r, R]).  Result
+// scaled by `scale`, rounded to bf16 into out[M, r].  ws holds the fp32 partials.
 size_t lora_skinny_ws(int64_t M, int64_t R, int r);
-hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, const uint16_t* B, bool b_is_kr, int r,
-                              float scale, uint16_t* out, float* ws, hipStream_t s);
+hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t lda, const uint16_t* B, bool b_is_kr,
+                              int r, float scale, uint16_t* out, float* ws, hipStream_t s);
 
-// C[p, c] = scale * sum_m A[m][p] * B[m][c] with A [M, P], B [M, r]; stored as
-// out[P, r] (transpose_out = false) or out[r, P] (true), fp32.
+// C[p, c] = scale * sum_m A[m][p] * B[m][c] with A [M, P] (row stride lda),
+// B [M, r]; stored as out[P, r] (transpose_out = false) or out[r, P] (true), fp32.
 size_t lora_tn_ws(int64_t M, int64_t P, int r);
-hipError_t launch_lora_tn(const uint16_t* A, const uint16_t* B, int64_t M, int64_t P, int r, float scale,
-                          bool transpose_out, float* out, float* ws, hipStream_t s);
+hipError_t launch_lora_tn(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t M, int64_t P, int r,
+                          float scale, bool transpose_out, float* out, float* ws, hipStream_t s);
 
 // --- adapter merge (merge.hip) ---------------------------------------------
 // W[n][k] = bf16(W'[n][k] + scale * sum_c L1[k][c] L2[c][n]), W' the bf16
 // dequantised base; W [N, K], K a multiple of 64.
 hipError_t launch_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t N, int64_t K,
                         const uint16_t* L1, const uint16_t* L2, int r, float scale, uint16_t* W, hipStream_t s);
+
+// --- adapter optimizer (adamw.hip) -------------------------------------------
+// One AdamW step over n fp32 weights (decoupled decay), optional bf16 copy.
+hipError_t launch_adamw(float* param, float* exp_avg, float* exp_avg_sq, const float* grad, uint16_t* param_bf16,
+                        int64_t n, float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                        hipStream_t s);
 
 // --- quantised GEMMs (gemm.hip, decode.hip) ----------------------------------
 // Y[M, N] = bf16(X W'^T + scale * T L2)
@@ -72,11 +78,14 @@ hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, 
                             float scale, uint16_t* Y, hipStream_t s);
 // Large-tile (256 x 256) versions of both GEMMs: dx = false computes the forward
 // (A = X, LA = T, LB = L2, C = Y), dx = true the dX product (A = dY, LA = G,
-// LB = L1, C = dX).  qgemm_big_ok says whether the shapes qualify.
+// LB = L1, C = dX).  qgemm_big_ok says whether the shapes qualify.  nseg > 1:
+// W [N, K] is nseg matrices of N / nseg rows stacked (N / nseg a multiple of
+// 256), each with its own adapter: LA holds nseg [M, r] blocks, LB nseg L2
+// [r, N / nseg] (fwd) or L1 [K, r] (dX) blocks.
 bool qgemm_big_ok(bool dx, int64_t M, int64_t K, int64_t N);
 hipError_t launch_qgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                             const uint8_t* c2, const float* c1, const uint16_t* LA, const uint16_t* LB, int r,
-                            float scale, uint16_t* C, hipStream_t s);
+                            float scale, uint16_t* C, hipStream_t s, int nseg = 1);
 // dX[M, K] = bf16(dY W' + G L1^T)
 hipError_t launch_qgemm_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                            const uint8_t* c2, const float* c1, const uint16_t* G, const uint16_t* L1, int r,

@@ -79,11 +79,12 @@ __device__ __forceinline__ void store_tile(const Tile& tl, LDS_AS uint16_t* dst)
   for (int i = 0; i < 2; ++i) *(LDS_AS u32x4*)(dst + ((t >> 3) + 32 * i) * kPitch + (t & 7) * 8) = tl.v[i];
 }
 
-// C[M, r] partial over one reduction slice: A [M, R] row-major times B, where
+// C[M, r] partial over one reduction slice: A [M, R] (row stride lda) times B, where
 // B(k, c) = Bm[k * r + c] (kBkr, L1 [R, r]) or Bm[c * R + k] (!kBkr, L2 [r, R]).
 template <bool kBkr>
 __global__ __launch_bounds__(kThreads) void k_lora_skinny(const uint16_t* __restrict__ A, int64_t M, int64_t R,
-                                                          const uint16_t* __restrict__ Bm, int r, int64_t chunk,
+                                                          int64_t lda, const uint16_t* __restrict__ Bm, int r,
+                                                          int64_t chunk,
                                                           float* __restrict__ part, int avec, int bvec) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * kPitch];
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void k_lora_skinny(const uint16_t* __rest
     const int64_t k0 = k_beg + st * kTile;
     const int64_t kl = k_end - k0;                     // columns of the slice left (<= 0: zeros)
     const int64_t k0c = kl > 0 ? k0 : 0;
-    ta = load_tile(A + m0 * R + k0c, R, M - m0, kl, (uint64_t)((M - m0) * R - k0c) * 2, avec);
+    ta = load_tile(A + m0 * lda + k0c, lda, M - m0, kl, (uint64_t)((M - m0) * lda - k0c) * 2, avec);
     if (kBkr) tb = load_tile(Bm + k0c * r, r, kl, r, (uint64_t)((R - k0c) * r) * 2, bvec);
     else tb = load_tile(Bm + k0c, R, r, kl, (uint64_t)(r * R - k0c) * 2, bvec);
   };
@@ -150,8 +151,9 @@ __global__ __launch_bounds__(kThreads) void k_skinny_reduce(const float* __restr
 }
 
 // C[p, c] partial over one slice of m: sum_m A[m][p] * B[m][c], A [M, P], B [M, r].
-__global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                                      int64_t M, int64_t P, int r, int64_t chunk,
+__global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict__ A, int64_t lda,
+                                                      const uint16_t* __restrict__ B, int64_t M, int64_t P, int r,
+                                                      int64_t chunk,
                                                       float* __restrict__ part, int avec, int bvec) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * kPitch];
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict
     const int64_t mm = m_beg + st * kTile;
     const int64_t ml = m_end - mm;                     // rows of the slice left (<= 0: zeros)
     const int64_t mmc = ml > 0 ? mm : 0;
-    ta = load_tile(A + mmc * P + p0, P, ml, P - p0, (uint64_t)((M - mmc) * P - p0) * 2, avec);   // [m][p]
+    ta = load_tile(A + mmc * lda + p0, lda, ml, P - p0, (uint64_t)((M - mmc) * lda - p0) * 2, avec);   // [m][p]
     tb = load_tile(B + mmc * r, r, ml, r, (uint64_t)((M - mmc) * r) * 2, bvec);                // [m][c]
   };
   f32x16 acc = {};
@@ -249,17 +251,19 @@ size_t lora_skinny_ws(int64_t M, int64_t R, int r) {
   return (size_t)sp.splits * M * r * sizeof(float);
 }
 
-hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, const uint16_t* B, bool b_is_kr, int r,
-                              float scale, uint16_t* out, float* ws, hipStream_t s) {
+hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t lda, const uint16_t* B, bool b_is_kr,
+                              int r, float scale, uint16_t* out, float* ws, hipStream_t s) {
   const int64_t tiles = (M + kTile - 1) / kTile;
   const SplitPlan sp = plan_rowsplit(tiles, R);
   dim3 grid((unsigned)tiles, (unsigned)sp.splits);
-  const int avec = (R % 8) == 0;
+  const int avec = (R % 8) == 0 && (lda % 8) == 0 && ((uintptr_t)A & 15) == 0;
   const int bvec = b_is_kr ? (r % 8) == 0 : (R % 8) == 0;
   if (b_is_kr)
-    hipLaunchKernelGGL(k_lora_skinny<true>, grid, dim3(kThreads), 0, s, A, M, R, B, r, sp.chunk, ws, avec, bvec);
+    hipLaunchKernelGGL(k_lora_skinny<true>, grid, dim3(kThreads), 0, s, A, M, R, lda, B, r, sp.chunk, ws, avec,
+                       bvec);
   else
-    hipLaunchKernelGGL(k_lora_skinny<false>, grid, dim3(kThreads), 0, s, A, M, R, B, r, sp.chunk, ws, avec, bvec);
+    hipLaunchKernelGGL(k_lora_skinny<false>, grid, dim3(kThreads), 0, s, A, M, R, lda, B, r, sp.chunk, ws, avec,
+                       bvec);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_skinny_reduce, dim3(grid_for(M * r)), dim3(kThreads), 0, s, ws, sp.splits, M * (int64_t)r,
@@ -272,12 +276,13 @@ size_t lora_tn_ws(int64_t M, int64_t P, int r) {
   return (size_t)sp.splits * P * r * sizeof(float);
 }
 
-hipError_t launch_lora_tn(const uint16_t* A, const uint16_t* B, int64_t M, int64_t P, int r, float scale,
-                          bool transpose_out, float* out, float* ws, hipStream_t s) {
+hipError_t launch_lora_tn(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t M, int64_t P, int r,
+                          float scale, bool transpose_out, float* out, float* ws, hipStream_t s) {
   const int64_t tiles = (P + kTile - 1) / kTile;
   const SplitPlan sp = plan_rowsplit(tiles, M);
   dim3 grid((unsigned)tiles, (unsigned)sp.splits);
-  hipLaunchKernelGGL(k_lora_tn, grid, dim3(kThreads), 0, s, A, B, M, P, r, sp.chunk, ws, (int)((P % 8) == 0),
+  const int avec = (P % 8) == 0 && (lda % 8) == 0 && ((uintptr_t)A & 15) == 0;
+  hipLaunchKernelGGL(k_lora_tn, grid, dim3(kThreads), 0, s, A, lda, B, M, P, r, sp.chunk, ws, avec,
                      (int)((r % 8) == 0));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -59,7 +59,8 @@ typedef enum {
   QL_ERR_DTYPE = -3,     /* unsupported dtype, code book or scale code            */
   QL_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned               */
   QL_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the query returns      */
-  QL_ERR_HIP = -6        /* a HIP launch failed (see ql_status_string)            */
+  QL_ERR_HIP = -6,       /* a HIP launch failed (see ql_status_string)            */
+  QL_ERR_VALUE = -7      /* a hyper-parameter outside its range                   */
 } ql_status;
 
 enum { QL_F32 = 0, QL_BF16 = 1 };
@@ -179,6 +180,46 @@ int qlora_linear_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N,
 int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t N, int64_t K,
                 const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
                 uint16_t* W_out, void* stream);
+
+/* Stacked linears that read the same input (q|k|v, gate|up of a Transformer
+ * block; adapters go on every linear: nlp-lineage page, "The idea"). W [G N, K]
+ * is G matrices of N rows stacked along the output dimension and quantized as
+ * one (codes/c2/c1 as nf4_quantize/nf4_double_quant of the stack; when each
+ * matrix's N K / 64 blocks are a multiple of 256 this is bit-identical to the
+ * G separate quantizations). Segment g has its own adapter: L1 holds G
+ * consecutive [K, r] blocks, L2 G consecutive [r, N] blocks.
+ *   qlora_group_fwd: Y [M, G N] = [Y_0 | ... | Y_{G-1}], Y_g exactly as
+ *     qlora_linear_fwd of segment g; T_out (G consecutive [M, r]) optional.
+ *   qlora_group_bwd: dY [M, G N]; per segment G_g, dL1_g [K, r], dL2_g [r, N]
+ *     exactly as qlora_linear_bwd of segment g (dL1, dL2: G consecutive blocks);
+ *     dX = bf16(sum_g (dY_g W'_g + G_g L1_g^T)), one rounding (NULL: skipped).
+ * Requirements beyond qlora_linear_*: 1 <= G <= 16; for G > 1, N % 256 == 0 and
+ * M > 16 (QL_ERR_SHAPE otherwise). Workspace from the _workspace queries.      */
+size_t qlora_group_fwd_workspace(int64_t M, int64_t K, int64_t N, int G, int r);
+int qlora_group_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, int G,
+                    const uint8_t* codes, const uint8_t* c2, const float* c1,
+                    const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
+                    uint16_t* Y, uint16_t* T_out, void* workspace, size_t ws_bytes, void* stream);
+size_t qlora_group_bwd_workspace(int64_t M, int64_t K, int64_t N, int G, int r);
+int qlora_group_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K, int64_t N, int G,
+                    const uint8_t* codes, const uint8_t* c2, const float* c1,
+                    const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
+                    const uint16_t* T, uint16_t* dX, float* dL1, float* dL2,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Adapter-only optimizer step (inferensys glossary, frozen-base paragraph: the
+ * optimizer keeps momentum and variance for the adapters only). AdamW with
+ * decoupled weight decay over n fp32 values (typically every adapter of a
+ * block, laid out in one flat array so that one call updates them all):
+ *   theta <- theta (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+ *   theta <- theta - lr/(1 - b1^step) * m / (sqrt(v)/sqrt(1 - b2^step) + eps)
+ * param, exp_avg, exp_avg_sq updated in place (fp32); grad fp32 (as
+ * qlora_linear_bwd writes dL1/dL2); param_bf16 (optional) receives bf16(theta),
+ * the copy the layers read. step >= 1 counts calls from 1. QL_ERR_VALUE unless
+ * lr >= 0, 0 <= beta1, beta2 < 1, eps > 0, weight_decay >= 0.                  */
+int qlora_adamw_step(float* param, float* exp_avg, float* exp_avg_sq, const float* grad,
+                     uint16_t* param_bf16, int64_t n, float lr, float beta1, float beta2, float eps,
+                     float weight_decay, int64_t step, void* stream);
 
 /* The 4-bit baselines the pages rank NF4 against (nlp-lineage page, "What it
  * showed": NF4 with double quantization against a standard 4-bit float and

@@ -95,7 +95,7 @@ def test_linear_validation_and_workspace():
 
 def test_status_strings():
     q, _ = _lib()
-    for s in range(0, -7, -1):
+    for s in range(0, -8, -1):
         assert isinstance(q.ql_status_string(s), str) and q.ql_status_string(s)
 
 
@@ -169,3 +169,41 @@ def test_q4_validation():
     buf = (ctypes.c_float * 16)()
     assert L.q4_levels(3, ctypes.cast(buf, ctypes.c_void_p)) == -3
     assert L.q4_levels(1, None) == -1
+
+
+def test_group_and_adamw_validation():
+    _, L = _lib()
+    M, K, N, r = 64, 512, 256, 8
+    assert L.qlora_group_fwd_workspace(M, K, N, 3, r) > 0
+    assert L.qlora_group_fwd_workspace(M, K, 200, 3, r) == 0        # segments must be multiples of 256
+    assert L.qlora_group_fwd_workspace(M, K, 200, 1, r) > 0         # a single segment is the plain layer
+    assert L.qlora_group_fwd_workspace(16, K, N, 3, r) == 0         # decode-sized M is not stacked
+    assert L.qlora_group_fwd_workspace(M, K, N, 0, r) == 0
+    assert L.qlora_group_fwd_workspace(M, K, N, 17, r) == 0
+    assert L.qlora_group_bwd_workspace(M, K, N, 3, 65) == 0
+    ws = L.qlora_group_fwd_workspace(M, K, N, 3, r)
+    fwd = lambda X=A, G=3, ws_b=ws, Y=A: L.qlora_group_fwd(X, M, K, N, G, A, A, A, A, A, r, 1.0, Y, None, A, ws_b,
+                                                           None)
+    assert fwd(X=None) == -1
+    assert fwd(G=0) == -2
+    assert fwd(Y=MIS) == -4
+    assert fwd(ws_b=ws - 1) == -5
+    wb = L.qlora_group_bwd_workspace(M, K, N, 3, r)
+    assert wb >= ws
+    bwd = lambda dL2=A, ws_b=wb: L.qlora_group_bwd(A, A, M, K, N, 3, A, A, A, A, A, r, 1.0, None, None, A, dL2,
+                                                   A, ws_b, None)
+    assert bwd(dL2=None) == -1
+    assert bwd(ws_b=wb - 256) == -5
+    ad = lambda p=A, n=100, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, step=1, pb=None: L.qlora_adamw_step(
+        p, A, A, A, pb, n, lr, b1, b2, eps, wd, step, None)
+    assert ad(p=None) == -1
+    assert ad(n=0) == -2
+    assert ad(step=0) == -2
+    assert ad(lr=-1.0) == -7
+    assert ad(b1=1.0) == -7
+    assert ad(b2=-0.1) == -7
+    assert ad(eps=0.0) == -7
+    assert ad(wd=-0.5) == -7
+    assert ad(lr=float("nan")) == -7
+    assert ad(p=MIS) == -4
+    assert ad(pb=MIS) == -4

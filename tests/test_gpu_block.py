@@ -1,0 +1,195 @@
+"""GPU tests of the block pipeline: stacked linears (q|k|v, gate|up) against
+the separate layers (bit for bit where the pages' formula makes them the same
+computation) and against the oracle; the adapter-only AdamW step against the
+float64 oracle; and one small Transformer block's adapters trained one step
+both ways."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from gpu_util import assert_close, bits, f32np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+B = O.block
+
+
+def qlib():
+    import bit_quantized_lora_blockwise_amd as q
+    return q
+
+
+def _segments(G, N, K, r, seed):
+    Ws = [WL.weight_gaussian(N, K, 0.02, seed + 10 * g) for g in range(G)]
+    L1 = torch.stack([WL.normal((K, r), 1.0 / K, seed + 10 * g + 1) for g in range(G)])
+    L2 = torch.stack([WL.normal((r, N), 0.3, seed + 10 * g + 2) for g in range(G)])
+    return Ws, L1, L2
+
+
+@pytest.mark.parametrize("M,K,N,G,r", [(128, 512, 256, 3, 16), (200, 768, 512, 2, 64), (40, 256, 256, 3, 5)])
+def test_stacked_equals_separate_and_oracle(M, K, N, G, r):
+    q = qlib()
+    s = 2.0
+    seed = M * 7 + K + N + G * 13 + r
+    print(f"[group] M={M} K={K} N={N} G={G} r={r}", flush=True)
+    Ws, L1, L2 = _segments(G, N, K, r, seed)
+    X = WL.normal((M, K), 1.0, seed + 100).to(DEV)
+    dY = WL.normal((M, G * N), 1.0, seed + 101).to(DEV)
+    L1d, L2d = L1.to(DEV), L2.to(DEV)
+    # the stack quantized as one equals the separate quantizations (N K / 64 is a multiple of 256)
+    codes, absmax = q.nf4_quantize(torch.cat(Ws).to(DEV))
+    c2, c1 = q.nf4_double_quant(absmax)
+    sep = []
+    for g in range(G):
+        cg, ag = q.nf4_quantize(Ws[g].to(DEV))
+        c2g, c1g = q.nf4_double_quant(ag)
+        sep.append((cg, c2g, c1g))
+    assert torch.equal(codes, torch.cat([x[0] for x in sep]))
+    assert torch.equal(c2, torch.cat([x[1] for x in sep]))
+    assert torch.equal(c1.view(torch.int32), torch.cat([x[2] for x in sep]).view(torch.int32))
+
+    Y, T = q.qlora_group_fwd(X, codes, c2, c1, N, G, L1d, L2d, s, T_out=True)
+    dX, dL1, dL2 = q.qlora_group_bwd(X, dY, codes, c2, c1, G, L1d, L2d, s, T=T)
+    dX_sep = torch.zeros((M, K), dtype=torch.float32, device=DEV)
+    for g in range(G):
+        Yg, Tg = q.qlora_linear_fwd(X, *sep[g], N, L1d[g], L2d[g], s, T_out=True)
+        dYg = dY[:, g * N:(g + 1) * N].contiguous()
+        dXg, dL1g, dL2g = q.qlora_linear_bwd(X, dYg, *sep[g], L1d[g], L2d[g], s, T=Tg)
+        torch.cuda.synchronize()
+        assert torch.equal(Y[:, g * N:(g + 1) * N].view(torch.int16), Yg.view(torch.int16)), g
+        assert torch.equal(T[g].view(torch.int16), Tg.view(torch.int16)), g
+        assert torch.equal(dL1[g].view(torch.int32), dL1g.view(torch.int32)), g
+        assert torch.equal(dL2[g].view(torch.int32), dL2g.view(torch.int32)), g
+        dX_sep += dXg.float()
+    rel = ((dX.float() - dX_sep).norm() / dX_sep.norm()).item()
+    print(f"[group] dX against the sum of the separate layers' dX: rel_l2 {rel:.2e}", flush=True)
+    assert rel < 8e-3
+
+    Wq = []
+    for g in range(G):                      # the oracle quantizes the weights itself
+        rc, ra = O.nf4_quantize(Ws[g].float().numpy())
+        rc2, rc1 = O.nf4_double_quant(ra)
+        Wq.append(O.nf4_dequantize(rc, rc2, rc1, N, K))
+    L1b = [bits(L1[g]) for g in range(G)]
+    L2b = [bits(L2[g]) for g in range(G)]
+    rY, rT = B.qlora_group_forward(bits(X), Wq, L1b, L2b, s)
+    rdX, rdL1, rdL2, _ = B.qlora_group_backward(bits(X), bits(dY), Wq, L1b, L2b, s, T_list=rT)
+    assert_close(bits(Y), rY, "stacked Y")
+    assert_close(bits(dX), rdX, "stacked dX")
+    for g in range(G):
+        assert_close(f32np(dL1[g]), rdL1[g], f"stacked dL1[{g}]")
+        assert_close(f32np(dL2[g]), rdL2[g], f"stacked dL2[{g}]")
+
+
+@pytest.mark.parametrize("n", [4096 * 33, 1001])
+def test_adamw_against_oracle(n):
+    q = qlib()
+    rng = np.random.default_rng(n)
+    theta0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    p = torch.from_numpy(theta0.copy()).to(DEV)
+    m = torch.zeros(n, device=DEV)
+    v = torch.zeros(n, device=DEV)
+    pb = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    rt, rm, rv = theta0.astype(np.float64), np.zeros(n), np.zeros(n)
+    hp = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    for step in range(1, 6):
+        g = (rng.standard_normal(n) * 0.05 / step).astype(np.float32)
+        q.qlora_adamw_step(p, m, v, torch.from_numpy(g).to(DEV), step, param_bf16=pb, **hp)
+        f = {k: float(np.float32(x)) for k, x in hp.items()}   # the fp32 values the call passes
+        rt, rm, rv = B.adamw_step(rt, rm, rv, g, f["lr"], f["beta1"], f["beta2"], f["eps"], f["weight_decay"],
+                                  step)
+    torch.cuda.synchronize()
+    gp, gm, gv = (t.cpu().numpy().astype(np.float64) for t in (p, m, v))
+    d_rel = np.linalg.norm((gp - theta0) - (rt - theta0)) / np.linalg.norm(rt - theta0)
+    m_rel = np.linalg.norm(gm - rm) / np.linalg.norm(rm)
+    v_rel = np.linalg.norm(gv - rv) / np.linalg.norm(rv)
+    print(f"[adamw] n={n}: update rel {d_rel:.2e}, m rel {m_rel:.2e}, v rel {v_rel:.2e}", flush=True)
+    assert d_rel < 1e-4 and m_rel < 1e-5 and v_rel < 1e-5
+    assert np.array_equal(bits(pb), O.bf16_bits(p.cpu().numpy()))   # the bf16 copy is bf16(master)
+
+
+def _block(hidden, ffn, r, seed):
+    """A small Transformer block's 7 linears: name -> (N, K)."""
+    shapes = {"q": (hidden, hidden), "k": (hidden, hidden), "v": (hidden, hidden), "o": (hidden, hidden),
+              "gate": (ffn, hidden), "up": (ffn, hidden), "down": (hidden, ffn)}
+    lin = {}
+    for i, (name, (N, K)) in enumerate(shapes.items()):
+        base = seed + 10 * i
+        lin[name] = (WL.weight_row_std(N, K, 0.01, 0.05, base), WL.normal((K, r), 1.0 / K, base + 1),
+                     WL.normal((r, N), 0.01, base + 2))
+    return lin
+
+
+def test_block_step_stacked_equals_separate():
+    """One training step of a block's adapters (forward, backward, AdamW over
+    one flat adapter buffer): the stacked pipeline (q|k|v, o, gate|up, down)
+    and the seven separate layers produce the same adapter gradients and the
+    same updated adapters, bit for bit."""
+    q = qlib()
+    hidden, ffn, r, M, s = 256, 768, 16, 96, 1.0
+    lin = _block(hidden, ffn, r, 900)
+    groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    X = {grp: WL.normal((M, lin[grp[0]][0].shape[1]), 1.0, 950 + i).to(DEV) for i, grp in enumerate(groups)}
+    dY = {grp: WL.normal((M, sum(lin[n][0].shape[0] for n in grp)), 0.01, 960 + i).to(DEV)
+          for i, grp in enumerate(groups)}
+    # flat adapter storage: L1 then L2 of each linear, in block order
+    sizes = {n: (lin[n][1].numel(), lin[n][2].numel()) for n in lin}
+    total = sum(a + b for a, b in sizes.values())
+    outs = {}
+    for mode in ("stacked", "separate"):
+        master = torch.empty(total, device=DEV)
+        off, views = 0, {}
+        for n in lin:
+            a, b = sizes[n]
+            master[off:off + a] = lin[n][1].float().flatten().to(DEV)
+            master[off + a:off + a + b] = lin[n][2].float().flatten().to(DEV)
+            views[n] = (off, a, b)
+            off += a + b
+        pb = master.to(torch.bfloat16)
+        grad = torch.empty(total, device=DEV)
+        m = torch.zeros(total, device=DEV)
+        v = torch.zeros(total, device=DEV)
+
+        def L1(n):
+            o, a, _ = views[n]
+            return pb[o:o + a].view(lin[n][1].shape)
+
+        def L2(n):
+            o, a, b = views[n]
+            return pb[o + a:o + a + b].view(lin[n][2].shape)
+
+        for grp in groups:
+            Ws = [lin[n][0] for n in grp]
+            N, K = Ws[0].shape
+            codes, absmax = q.nf4_quantize(torch.cat(Ws).to(DEV))
+            c2, c1 = q.nf4_double_quant(absmax)
+            if mode == "stacked":
+                G = len(grp)
+                L1s = torch.stack([L1(n) for n in grp])
+                L2s = torch.stack([L2(n) for n in grp])
+                Y, T = q.qlora_group_fwd(X[grp], codes, c2, c1, N, G, L1s, L2s, s, T_out=True)
+                _, dL1, dL2 = q.qlora_group_bwd(X[grp], dY[grp], codes, c2, c1, G, L1s, L2s, s, T=T)
+                for g, n in enumerate(grp):
+                    o, a, b = views[n]
+                    grad[o:o + a] = dL1[g].flatten()
+                    grad[o + a:o + a + b] = dL2[g].flatten()
+            else:
+                nb = N * K // 64
+                for g, n in enumerate(grp):
+                    cg = codes[g * N:(g + 1) * N]
+                    c2g = c2[g * nb:(g + 1) * nb]
+                    c1g = c1[g * nb // 256:(g + 1) * nb // 256]
+                    Yg, Tg = q.qlora_linear_fwd(X[grp], cg, c2g, c1g, N, L1(n), L2(n), s, T_out=True)
+                    dYg = dY[grp][:, g * N:(g + 1) * N].contiguous()
+                    o, a, b = views[n]
+                    q.qlora_linear_bwd(X[grp], dYg, cg, c2g, c1g, L1(n), L2(n), s, T=Tg, dX=False,
+                                       dL1=grad[o:o + a].view(lin[n][1].shape),
+                                       dL2=grad[o + a:o + a + b].view(lin[n][2].shape))
+        q.qlora_adamw_step(master, m, v, grad, 1, 1e-3, weight_decay=0.01, param_bf16=pb)
+        torch.cuda.synchronize()
+        outs[mode] = (grad.clone(), master.clone(), pb.clone())
+    assert torch.equal(outs["stacked"][0].view(torch.int32), outs["separate"][0].view(torch.int32))
+    assert torch.equal(outs["stacked"][1].view(torch.int32), outs["separate"][1].view(torch.int32))
+    assert torch.equal(outs["stacked"][2].view(torch.int16), outs["separate"][2].view(torch.int16))
