@@ -363,6 +363,133 @@ def quant_study(dev, n=4096, reps=10):
     return out
 
 
+BLOCK_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+
+class BlockPipe:
+    """One LLaMA-65B Transformer block's seven quantized LoRA linears at M tokens,
+    trained one step: forward and backward of every linear, then one AdamW step
+    over all adapters held in one flat buffer.  stacked=True runs q|k|v and
+    gate|up as stacked matrices (4 layer calls), False the seven separate layers.
+    The packed bases are built once (the base is frozen); everything the timed
+    step touches is allocated here."""
+
+    def __init__(self, dev, M, stacked, r=64):
+        import torch
+        import bit_quantized_lora_blockwise_amd as q
+        import workloads as WL
+        self.q, self.stacked, self.M, self.r = q, stacked, M, r
+        f32, bf, u8 = torch.float32, torch.bfloat16, torch.uint8
+        self.groups = []
+        sizes = 0
+        for gi, grp in enumerate(BLOCK_GROUPS):
+            N, K = WL.LLAMA65B_BLOCK[grp[0]]
+            G = len(grp)
+            sizes += G * (K * r + r * N)
+        self.master = torch.empty(sizes, dtype=f32, device=dev)
+        self.grad = torch.zeros(sizes, dtype=f32, device=dev)
+        self.m = torch.zeros(sizes, dtype=f32, device=dev)
+        self.v = torch.zeros(sizes, dtype=f32, device=dev)
+        self.pb = torch.empty(sizes, dtype=bf, device=dev)
+        off = 0
+        for gi, grp in enumerate(BLOCK_GROUPS):
+            N, K = WL.LLAMA65B_BLOCK[grp[0]]
+            G = len(grp)
+            Ws, L1s, L2s = [], [], []
+            for name in grp:
+                i = list(WL.LLAMA65B_BLOCK).index(name)
+                base = 100 * (i + 1)
+                Ws.append(WL.weight_row_std(N, K, 0.01, 0.05, base, torch.bfloat16, dev))
+                L1s.append(WL.normal((K, r), 1.0 / K, base + 1, device=dev))
+                L2s.append(WL.normal((r, N), 0.01, base + 2, device=dev))
+            codes, absmax = q.nf4_quantize(torch.cat(Ws))
+            c2, c1 = q.nf4_double_quant(absmax)
+            del Ws, absmax
+            a, b = G * K * r, G * r * N
+            self.master[off:off + a] = torch.stack(L1s).float().flatten()
+            self.master[off + a:off + a + b] = torch.stack(L2s).float().flatten()
+            gr = {"names": grp, "N": N, "K": K, "G": G, "codes": codes, "c2": c2, "c1": c1,
+                  "L1": self.pb[off:off + a].view(G, K, r), "L2": self.pb[off + a:off + a + b].view(G, r, N),
+                  "dL1": self.grad[off:off + a].view(G, K, r), "dL2": self.grad[off + a:off + a + b].view(G, r, N),
+                  "X": WL.normal((M, K), 1.0, 1000 + gi, device=dev)}
+            off += a + b
+            dY = WL.normal((M, G * N), 1e-2, 1100 + gi, device=dev)
+            nb = N * K // 64
+            if stacked:
+                gr["dY"] = dY
+                gr["Y"] = torch.empty((M, G * N), dtype=bf, device=dev)
+                gr["T"] = torch.empty((G, M, r), dtype=bf, device=dev)
+                gr["dX"] = torch.empty((M, K), dtype=bf, device=dev)
+                gr["ws_f"] = torch.empty(max(16, q.lib().qlora_group_fwd_workspace(M, K, N, G, r)), dtype=u8,
+                                         device=dev)
+                gr["ws_b"] = torch.empty(max(16, q.lib().qlora_group_bwd_workspace(M, K, N, G, r)), dtype=u8,
+                                         device=dev)
+            else:
+                gr["seg"] = []
+                for g in range(G):
+                    gr["seg"].append({
+                        "codes": codes[g * N:(g + 1) * N], "c2": c2[g * nb:(g + 1) * nb],
+                        "c1": c1[g * nb // 256:(g + 1) * nb // 256], "dY": dY[:, g * N:(g + 1) * N].contiguous(),
+                        "Y": torch.empty((M, N), dtype=bf, device=dev), "T": torch.empty((M, r), dtype=bf, device=dev),
+                        "dX": torch.empty((M, K), dtype=bf, device=dev)})
+                gr["ws_f"] = torch.empty(max(16, q.qlora_linear_fwd_workspace(M, K, N, r)), dtype=u8, device=dev)
+                gr["ws_b"] = torch.empty(max(16, q.qlora_linear_bwd_workspace(M, K, N, r)), dtype=u8, device=dev)
+                del dY
+            self.groups.append(gr)
+        self.pb.copy_(self.master)
+        self.n_adapter = sizes
+        self.t = 0
+
+    def fwd_bwd(self):
+        q = self.q
+        for gr in self.groups:
+            if self.stacked:
+                q.qlora_group_fwd(gr["X"], gr["codes"], gr["c2"], gr["c1"], gr["N"], gr["G"], gr["L1"], gr["L2"],
+                                  1.0, Y=gr["Y"], T_out=gr["T"], workspace=gr["ws_f"])
+                q.qlora_group_bwd(gr["X"], gr["dY"], gr["codes"], gr["c2"], gr["c1"], gr["G"], gr["L1"], gr["L2"],
+                                  1.0, T=gr["T"], dX=gr["dX"], dL1=gr["dL1"], dL2=gr["dL2"], workspace=gr["ws_b"])
+            else:
+                for g, sg in enumerate(gr["seg"]):
+                    q.qlora_linear_fwd(gr["X"], sg["codes"], sg["c2"], sg["c1"], gr["N"], gr["L1"][g], gr["L2"][g],
+                                       1.0, Y=sg["Y"], T_out=sg["T"], workspace=gr["ws_f"])
+                    q.qlora_linear_bwd(gr["X"], sg["dY"], sg["codes"], sg["c2"], sg["c1"], gr["L1"][g],
+                                       gr["L2"][g], 1.0, T=sg["T"], dX=sg["dX"], dL1=gr["dL1"][g],
+                                       dL2=gr["dL2"][g], workspace=gr["ws_b"])
+
+    def optimizer(self):
+        self.t += 1
+        self.q.qlora_adamw_step(self.master, self.m, self.v, self.grad, self.t, 1e-4, weight_decay=0.0,
+                                param_bf16=self.pb)
+
+    def step(self):
+        self.fwd_bwd()
+        self.optimizer()
+
+
+def block_bench(dev, reps=5, M=2048):
+    """LLaMA-65B block (7 linears, r = 64, M = 2048 tokens): fwd + bwd of every
+    linear and one AdamW step over all adapters, stacked and separate."""
+    import torch
+    import workloads as WL
+    flops = sum(layer_flops(M, K, N, 64) for N, K in WL.LLAMA65B_BLOCK.values())
+    out = {"workload": "llama65b block: q,k,v,o 8192x8192, gate,up 8192->22016, down 22016->8192, r=64, M=2048",
+           "flops_per_step": flops}
+    for stacked in (True, False):
+        pipe = BlockPipe(dev, M, stacked)
+        key = "stacked" if stacked else "separate"
+        ms = time_launches(pipe.step, reps)
+        ms_fb = time_launches(pipe.fwd_bwd, reps)
+        ms_opt = time_launches(pipe.optimizer, reps)
+        out[key] = {"step_ms": round(ms, 4), "fwd_bwd_ms": round(ms_fb, 4), "adamw_ms": round(ms_opt, 4),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "adamw_gbps": round(pipe.n_adapter * 30 / (ms_opt * 1e-3) / 1e9, 1)}
+        out["adapter_params"] = pipe.n_adapter
+        del pipe
+        torch.cuda.empty_cache()
+    out["frac_of_bf16_peak"] = round(out["stacked"]["tflops"] / PEAK_BF16_TFLOPS, 4)
+    return out
+
+
 def cpu_baseline():
     """The CPU oracle on a bounded sample of the headline step: the whole
     up-projection half of it (4096 -> 11008, r = 64, M = 4096 tokens) -- encode,
@@ -485,6 +612,7 @@ def main():
     enc = encode_bench(dev)
     mrg = merge_bench(dev)
     study = quant_study(dev)
+    blk = block_bench(dev)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -504,6 +632,7 @@ def main():
         "encode": enc,
         "merge": mrg,
         "quant_study": study,
+        "block": blk,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
