@@ -47,11 +47,14 @@ struct Tile {
 
 // Tile at `base` (its element (0, 0)) of a matrix with `ld` elements per row;
 // rows at or past `rows` and columns at or past `cols` read as zero.  With
-// `vec` (ld and cols multiples of 8) each thread issues two 16-byte buffer
-// loads; otherwise it reads element by element.  `bytes`: extent of the
-// matrix from `base`.
+// kVec (ld and cols multiples of 8, base 16-byte aligned) each thread issues
+// two 16-byte buffer loads with no branch, so that the loads of later steps
+// stay in flight; otherwise it reads element by element.  `bytes`: extent of
+// the matrix from `base`.
+template <bool kVec>
 __device__ __forceinline__ Tile load_tile(const uint16_t* base, int64_t ld, int64_t rows, int64_t cols,
-                                          uint64_t bytes, bool vec) {
+                                          uint64_t bytes) {
+  constexpr bool vec = kVec;
   const int t = threadIdx.x;
   const int cc = (t & 7) * 8;
   Tile tl;
@@ -81,11 +84,10 @@ __device__ __forceinline__ void store_tile(const Tile& tl, LDS_AS uint16_t* dst)
 
 // C[M, r] partial over one reduction slice: A [M, R] (row stride lda) times B, where
 // B(k, c) = Bm[k * r + c] (kBkr, L1 [R, r]) or Bm[c * R + k] (!kBkr, L2 [r, R]).
-template <bool kBkr>
+template <bool kBkr, bool kVecA, bool kVecB>
 __global__ __launch_bounds__(kThreads) void k_lora_skinny(const uint16_t* __restrict__ A, int64_t M, int64_t R,
                                                           int64_t lda, const uint16_t* __restrict__ Bm, int r,
-                                                          int64_t chunk,
-                                                          float* __restrict__ part, int avec, int bvec) {
+                                                          int64_t chunk, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * kPitch];
   const int w = threadIdx.x >> 6;
@@ -99,9 +101,9 @@ __global__ __launch_bounds__(kThreads) void k_lora_skinny(const uint16_t* __rest
     const int64_t k0 = k_beg + st * kTile;
     const int64_t kl = k_end - k0;                     // columns of the slice left (<= 0: zeros)
     const int64_t k0c = kl > 0 ? k0 : 0;
-    ta = load_tile(A + m0 * lda + k0c, lda, M - m0, kl, (uint64_t)((M - m0) * lda - k0c) * 2, avec);
-    if (kBkr) tb = load_tile(Bm + k0c * r, r, kl, r, (uint64_t)((R - k0c) * r) * 2, bvec);
-    else tb = load_tile(Bm + k0c, R, r, kl, (uint64_t)(r * R - k0c) * 2, bvec);
+    ta = load_tile<kVecA>(A + m0 * lda + k0c, lda, M - m0, kl, (uint64_t)((M - m0) * lda - k0c) * 2);
+    if (kBkr) tb = load_tile<kVecB>(Bm + k0c * r, r, kl, r, (uint64_t)((R - k0c) * r) * 2);
+    else tb = load_tile<kVecB>(Bm + k0c, R, r, kl, (uint64_t)(r * R - k0c) * 2);
   };
   f32x16 acc = {};
   auto step = [&](int64_t st, const Tile& na, const Tile& nb, Tile& la, Tile& lb) {
@@ -151,10 +153,10 @@ __global__ __launch_bounds__(kThreads) void k_skinny_reduce(const float* __restr
 }
 
 // C[p, c] partial over one slice of m: sum_m A[m][p] * B[m][c], A [M, P], B [M, r].
+template <bool kVecA, bool kVecB>
 __global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict__ A, int64_t lda,
                                                       const uint16_t* __restrict__ B, int64_t M, int64_t P, int r,
-                                                      int64_t chunk,
-                                                      float* __restrict__ part, int avec, int bvec) {
+                                                      int64_t chunk, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * kPitch];
   const int w = threadIdx.x >> 6;
@@ -168,8 +170,8 @@ __global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict
     const int64_t mm = m_beg + st * kTile;
     const int64_t ml = m_end - mm;                     // rows of the slice left (<= 0: zeros)
     const int64_t mmc = ml > 0 ? mm : 0;
-    ta = load_tile(A + mmc * lda + p0, lda, ml, P - p0, (uint64_t)((M - mmc) * lda - p0) * 2, avec);   // [m][p]
-    tb = load_tile(B + mmc * r, r, ml, r, (uint64_t)((M - mmc) * r) * 2, bvec);                // [m][c]
+    ta = load_tile<kVecA>(A + mmc * lda + p0, lda, ml, P - p0, (uint64_t)((M - mmc) * lda - p0) * 2);   // [m][p]
+    tb = load_tile<kVecB>(B + mmc * r, r, ml, r, (uint64_t)((M - mmc) * r) * 2);                // [m][c]
   };
   f32x16 acc = {};
   auto step = [&](int64_t st, const Tile& na, const Tile& nb, Tile& la, Tile& lb) {
@@ -256,14 +258,22 @@ hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t l
   const int64_t tiles = (M + kTile - 1) / kTile;
   const SplitPlan sp = plan_rowsplit(tiles, R);
   dim3 grid((unsigned)tiles, (unsigned)sp.splits);
-  const int avec = (R % 8) == 0 && (lda % 8) == 0 && ((uintptr_t)A & 15) == 0;
-  const int bvec = b_is_kr ? (r % 8) == 0 : (R % 8) == 0;
-  if (b_is_kr)
-    hipLaunchKernelGGL(k_lora_skinny<true>, grid, dim3(kThreads), 0, s, A, M, R, lda, B, r, sp.chunk, ws, avec,
-                       bvec);
-  else
-    hipLaunchKernelGGL(k_lora_skinny<false>, grid, dim3(kThreads), 0, s, A, M, R, lda, B, r, sp.chunk, ws, avec,
-                       bvec);
+  const bool avec = (R % 8) == 0 && (lda % 8) == 0 && ((uintptr_t)A & 15) == 0;
+  const bool bvec = (b_is_kr ? (r % 8) == 0 : (R % 8) == 0) && ((uintptr_t)B & 15) == 0;
+#define QL_SKINNY(BKR, VA, VB)                                                                                \
+  hipLaunchKernelGGL((k_lora_skinny<BKR, VA, VB>), grid, dim3(kThreads), 0, s, A, M, R, lda, B, r, sp.chunk, ws)
+  if (b_is_kr) {
+    if (avec && bvec) QL_SKINNY(true, true, true);
+    else if (avec) QL_SKINNY(true, true, false);
+    else if (bvec) QL_SKINNY(true, false, true);
+    else QL_SKINNY(true, false, false);
+  } else {
+    if (avec && bvec) QL_SKINNY(false, true, true);
+    else if (avec) QL_SKINNY(false, true, false);
+    else if (bvec) QL_SKINNY(false, false, true);
+    else QL_SKINNY(false, false, false);
+  }
+#undef QL_SKINNY
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_skinny_reduce, dim3(grid_for(M * r)), dim3(kThreads), 0, s, ws, sp.splits, M * (int64_t)r,
@@ -281,9 +291,15 @@ hipError_t launch_lora_tn(const uint16_t* A, int64_t lda, const uint16_t* B, int
   const int64_t tiles = (P + kTile - 1) / kTile;
   const SplitPlan sp = plan_rowsplit(tiles, M);
   dim3 grid((unsigned)tiles, (unsigned)sp.splits);
-  const int avec = (P % 8) == 0 && (lda % 8) == 0 && ((uintptr_t)A & 15) == 0;
-  hipLaunchKernelGGL(k_lora_tn, grid, dim3(kThreads), 0, s, A, lda, B, M, P, r, sp.chunk, ws, avec,
-                     (int)((r % 8) == 0));
+  const bool avec = (P % 8) == 0 && (lda % 8) == 0 && ((uintptr_t)A & 15) == 0;
+  const bool bvec = (r % 8) == 0 && ((uintptr_t)B & 15) == 0;
+#define QL_TN(VA, VB) \
+  hipLaunchKernelGGL((k_lora_tn<VA, VB>), grid, dim3(kThreads), 0, s, A, lda, B, M, P, r, sp.chunk, ws)
+  if (avec && bvec) QL_TN(true, true);
+  else if (avec) QL_TN(true, false);
+  else if (bvec) QL_TN(false, true);
+  else QL_TN(false, false);
+#undef QL_TN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_tn_reduce, dim3(grid_for(P * r)), dim3(kThreads), 0, s, ws, sp.splits, P, r, scale,
