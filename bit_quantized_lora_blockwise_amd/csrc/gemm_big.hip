@@ -136,7 +136,11 @@ __device__ __forceinline__ bf16x8 frag_planes(const LDS_AS uint8_t* base, int k0
   const int l = threadIdx.x & 63;
   const int g = l >> 4, i = l & 15;
   const int row = 2 * (k0 + 8 * (g >> 1)) + (i >> 1);
-  const LDS_AS uint8_t* p = base + row * kPlane + col0 + 16 * (g & 1) + 8 * (i & 1);
+  // 8-byte chunk c of each 32-byte column group of weight row k is stored at
+  // chunk c ^ (k % 4) (k % 4 = (i / 4) % 4 here), which keeps the writes of the
+  // dequantisation free of bank conflicts
+  const int chunk = (2 * (g & 1) + (i & 1)) ^ ((i >> 2) & 3);
+  const LDS_AS uint8_t* p = base + row * kPlane + col0 + 8 * chunk;
   typedef int v2i __attribute__((ext_vector_type(2)));
   const v2i a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)p);
   const v2i b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 8 * kPlane));
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     if (kDx) {
       u32x2 lo8, hi8;
       dequant8_planes(L, c, lo8, hi8);
-      LDS_AS uint8_t* d = (LDS_AS uint8_t*)buf + dq_off + 8 * q;
+      LDS_AS uint8_t* d = (LDS_AS uint8_t*)buf + dq_off + 8 * (q ^ ((t >> 3) & 3));   // chunk swizzle, see frag_planes
       *(LDS_AS u32x2*)d = lo8;
       *(LDS_AS u32x2*)(d + kPlane) = hi8;
     } else {
