@@ -10,7 +10,7 @@
 // turn; in a step, lane (g = l / 16, row = l % 16) holds one block (64 weights,
 // 32 bytes of codes): it builds the block's 16-entry bf16 table in registers
 // (two byte planes) and looks each nibble up with v_perm_b32.
-// When X is small (M * K <= 8192) it is staged once in LDS, with each group of
+// When X is small (M * K <= 16384) it is staged once in LDS, with each group of
 // eight columns stored in the order (0, 2, 4, 6, 1, 3, 5, 7): that is the order
 // in which the lookups produce the weights (low nibbles, then high nibbles), so
 // the MFMA needs no re-interleaving of the looked-up values.  The staging is
@@ -24,7 +24,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = 16;                 // weight rows (output columns) per work group
 constexpr int kChunk = 4;                 // steps of a lane whose loads are issued together
-constexpr int kXBytes = 16384;            // LDS budget for X: M * K <= 8192
+constexpr int kXBytes = 32768;            // LDS budget for X: M * K <= 16384
 constexpr int kZeroBytes = 128;           // zeros read in place of X by idle lanes
 constexpr int kRedBytes = kWaves * 64 * 16;
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset past every range: the load returns 0
