@@ -4,7 +4,7 @@ kernels behind the C ABI in include/qlora.h.  This package is the thin ctypes
 binding; torch provides device memory and streams only."""
 from ._lib import (  # noqa: F401
     QloraError, lib, EXPORTS,
-    nf4_quantize, nf4_double_quant, nf4_dequantize,
+    nf4_quantize, nf4_quantize_dq, nf4_double_quant, nf4_dequantize,
     qlora_linear_fwd_workspace, qlora_linear_fwd,
     qlora_linear_bwd_workspace, qlora_linear_bwd,
     qlora_nf4_levels, ql_status_string,

@@ -21,7 +21,7 @@ CODEBOOKS = {"nf4": 0, "fp4": 1, "int4": 2}
 SCALE_CODES = {"groupmax": 0, "fullrange": 1, "mean": 2, "absmax": 3}
 STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_DTYPE", -4: "QL_ERR_ALIGN",
           -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_HIP", -7: "QL_ERR_VALUE"}
-EXPORTS = ("nf4_quantize", "nf4_double_quant", "nf4_dequantize", "qlora_linear_fwd_workspace",
+EXPORTS = ("nf4_quantize", "nf4_quantize_dq", "nf4_double_quant", "nf4_dequantize", "qlora_linear_fwd_workspace",
            "qlora_linear_fwd", "qlora_linear_bwd_workspace", "qlora_linear_bwd", "qlora_nf4_levels",
            "ql_status_string", "qlora_lora_down_workspace", "qlora_lora_down", "qlora_linear_fwd_t",
            "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx", "qlora_merge",
@@ -49,6 +49,7 @@ def lib():
             "nf4_quantize": ([P, I32, I64, I64, P, P, P], I32),
             "nf4_double_quant": ([P, I64, P, P, P], I32),
             "nf4_dequantize": ([P, P, P, I64, I64, P, P], I32),
+            "nf4_quantize_dq": ([P, I32, I64, I64, P, P, P, P, P], I32),
             "qlora_linear_fwd_workspace": ([I64, I64, I64, I32], SZ),
             "qlora_linear_fwd": ([P, I64, I64, I64, P, P, P, P, P, I32, F32, P, P, P, SZ, P], I32),
             "qlora_linear_bwd_workspace": ([I64, I64, I64, I32], SZ),
@@ -123,6 +124,26 @@ def nf4_quantize(W, codes=None, absmax=None, stream=None):
     _check("nf4_quantize", lib().nf4_quantize(_ptr(W), QL_BF16 if W.dtype == torch.bfloat16 else QL_F32, rows, cols,
                                               _ptr(codes), _ptr(absmax), _stream(stream)))
     return codes, absmax
+
+
+def nf4_quantize_dq(W, codes=None, c2=None, c1=None, absmax=None, stream=None):
+    """Codes, c2 and c1 of W [rows, cols] in one pass (absmax written too when given a buffer or True)."""
+    if W.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("W must be float32 or bfloat16")
+    _need(W, "W", W.dtype, 2)
+    rows, cols = W.shape
+    nb = rows * cols // 64
+    codes = _empty((rows, cols // 2), torch.uint8, W) if codes is None else _need(codes, "codes", torch.uint8)
+    c2 = _empty((nb,), torch.uint8, W) if c2 is None else _need(c2, "c2", torch.uint8)
+    c1 = _empty(((nb + 255) // 256,), torch.float32, W) if c1 is None else _need(c1, "c1", torch.float32)
+    if absmax is True:
+        absmax = _empty((nb,), torch.float32, W)
+    elif absmax is not None:
+        _need(absmax, "absmax", torch.float32)
+    _check("nf4_quantize_dq", lib().nf4_quantize_dq(_ptr(W), QL_BF16 if W.dtype == torch.bfloat16 else QL_F32, rows,
+                                                    cols, _ptr(codes), _ptr(absmax), _ptr(c2), _ptr(c1),
+                                                    _stream(stream)))
+    return codes, c2, c1, absmax
 
 
 def nf4_double_quant(absmax, c2=None, c1=None, stream=None):

@@ -120,6 +120,17 @@ int nf4_quantize(const void* W, int w_dtype, int64_t rows, int64_t cols, uint8_t
   return QL_OK;
 }
 
+int nf4_quantize_dq(const void* W, int w_dtype, int64_t rows, int64_t cols, uint8_t* codes, float* absmax,
+                    uint8_t* c2, float* c1, void* stream) {
+  if (!W || !codes || !c2 || !c1) return QL_ERR_NULL;
+  if (w_dtype != QL_F32 && w_dtype != QL_BF16) return QL_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || cols % 64 != 0 || rows > (int64_t(1) << 40) / cols) return QL_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(c2) || !aligned16(c1) || (absmax && !aligned16(absmax)))
+    return QL_ERR_ALIGN;
+  QL_TRY(launch_nf4_encode_dq(W, w_dtype == QL_BF16, rows * cols, codes, absmax, c2, c1, (hipStream_t)stream));
+  return QL_OK;
+}
+
 int nf4_double_quant(const float* absmax, int64_t n_blocks, uint8_t* c2, float* c1, void* stream) {
   if (!absmax || !c2 || !c1) return QL_ERR_NULL;
   if (n_blocks <= 0 || n_blocks > (int64_t(1) << 36)) return QL_ERR_SHAPE;

@@ -23,6 +23,83 @@ constexpr int kThreads = 256;
 // all weights of blocks whose absmax is not a normal number -- are redone
 // with the correctly rounded division, so the codes are exactly those of the
 // definition.
+// The eight weights of a thread -> eight packed codes; `a` returns the block's
+// absmax (shared by the 8 lanes of an aligned group through DPP, so all eight
+// lanes of a block must be active together).  tab: the bucket table in LDS.
+__device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t* tab, uint32_t tab_base,
+                                            float& a_out) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(w[j]) & 0x7FFFFFFFu);
+  m = qk::dpp_max8(m);
+  const float a = __uint_as_float(m);
+  // 16 / a for a normal absmax; an all-zero block gives n' = 0 (codes 7)
+  const bool a_normal = m >= 0x00800000u;
+  const float y16 = a_normal ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
+  uint32_t packed = 0, redo = (m != 0 && !a_normal) ? 0xFFu : 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float n16 = w[j] * y16;
+    const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);   // bucket (clamped: non-finite input)
+    const uint32_t addr = tab_base + 8u * (uint32_t)bi;
+    const float t16 = __uint_as_float(*(const LDS_AS uint32_t*)(uintptr_t)addr);
+    const uint32_t mb = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
+    const uint32_t c = (mb & 15u) + (n16 >= t16 ? 1u : 0u);
+    redo |= (__builtin_fabsf(n16 - t16) <= __uint_as_float(mb) ? 1u : 0u) << j;
+    packed |= c << (4 * j);
+  }
+  if (redo) {
+    // correctly rounded quotient for the undecided weights
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((redo >> j) & 1u) {
+        const float n = (m == 0) ? 0.0f : w[j] / a;
+        const float n16 = 16.0f * n;                            // exact
+        const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);
+        const float t16 = __uint_as_float(tab[2 * bi]);
+        const uint32_t c = (tab[2 * bi + 1] & 15u) + (n16 >= t16 ? 1u : 0u);
+        packed = (packed & ~(15u << (4 * j))) | (c << (4 * j));
+      }
+    }
+  }
+  a_out = a;
+  return packed;
+}
+
+struct RawOct {
+  u32x4 v0, v1;
+};
+
+template <bool kBf16>
+__device__ __forceinline__ RawOct load_oct(const void* __restrict__ W, int64_t o) {
+  RawOct r;
+  if (kBf16) {
+    r.v0 = __builtin_nontemporal_load((const u32x4*)W + o);
+    r.v1 = u32x4{0, 0, 0, 0};
+  } else {
+    r.v0 = __builtin_nontemporal_load((const u32x4*)W + 2 * o);
+    r.v1 = __builtin_nontemporal_load((const u32x4*)W + 2 * o + 1);
+  }
+  return r;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void unpack_oct(const RawOct& r, float (&w)[8]) {
+  if (kBf16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = __uint_as_float(r.v0[j] << 16);
+      w[2 * j + 1] = __uint_as_float(r.v0[j] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = __uint_as_float(r.v0[j]);
+      w[4 + j] = __uint_as_float(r.v1[j]);
+    }
+  }
+}
+
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict__ W, int64_t n_oct,
                                                          uint32_t* __restrict__ codes,
@@ -37,58 +114,74 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict_
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t o = (int64_t)blockIdx.x * kThreads + threadIdx.x; o < n_oct; o += stride) {
     float w[8];
-    if (kBf16) {
-      u32x4 v = __builtin_nontemporal_load((const u32x4*)W + o);
+    unpack_oct<kBf16>(load_oct<kBf16>(W, o), w);
+    float a;
+    codes[o] = encode8(w, tab, tab_base, a);
+    if ((threadIdx.x & 7) == 0) absmax[o >> 3] = a;
+  }
+}
+
+// Encoder and double quantization in one pass: a work group owns whole groups
+// of 256 blocks (2048 octets, eight per thread, all requested up front); the
+// group's max is reduced across the work group and every block's scale code
+// follows at once.  Results equal those of k_nf4_encode then k_double_quant.
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restrict__ W, int64_t n_oct,
+                                                            uint32_t* __restrict__ codes,
+                                                            float* __restrict__ absmax, uint8_t* __restrict__ c2,
+                                                            float* __restrict__ c1, int64_t ngroups,
+                                                            Nf4Buckets bk) {
+  __shared__ __attribute__((aligned(8))) uint32_t tab[34 * 2];
+  __shared__ uint32_t red[kThreads / 64];
+  if (threadIdx.x < 34) {
+    tab[2 * threadIdx.x] = __float_as_uint(bk.t16[threadIdx.x]);
+    tab[2 * threadIdx.x + 1] = bk.mb[threadIdx.x];
+  }
+  __syncthreads();
+  const uint32_t tab_base = (uint32_t)(uintptr_t)(LDS_AS uint32_t*)tab;
+  const int t = threadIdx.x;
+  constexpr int kIt = qk::kGroup * 8 / kThreads;    // octets per thread per group (8)
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    const int64_t o0 = g * qk::kGroup * 8 + t;
+    RawOct raw[kIt];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[2 * j] = __uint_as_float(v[j] << 16);
-        w[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
-      }
-    } else {
-      u32x4 v0 = __builtin_nontemporal_load((const u32x4*)W + 2 * o);
-      u32x4 v1 = __builtin_nontemporal_load((const u32x4*)W + 2 * o + 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[j] = __uint_as_float(v0[j]);
-        w[4 + j] = __uint_as_float(v1[j]);
-      }
+    for (int it = 0; it < kIt; ++it) {
+      const int64_t o = o0 + (int64_t)it * kThreads;
+      raw[it] = load_oct<kBf16>(W, o < n_oct ? o : 0);
     }
+    float a[kIt];
     uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(w[j]) & 0x7FFFFFFFu);
-    m = qk::dpp_max8(m);
-    const float a = __uint_as_float(m);
-    // 16 / a for a normal absmax; an all-zero block gives n' = 0 (codes 7)
-    const bool a_normal = m >= 0x00800000u;
-    const float y16 = a_normal ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
-    uint32_t packed = 0, redo = (m != 0 && !a_normal) ? 0xFFu : 0u;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float n16 = w[j] * y16;
-      const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);   // bucket (clamped: non-finite input)
-      const uint32_t addr = tab_base + 8u * (uint32_t)bi;
-      const float t16 = __uint_as_float(*(const LDS_AS uint32_t*)(uintptr_t)addr);
-      const uint32_t mb = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
-      const uint32_t c = (mb & 15u) + (n16 >= t16 ? 1u : 0u);
-      redo |= (__builtin_fabsf(n16 - t16) <= __uint_as_float(mb) ? 1u : 0u) << j;
-      packed |= c << (4 * j);
+    for (int it = 0; it < kIt; ++it) {
+      const int64_t o = o0 + (int64_t)it * kThreads;
+      a[it] = 0.0f;
+      if (o < n_oct) {                                // whole blocks (8 lanes) are in or out together
+        float w[8];
+        unpack_oct<kBf16>(raw[it], w);
+        codes[o] = encode8(w, tab, tab_base, a[it]);
+      }
+      m = max(m, __float_as_uint(a[it]));
     }
-    if (redo) {
-      // correctly rounded quotient for the undecided weights
+    m = qk::wave_max_u32(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    uint32_t gm = red[0];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if ((redo >> j) & 1u) {
-          const float n = (m == 0) ? 0.0f : w[j] / a;
-          const float n16 = 16.0f * n;                            // exact
-          const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);
-          const float t16 = __uint_as_float(tab[2 * bi]);
-          const uint32_t c = (tab[2 * bi + 1] & 15u) + (n16 >= t16 ? 1u : 0u);
-          packed = (packed & ~(15u << (4 * j))) | (c << (4 * j));
+    for (int i = 1; i < kThreads / 64; ++i) gm = max(gm, red[i]);
+    __syncthreads();                                  // red is reused by the next group
+    const float cmax = __uint_as_float(gm);
+    if ((t & 7) == 0) {
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int64_t o = o0 + (int64_t)it * kThreads;
+        if (o < n_oct) {
+          const int64_t b = o >> 3;
+          c2[b] = (uint8_t)qk::e4m3fn_encode(gm == 0 ? 0.0f : a[it] / cmax);
+          if (absmax) absmax[b] = a[it];
         }
       }
     }
-    codes[o] = packed;
-    if ((threadIdx.x & 7) == 0) absmax[o >> 3] = a;
+    if (t == 0) c1[g] = cmax;
   }
 }
 
@@ -186,5 +279,21 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* 
   const int grid = grid_for(n_oct, kThreads);
   hipLaunchKernelGGL(k_dequant, dim3(grid), dim3(kThreads), 0, s, (const uint32_t*)codes, c2, c1, n_oct,
                      (u32x4*)out, nf4_params());
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_encode_dq(const void* W, bool bf16, int64_t elems, uint8_t* codes, float* absmax, uint8_t* c2,
+                                float* c1, hipStream_t s) {
+  const int64_t n_oct = elems / 8;
+  const int64_t nblocks = elems / qk::kBlock;
+  const int64_t ngroups = (nblocks + qk::kGroup - 1) / qk::kGroup;
+  if (!nf4_buckets().ok) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(ngroups < 65536 ? ngroups : 65536);
+  if (bf16)
+    hipLaunchKernelGGL(k_nf4_encode_dq<true>, dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes, absmax,
+                       c2, c1, ngroups, nf4_buckets());
+  else
+    hipLaunchKernelGGL(k_nf4_encode_dq<false>, dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes, absmax,
+                       c2, c1, ngroups, nf4_buckets());
   return hipGetLastError();
 }

@@ -18,6 +18,9 @@ const Nf4Params* codebook_params(int codebook);
 hipError_t launch_nf4_encode(const void* W, bool bf16, int64_t elems, uint8_t* codes, float* absmax,
                              hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t n_blocks, uint8_t* c2, float* c1, hipStream_t s);
+// Both in one pass (absmax optional: may be null).
+hipError_t launch_nf4_encode_dq(const void* W, bool bf16, int64_t elems, uint8_t* codes, float* absmax, uint8_t* c2,
+                                float* c1, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t elems,
                           uint16_t* out, hipStream_t s);
 

@@ -90,6 +90,13 @@ int nf4_quantize(const void* W, int w_dtype, int64_t rows, int64_t cols,
 int nf4_double_quant(const float* absmax, int64_t n_blocks,
                      uint8_t* c2, float* c1, void* stream);
 
+/* nf4_quantize followed by nf4_double_quant in one pass over W (same
+ * passages): codes [rows, cols/2], c2 [n_blocks], c1 [ceil(n_blocks / 256)],
+ * bit-identical to the two calls; absmax [n_blocks] is written too when
+ * non-NULL. Errors as nf4_quantize.                                             */
+int nf4_quantize_dq(const void* W, int w_dtype, int64_t rows, int64_t cols,
+                    uint8_t* codes, float* absmax, uint8_t* c2, float* c1, void* stream);
+
 /* doubleDequant(c1, c2, W_NF4) written out as bf16 (nlp-lineage page, notation
  * paragraph): s'_b = fl32(dec(c2[b]) * c1[b / 256]); W'[e] = bf16(fl32(q[code_e] * s'_b)),
  * both roundings to nearest-even. Output W_bf16 [rows, cols]. This is the exact

@@ -207,3 +207,12 @@ def test_group_and_adamw_validation():
     assert ad(lr=float("nan")) == -7
     assert ad(p=MIS) == -4
     assert ad(pb=MIS) == -4
+
+
+def test_fused_quantize_validation():
+    _, L = _lib()
+    assert L.nf4_quantize_dq(None, 0, 4, 64, A, A, A, A, None) == -1
+    assert L.nf4_quantize_dq(A, 0, 4, 64, A, None, None, A, None) == -1
+    assert L.nf4_quantize_dq(A, 5, 4, 64, A, None, A, A, None) == -3
+    assert L.nf4_quantize_dq(A, 1, 4, 96, A, None, A, A, None) == -2
+    assert L.nf4_quantize_dq(A, 1, 4, 64, A, MIS, A, A, None) == -4

@@ -170,3 +170,33 @@ def test_nearest_code_sweep():
     r_codes, r_absmax = O.nf4_quantize(W)
     assert_bitexact(absmax.cpu().numpy().view(np.uint32), r_absmax.view(np.uint32), "sweep absmax")
     assert_bitexact(codes.cpu().numpy(), r_codes, "sweep codes")
+
+
+@pytest.mark.parametrize("rows,cols,dtype", [(512, 512, "fp32"), (11008, 4096, "bf16"), (3, 320, "fp32"),
+                                             (257, 64, "bf16"), (5, 64 * 51, "bf16")])
+def test_fused_quantize_and_double_quant(rows, cols, dtype):
+    """nf4_quantize_dq equals nf4_quantize followed by nf4_double_quant, bit for
+    bit (and so the oracle), including partial last groups."""
+    import bit_quantized_lora_blockwise_amd as q
+    W = WL.normal((rows, cols), 0.02, rows * 31 + cols, torch.float32)
+    W[0, :64] = 0.0                                           # an all-zero block
+    if dtype == "bf16":
+        W = W.to(torch.bfloat16)
+    Wd = W.to(DEV)
+    print(f"[fused encode] {rows}x{cols} {dtype}", flush=True)
+    codes, c2, c1, absmax = q.nf4_quantize_dq(Wd, absmax=True)
+    codes_s, absmax_s = q.nf4_quantize(Wd)
+    c2_s, c1_s = q.nf4_double_quant(absmax_s)
+    codes_n, c2_n, c1_n, _ = q.nf4_quantize_dq(Wd)            # without absmax
+    torch.cuda.synchronize()
+    assert torch.equal(codes, codes_s) and torch.equal(codes_n, codes_s)
+    assert torch.equal(absmax.view(torch.int32), absmax_s.view(torch.int32))
+    assert torch.equal(c2, c2_s) and torch.equal(c2_n, c2_s)
+    assert torch.equal(c1.view(torch.int32), c1_s.view(torch.int32)) and torch.equal(c1_n.view(torch.int32),
+                                                                                       c1_s.view(torch.int32))
+    if rows * cols <= 1 << 20:
+        rc, ra = O.nf4_quantize(W.float().numpy())
+        rc2, rc1 = O.nf4_double_quant(ra)
+        assert_bitexact(codes.cpu().numpy(), rc, "fused codes")
+        assert_bitexact(c2.cpu().numpy(), rc2, "fused c2")
+        assert_bitexact(c1.cpu().numpy().view(np.uint32), rc1.view(np.uint32), "fused c1")
