@@ -138,6 +138,33 @@ def time_launches(fn, reps):
     return a.elapsed_time(b) / reps
 
 
+def time_graph_launches(fn, calls, reps):
+    """Average duration (ms) of one `fn` call when `calls` calls are captured in
+    a HIP graph and the graph is replayed `reps` times (HIP events on the
+    current stream): back-to-back launches without the host in between."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / (reps * calls)
+
+
 def kernel_rooflines(lins, reps):
     """Fused forward GEMM and fused dX GEMM, each launched alone (stage entry points)."""
     q = lins[0].q
@@ -240,12 +267,17 @@ def decode_bench(dev, reps=200):
             it[0] += 1
             q.qlora_linear_fwd(X, cd, cc2, cc1, N, L1, L2, 1.0, Y=Y, T_out=T, workspace=ws)
 
-        kms = time_launches(kern, reps)
-        fms = time_launches(full, reps)
+        # launches replayed from a captured graph (the copies rotate inside it),
+        # and the same calls issued one by one from Python for comparison
+        kms = time_graph_launches(kern, copies * 2, max(4, reps // (copies * 2)))
+        fms = time_graph_launches(full, copies * 2, max(4, reps // (copies * 2)))
+        kms_eager = time_launches(kern, reps)
+        fms_eager = time_launches(full, reps)
         alg = packed + r * N * 2 + M * K * 2 + M * r * 2 + M * N * 2
         res[f"M{M}"] = {"kernel_us": kms * 1e3, "packed_gbps": packed / (kms * 1e-3) / 1e9,
                         "alg_gbps": alg / (kms * 1e-3) / 1e9, "full_call_us": fms * 1e3,
-                        "full_call_packed_gbps": packed / (fms * 1e-3) / 1e9}
+                        "full_call_packed_gbps": packed / (fms * 1e-3) / 1e9,
+                        "eager_kernel_us": kms_eager * 1e3, "eager_full_call_us": fms_eager * 1e3}
     res["packed_bytes"] = packed
     res["copies_rotated"] = copies
     del layers

@@ -6,28 +6,32 @@
 // Layer formula: nlp-lineage milestone page on QLoRA, "The idea", notation
 // paragraph; dequantisation on the fly: examadda page, "The Core Idea".
 //
-// Work group: 16 weight rows x all of K, four waves taking 256-column steps in
-// turn; in a step, lane (g = l / 16, row = l % 16) holds one block (64 weights,
-// 32 bytes of codes): it builds the block's 16-entry bf16 table in registers
-// (two byte planes) and looks each nibble up with v_perm_b32.
+// Work group: 16 weight rows x all of K, split over 8 waves (16 when the grid
+// has few work groups) that take 256-column steps in turn; in a step, lane
+// (g = l / 16, row = l % 16) holds one block (64 weights, 32 bytes of codes): it
+// builds the block's 16-entry bf16 table in registers (two byte planes) and
+// looks each nibble up with v_perm_b32.  Each wave keeps one step in flight
+// ahead of the one it converts: with many short waves per SIMD the memory
+// system returns data in the order it is consumed and the VALU work of one wave
+// overlaps the waits of the others (measured better than deeper prefetch in
+// fewer waves).  The partial sums of the waves are added in LDS.
 // When X is small (M * K <= 16384) it is staged once in LDS, with each group of
 // eight columns stored in the order (0, 2, 4, 6, 1, 3, 5, 7): that is the order
 // in which the lookups produce the weights (low nibbles, then high nibbles), so
 // the MFMA needs no re-interleaving of the looked-up values.  The staging is
 // finished before the code stream is requested, so the first steps do not wait
-// for X behind the stream.  Larger X is read per step from global memory.
+// for X behind the stream.  Larger X is read from global memory together with
+// the step's codes.
 #include "kernels.h"
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kRows = 16;                 // weight rows (output columns) per work group
-constexpr int kChunk = 4;                 // steps of a lane whose loads are issued together
 constexpr int kXBytes = 32768;            // LDS budget for X: M * K <= 16384
 constexpr int kZeroBytes = 128;           // zeros read in place of X by idle lanes
-constexpr int kRedBytes = kWaves * 64 * 16;
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset past every range: the load returns 0
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -35,6 +39,14 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, 0x00020000);
+}
+
+// (a & m) | o in one instruction; m and o are kept in VGPRs (a VOP3 encoding
+// takes no literal and at most one SGPR).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -56,69 +68,84 @@ __device__ __forceinline__ BlockLut make_lut(float s, const Nf4Params& p) {
   return L;
 }
 
-// 16-entry byte lookup of the four index bytes of x (values 0..15).
-__device__ __forceinline__ uint32_t lut16(const uint32_t (&T)[4], uint32_t x, uint32_t x7, uint32_t selc) {
-  const uint32_t a = __builtin_amdgcn_perm(T[1], T[0], x);    // entries 0..7 (bytes of x < 8 are right)
-  const uint32_t b = __builtin_amdgcn_perm(T[3], T[2], x7);   // entries 8..15
-  return __builtin_amdgcn_perm(b, a, selc);                   // byte i from b when x_i >= 8
-}
-
-// Eight nibbles (one 32-bit word, element j in bits 4j..4j+3) -> four packed
-// bf16 pairs in element order.
-__device__ __forceinline__ u32x4 dequant8(const BlockLut& L, uint32_t c) {
-  const uint32_t xe = c & 0x0F0F0F0Fu;             // elements 0, 2, 4, 6
-  const uint32_t xo = (c >> 4) & 0x0F0F0F0Fu;      // elements 1, 3, 5, 7
-  const uint32_t se = ((xe >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t so = ((xo >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t xe7 = xe & 0x07070707u, xo7 = xo & 0x07070707u;
-  const uint32_t le = lut16(L.lo, xe, xe7, se), he = lut16(L.hi, xe, xe7, se);
-  const uint32_t lo_ = lut16(L.lo, xo, xo7, so), ho = lut16(L.hi, xo, xo7, so);
-  const uint32_t e02 = __builtin_amdgcn_perm(he, le, 0x05010400u);   // [W'(e0), W'(e2)]
-  const uint32_t e46 = __builtin_amdgcn_perm(he, le, 0x07030602u);   // [W'(e4), W'(e6)]
-  const uint32_t o13 = __builtin_amdgcn_perm(ho, lo_, 0x05010400u);  // [W'(e1), W'(e3)]
-  const uint32_t o57 = __builtin_amdgcn_perm(ho, lo_, 0x07030602u);  // [W'(e5), W'(e7)]
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(o13, e02, 0x05040100u);   // e0, e1
-  r[1] = __builtin_amdgcn_perm(o13, e02, 0x07060302u);   // e2, e3
-  r[2] = __builtin_amdgcn_perm(o57, e46, 0x05040100u);   // e4, e5
-  r[3] = __builtin_amdgcn_perm(o57, e46, 0x07060302u);   // e6, e7
-  return r;
-}
-
-
-// Same lookup, weights in the order (0, 2, 4, 6, 1, 3, 5, 7) of the word.
-__device__ __forceinline__ u32x4 dequant8_eo(const BlockLut& L, uint32_t c) {
-  const uint32_t xe = c & 0x0F0F0F0Fu;
-  const uint32_t xo = (c >> 4) & 0x0F0F0F0Fu;
-  const uint32_t se = ((xe >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t so = ((xo >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t xe7 = xe & 0x07070707u, xo7 = xo & 0x07070707u;
-  const uint32_t le = lut16(L.lo, xe, xe7, se), he = lut16(L.hi, xe, xe7, se);
-  const uint32_t lo_ = lut16(L.lo, xo, xo7, so), ho = lut16(L.hi, xo, xo7, so);
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(he, le, 0x05010400u);    // W'(e0), W'(e2)
-  r[1] = __builtin_amdgcn_perm(he, le, 0x07030602u);    // W'(e4), W'(e6)
-  r[2] = __builtin_amdgcn_perm(ho, lo_, 0x05010400u);   // W'(e1), W'(e3)
-  r[3] = __builtin_amdgcn_perm(ho, lo_, 0x07030602u);   // W'(e5), W'(e7)
-  return r;
-}
-
-// Codes and scales of kChunk steps of one lane.
-struct Chunk {
-  u32x4 cw[kChunk][2];
-  uint32_t c2b[kChunk];
-  float c1v[kChunk];
+// Constants of the nibble split, held in VGPRs for v_and_or_b32.
+struct SplitConst {
+  uint32_t m4, b0;   // 0x04040404, 0x03020100
 };
 
+// 16-entry byte lookup of four 4-bit indices: x7 holds their low three bits,
+// sel = 0x03020100 + 4 * (bit 3 of each index) picks the entry 8..15 candidate.
+__device__ __forceinline__ uint32_t lut16(const uint32_t (&T)[4], uint32_t x7, uint32_t sel) {
+  const uint32_t a = __builtin_amdgcn_perm(T[1], T[0], x7);   // entries 0..7
+  const uint32_t b = __builtin_amdgcn_perm(T[3], T[2], x7);   // entries 8..15
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+
+// Eight nibbles of one 32-bit word (element j in bits 4j..4j+3) -> byte-plane
+// lookups of the even elements (le, he) and odd elements (lo, ho).
+struct Planes {
+  uint32_t le, he, lo, ho;
+};
+
+__device__ __forceinline__ Planes lookup8(const BlockLut& L, uint32_t c, const SplitConst& k) {
+  const uint32_t xe = c & 0x07070707u;               // elements 0, 2, 4, 6: low 3 bits
+  const uint32_t se = and_or(c >> 1, k.m4, k.b0);    //   and their bit 3 as a selector
+  const uint32_t xo = (c >> 4) & 0x07070707u;        // elements 1, 3, 5, 7
+  const uint32_t so = and_or(c >> 5, k.m4, k.b0);
+  Planes P;
+  P.le = lut16(L.lo, xe, se);
+  P.he = lut16(L.hi, xe, se);
+  P.lo = lut16(L.lo, xo, so);
+  P.ho = lut16(L.hi, xo, so);
+  return P;
+}
+
+// Weights in element order (bf16 pairs e0 e1, e2 e3, e4 e5, e6 e7).
+__device__ __forceinline__ u32x4 dequant8(const BlockLut& L, uint32_t c, const SplitConst& k) {
+  const Planes P = lookup8(L, c, k);
+  const uint32_t e02 = __builtin_amdgcn_perm(P.he, P.le, 0x05010400u);   // [W'(e0), W'(e2)]
+  const uint32_t e46 = __builtin_amdgcn_perm(P.he, P.le, 0x07030602u);   // [W'(e4), W'(e6)]
+  const uint32_t o13 = __builtin_amdgcn_perm(P.ho, P.lo, 0x05010400u);   // [W'(e1), W'(e3)]
+  const uint32_t o57 = __builtin_amdgcn_perm(P.ho, P.lo, 0x07030602u);   // [W'(e5), W'(e7)]
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(o13, e02, 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(o13, e02, 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(o57, e46, 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(o57, e46, 0x07060302u);
+  return r;
+}
+
+// Weights in the order (0, 2, 4, 6, 1, 3, 5, 7) of the word.
+__device__ __forceinline__ u32x4 dequant8_eo(const BlockLut& L, uint32_t c, const SplitConst& k) {
+  const Planes P = lookup8(L, c, k);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(P.he, P.le, 0x05010400u);   // W'(e0), W'(e2)
+  r[1] = __builtin_amdgcn_perm(P.he, P.le, 0x07030602u);   // W'(e4), W'(e6)
+  r[2] = __builtin_amdgcn_perm(P.ho, P.lo, 0x05010400u);   // W'(e1), W'(e3)
+  r[3] = __builtin_amdgcn_perm(P.ho, P.lo, 0x07030602u);   // W'(e5), W'(e7)
+  return r;
+}
+
+// Operands of one step of a lane: its block's codes and scales, and (when X is
+// not staged in LDS) the 64 matching columns of its row of X.
 template <bool kXLds>
-__global__ __launch_bounds__(kThreads) void k_qgemv_fwd(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+struct Step {
+  u32x4 cw[2];
+  uint32_t c2b;
+  float c1v;
+  u32x4 xa[kXLds ? 1 : 8];
+};
+
+template <bool kXLds, int kWv, int kXPer>
+__global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         int64_t N, int64_t ld, const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ c2,
                                                         const float* __restrict__ c1,
                                                         const uint16_t* __restrict__ T,
                                                         const uint16_t* __restrict__ L2, int r, float scale,
                                                         uint16_t* __restrict__ Y, Nf4Params p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[(kXLds ? kXBytes + kZeroBytes : 0) + kRedBytes];
+  constexpr int kThr = 64 * kWv;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[(kXLds ? kXBytes + kZeroBytes : 0) + kWv * 64 * 16];
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
   const int g = l >> 4, col = l & 15;
@@ -127,14 +154,17 @@ __global__ __launch_bounds__(kThreads) void k_qgemv_fwd(const uint16_t* __restri
   const bool row_ok = nrow < N;
   const bool m_ok = col < M;                       // A-operand row of this lane is X[col]
   const uint32_t kblocks = (uint32_t)(K / qk::kBlock);
+  SplitConst kc;
+  asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
+  asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
 
   // K is walked in steps of four blocks (256 columns); the waves take the steps
   // in turn, and in step s lane group g takes block 4 s + g, so the four lanes
-  // of a row read 128 contiguous bytes of codes.  Step i of wave w is s = w + 4 i.
+  // of a row read 128 contiguous bytes of codes.  Step i of wave w is s = w + kWv i.
   const uint32_t nsteps = (kblocks + 3) / 4;
-  const uint32_t nst = nsteps > (uint32_t)w ? (nsteps - (uint32_t)w + kWaves - 1) / kWaves : 0u;   // uniform
+  const uint32_t nst = nsteps > (uint32_t)w ? (nsteps - (uint32_t)w + kWv - 1) / kWv : 0u;   // uniform
   const uint32_t kb0 = 4u * (uint32_t)w + (uint32_t)g;
-  const uint32_t kbstep = 4u * kWaves;
+  const uint32_t kbstep = 4u * kWv;
   const uint32_t kb_lim = row_ok ? kblocks : 0u;   // blocks valid for the lane's weight row
 
   const __amdgpu_buffer_rsrc_t rc = rsrc(codes, (uint64_t)N * (K / 2));
@@ -142,68 +172,68 @@ __global__ __launch_bounds__(kThreads) void k_qgemv_fwd(const uint16_t* __restri
   const __amdgpu_buffer_rsrc_t r1 = rsrc(c1, 4 * (((uint64_t)N * kblocks + 255) / 256));
   const __amdgpu_buffer_rsrc_t rx = rsrc(X, (uint64_t)M * K * 2);
 
-  // ---- small X: its loads are issued first, then the first chunk of the code
+  // ---- small X: its loads are issued first, then the first step of the code
   // stream, then X is written to LDS (waiting for the X loads only).  Every
   // 16-byte group of eight columns is stored as (0, 2, 4, 6, 1, 3, 5, 7).
   LDS_AS uint8_t* xl = (LDS_AS uint8_t*)lds;
-  constexpr int kXPer = kXBytes / (16 * kThreads);       // 16-byte X loads per thread
   u32x4 xr[kXLds ? kXPer : 1];
   const uint32_t xbytes = kXLds ? (uint32_t)(M * K * 2) : 0u;
   if (kXLds) {
 #pragma unroll
     for (int j = 0; j < kXPer; ++j) {
-      const uint32_t o = 16u * (uint32_t)(t + j * kThreads);
+      const uint32_t o = 16u * (uint32_t)(t + j * kThr);
       xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, o < xbytes ? o : kOOB, 0, 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // ---- code stream: chunk c covers steps 4c .. 4c + 3 of the lane
   const uint32_t code_row = (uint32_t)(nrow * (K / 2));
   const uint32_t blk_row = (uint32_t)(nrow * kblocks);
-  auto load_chunk = [&](uint32_t i0, Chunk& ch) {
+  auto load_step = [&](uint32_t i, Step<kXLds>& st) {
+    const uint32_t kb = kb0 + i * kbstep;
+    const bool ok = kb < kb_lim;
+    const uint32_t co = ok ? code_row + 32u * kb : kOOB;
+    const uint32_t b = blk_row + kb;
+    st.cw[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
+    st.cw[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, co + 16, 0, 0);
+    st.c2b = __builtin_amdgcn_raw_buffer_load_b8(r2, ok ? b : kOOB, 0, 0);
+    st.c1v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ok ? 4 * (b >> 8) : kOOB, 0, 0));
+    if (!kXLds) {
+      const bool xok = m_ok && kb < kblocks;      // the lane's row of X (independent of its weight row)
+      const uint32_t xo = xok ? (uint32_t)((col * K) * 2) + 128u * kb : kOOB;
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      const uint32_t kb = kb0 + (i0 + i) * kbstep;
-      const bool ok = kb < kb_lim;
-      const uint32_t co = ok ? code_row + 32u * kb : kOOB;
-      const uint32_t b = blk_row + kb;
-      ch.cw[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
-      ch.cw[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rc, co + 16, 0, 0);
-      ch.c2b[i] = __builtin_amdgcn_raw_buffer_load_b8(r2, ok ? b : kOOB, 0, 0);
-      ch.c1v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ok ? 4 * (b >> 8) : kOOB, 0, 0));
+      for (int d = 0; d < 8; ++d) st.xa[d] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16 * d, 0, 0);
     }
   };
-  Chunk ca, cb;
-  load_chunk(0, ca);
+  Step<kXLds> sa, sb;
+  load_step(0, sa);                                // all-zero (out-of-range offsets) when the wave has no step
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- LoRA term operands, one 16x16x32 MFMA per wave: wave w covers ranks
-  // 16 w .. 16 w + 15 (lane groups 0 and 1; groups 2 and 3 contribute zeros).
-  u32x4 lt, ll;
+  // ---- LoRA term operands, one 16x16x16 MFMA per wave: wave w covers ranks
+  // 16 w .. 16 w + 15, lane group g ranks 16 w + 4 g .. + 3.
+  uint32_t ll[2], lt[2];
   {
     const __amdgpu_buffer_rsrc_t rl = rsrc(L2, 2 * ((uint64_t)(r - 1) * ld + N));
     const __amdgpu_buffer_rsrc_t rt = rsrc(T, 2 * (uint64_t)M * r);
-    const int rb = 16 * w + 8 * g;        // first rank of this lane's eight
-    uint32_t vl[8], vt[8];
+    const int rb = 16 * w + 4 * g;        // first rank of this lane's four
+    uint32_t vl[4], vt[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool rk = g < 2 && rb + j < r;
+    for (int j = 0; j < 4; ++j) {
+      const bool rk = rb + j < r;
       const uint32_t ol = (rk && row_ok) ? (uint32_t)(2 * ((int64_t)(rb + j) * ld + nrow)) : kOOB;
       const uint32_t ot = (rk && m_ok) ? (uint32_t)(2 * (col * r + rb + j)) : kOOB;
       vl[j] = __builtin_amdgcn_raw_buffer_load_b16(rl, ol, 0, 0);
       vt[j] = __builtin_amdgcn_raw_buffer_load_b16(rt, ot, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ll[j] = vl[2 * j] | (vl[2 * j + 1] << 16);
-      lt[j] = vt[2 * j] | (vt[2 * j + 1] << 16);
-    }
+    ll[0] = vl[0] | (vl[1] << 16);
+    ll[1] = vl[2] | (vl[3] << 16);
+    lt[0] = vt[0] | (vt[1] << 16);
+    lt[1] = vt[2] | (vt[3] << 16);
   }
 
   if (kXLds) {
 #pragma unroll
     for (int j = 0; j < kXPer; ++j) {
-      const uint32_t o = 16u * (uint32_t)(t + j * kThreads);
+      const uint32_t o = 16u * (uint32_t)(t + j * kThr);
       const u32x4 v = xr[j];
       u32x4 e;
       e[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
@@ -217,48 +247,41 @@ __global__ __launch_bounds__(kThreads) void k_qgemv_fwd(const uint16_t* __restri
   }
 
   f32x4 acc = {0, 0, 0, 0};
-  auto compute_chunk = [&](uint32_t i0, const Chunk& ch) {
+  auto compute_step = [&](uint32_t i, const Step<kXLds>& st) {
+    const uint32_t kb = kb0 + i * kbstep;
+    const BlockLut L = make_lut(qk::e4m3fn_to_f32(st.c2b) * st.c1v, p);
+    if (kXLds) {
+      // X'[col][64 kb .. +64] (eight 16-byte groups), zeros for idle lanes
+      const bool xok = m_ok && kb < kblocks;
+      const LDS_AS u32x4* xs =
+          (const LDS_AS u32x4*)(xl + (xok ? ((uint32_t)col * (uint32_t)K + 64u * kb) * 2u : (uint32_t)kXBytes));
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      if (i0 + i >= nst) break;                  // uniform
-      const uint32_t kb = kb0 + (i0 + i) * kbstep;
-      const bool xok = m_ok && kb < kblocks;      // the lane's row of X (independent of its weight row)
-      const BlockLut L = make_lut(qk::e4m3fn_to_f32(ch.c2b[i]) * ch.c1v[i], p);
-      if (kXLds) {
-        // X'[col][64 kb .. +64] (eight 16-byte groups), zeros for idle lanes
-        const LDS_AS u32x4* xs =
-            (const LDS_AS u32x4*)(xl + (xok ? ((uint32_t)col * (uint32_t)K + 64u * kb) * 2u : (uint32_t)kXBytes));
+      for (int d = 0; d < 8; ++d) {
+        const u32x4 bv = dequant8_eo(L, st.cw[d >> 2][d & 3], kc);
+        acc = mfma16(__builtin_bit_cast(bf16x8, xs[d]), __builtin_bit_cast(bf16x8, bv), acc);
+      }
+    } else {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const u32x4 bv = dequant8_eo(L, ch.cw[i][d >> 2][d & 3]);
-          acc = mfma16(__builtin_bit_cast(bf16x8, xs[d]), __builtin_bit_cast(bf16x8, bv), acc);
-        }
-      } else {
-        const uint32_t xo = xok ? (uint32_t)((col * K) * 2) + 128u * kb : kOOB;
-        u32x4 a[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) a[d] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16 * d, 0, 0);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const u32x4 bv = dequant8(L, ch.cw[i][d >> 2][d & 3]);
-          acc = mfma16(__builtin_bit_cast(bf16x8, a[d]), __builtin_bit_cast(bf16x8, bv), acc);
-        }
+      for (int d = 0; d < 8; ++d) {
+        const u32x4 bv = dequant8(L, st.cw[d >> 2][d & 3], kc);
+        acc = mfma16(__builtin_bit_cast(bf16x8, st.xa[d]), __builtin_bit_cast(bf16x8, bv), acc);
       }
     }
   };
-  // chunks in pairs: the loads of the next chunk are issued before the current
-  // one is converted
-  for (uint32_t i0 = 0; i0 < nst; i0 += 2 * kChunk) {
-    if (i0 + kChunk < nst) load_chunk(i0 + kChunk, cb);
-    compute_chunk(i0, ca);
-    if (i0 + kChunk >= nst) break;
-    if (i0 + 2 * kChunk < nst) load_chunk(i0 + 2 * kChunk, ca);
-    compute_chunk(i0 + kChunk, cb);
+  // steps in pairs: the next step's loads are issued before the current one is
+  // converted
+  for (uint32_t i = 0; i < nst; i += 2) {
+    if (i + 1 < nst) load_step(i + 1, sb);
+    compute_step(i, sa);
+    if (i + 1 >= nst) break;
+    if (i + 2 < nst) load_step(i + 2, sa);
+    compute_step(i + 1, sb);
   }
 
   {
     f32x4 zl = {0, 0, 0, 0};
-    zl = mfma16(__builtin_bit_cast(bf16x8, lt), __builtin_bit_cast(bf16x8, ll), zl);
+    zl = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{lt[0], lt[1]}),
+                                                   __builtin_bit_cast(s16x4, u32x2{ll[0], ll[1]}), zl, 0, 0, 0);
     acc += scale * zl;
   }
   f32x4* red = (f32x4*)(lds + (kXLds ? kXBytes + kZeroBytes : 0));
@@ -267,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_qgemv_fwd(const uint16_t* __restri
   if (w == 0) {
     f32x4 sum = red[l];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) sum += red[ww * 64 + l];
+    for (int ww = 1; ww < kWv; ++ww) sum += red[ww * 64 + l];
     // lane l holds C[m = 4g + i][n = col]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -275,6 +298,27 @@ __global__ __launch_bounds__(kThreads) void k_qgemv_fwd(const uint16_t* __restri
       if (m < M && row_ok) Y[(int64_t)m * ld + nrow] = qk::f32_to_bf16(sum[i]);
     }
   }
+}
+
+template <bool kXLds, int kWv, int kXPer>
+hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* X, int64_t M, int64_t K, int64_t rows, int64_t ld,
+                      const uint8_t* codes, const uint8_t* c2, const float* c1, const uint16_t* T,
+                      const uint16_t* L2, int r, float scale, uint16_t* Y) {
+  hipLaunchKernelGGL((k_qgemv_fwd<kXLds, kWv, kXPer>), grid, dim3(64 * kWv), 0, s, X, M, K, rows, ld, codes, c2, c1,
+                     T, L2, r, scale, Y, nf4_params());
+  return hipGetLastError();
+}
+
+// Small-X variant for kWv waves: the fewest X loads per thread (1, 2 or 4)
+// that cover M * K * 2 bytes.
+template <int kWv>
+hipError_t launch_lds(dim3 grid, hipStream_t s, const uint16_t* X, int64_t M, int64_t K, int64_t rows, int64_t ld,
+                      const uint8_t* codes, const uint8_t* c2, const float* c1, const uint16_t* T,
+                      const uint16_t* L2, int r, float scale, uint16_t* Y) {
+  const int64_t per = (M * K * 2 + 16 * 64 * kWv - 1) / (16 * 64 * kWv);
+  if (per <= 1) return launch_one<true, kWv, 1>(grid, s, X, M, K, rows, ld, codes, c2, c1, T, L2, r, scale, Y);
+  if (per <= 2) return launch_one<true, kWv, 2>(grid, s, X, M, K, rows, ld, codes, c2, c1, T, L2, r, scale, Y);
+  return launch_one<true, kWv, 4>(grid, s, X, M, K, rows, ld, codes, c2, c1, T, L2, r, scale, Y);
 }
 
 }  // namespace
@@ -293,14 +337,21 @@ hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, 
   const bool xlds = M * K * 2 <= kXBytes;
   for (int64_t r0 = 0; r0 < N; r0 += chunk) {
     const int64_t rows = N - r0 < chunk ? N - r0 : chunk;
-    dim3 grid((unsigned)((rows + kRows - 1) / kRows));
+    const int64_t wgs = (rows + kRows - 1) / kRows;
+    dim3 grid((unsigned)wgs);
+    // 16 waves per work group when the grid alone would leave SIMDs with fewer
+    // than two waves, else 8
+    const bool wide = wgs <= 384;
+    const uint8_t* cd = codes + r0 * (K / 2);
+    const uint8_t* cc2 = c2 + r0 * kblocks;
+    const float* cc1 = c1 + r0 * kblocks / 256;
+    hipError_t e;
     if (xlds)
-      hipLaunchKernelGGL(k_qgemv_fwd<true>, grid, dim3(kThreads), 0, s, X, M, K, rows, N, codes + r0 * (K / 2),
-                         c2 + r0 * kblocks, c1 + r0 * kblocks / 256, T, L2 + r0, r, scale, Y + r0, nf4_params());
+      e = wide ? launch_lds<16>(grid, s, X, M, K, rows, N, cd, cc2, cc1, T, L2 + r0, r, scale, Y + r0)
+               : launch_lds<8>(grid, s, X, M, K, rows, N, cd, cc2, cc1, T, L2 + r0, r, scale, Y + r0);
     else
-      hipLaunchKernelGGL(k_qgemv_fwd<false>, grid, dim3(kThreads), 0, s, X, M, K, rows, N, codes + r0 * (K / 2),
-                         c2 + r0 * kblocks, c1 + r0 * kblocks / 256, T, L2 + r0, r, scale, Y + r0, nf4_params());
-    hipError_t e = hipGetLastError();
+      e = wide ? launch_one<false, 16, 1>(grid, s, X, M, K, rows, N, cd, cc2, cc1, T, L2 + r0, r, scale, Y + r0)
+               : launch_one<false, 8, 1>(grid, s, X, M, K, rows, N, cd, cc2, cc1, T, L2 + r0, r, scale, Y + r0);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

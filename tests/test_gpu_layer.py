@@ -129,6 +129,68 @@ def test_decode_llama7b_up_full(M):
     assert_close(bits(Y), rY, f"decode M={M} Y")
 
 
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_llama7b_down_full(M):
+    """Decode-sized forward at the 11008 -> 4096 shape (few work groups, so the
+    kernel splits K over more waves; X staged in LDS at M = 1, read from global
+    memory above), every output compared."""
+    inp = WL.layer_inputs(4096, 11008, M, 64, seed_base=7100 + M)
+    print(f"[decode] M={M} K=11008 N=4096", flush=True)
+    q = qlib()
+    gq, rq = quantize_both(inp["W"])
+    X, L1, L2 = (inp[k].to(DEV) for k in ("X", "L1", "L2"))
+    Y, T = q.qlora_linear_fwd(X, *gq, 4096, L1, L2, 1.0, T_out=True)
+    torch.cuda.synchronize()
+    Wq = O.nf4_dequantize(*rq, 4096, 11008)
+    rY, rT = O.qlora_forward(bits(inp["X"]), Wq, bits(inp["L1"]), bits(inp["L2"]), 1.0)
+    assert_close(bits(T), rT, f"decode down M={M} T")
+    assert_close(bits(Y), rY, f"decode down M={M} Y")
+
+
+def test_decode_graph_replay_matches_eager():
+    """The decode forward captured in a HIP graph (as the decode timing runs it):
+    every replay, with eager work and synchronisations in between, gives the
+    eager call's Y and T bit for bit."""
+    q = qlib()
+    inp = WL.layer_inputs(4096, 2048, 4, 64, seed_base=4242)
+    gq, _ = quantize_both(inp["W"])
+    X, L1, L2 = (inp[k].to(DEV) for k in ("X", "L1", "L2"))
+    Y0, T0 = q.qlora_linear_fwd(X, *gq, 4096, L1, L2, 1.0, T_out=True)
+    Y = torch.empty_like(Y0)
+    T = torch.empty_like(T0)
+    ws = torch.empty((q.qlora_linear_fwd_workspace(4, 2048, 4096, 64),), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q.qlora_linear_fwd(X, *gq, 4096, L1, L2, 1.0, Y=Y, T_out=T, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.qlora_linear_fwd(X, *gq, 4096, L1, L2, 1.0, Y=Y, T_out=T, workspace=ws)
+    for rep in range(4):
+        Y.fill_(0)
+        T.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), Y0.view(torch.int16)), rep
+        assert torch.equal(T.view(torch.int16), T0.view(torch.int16)), rep
+        q.nf4_dequantize(*gq, 4096, 2048)                  # eager work between replays
+    del g
+
+
+# decode shapes whose step counts do not divide evenly over the waves: 8-wave
+# work groups (over 384 of them) and 16-wave ones, X in LDS and in global memory
+DECODE_SPLIT = [(3, 2880, 6200, 8), (2, 2368, 100, 64), (9, 4160, 6500, 16), (12, 1600, 40, 20)]
+
+
+@pytest.mark.parametrize("M,K,N,r", DECODE_SPLIT)
+def test_decode_uneven_wave_split(M, K, N, r):
+    inp = WL.layer_inputs(N, K, M, r, seed_base=M * 131 + K + N + r, l2_std=0.3)
+    full_case(inp, 1.25, "decode split")
+
+
 def _sampled_case(inp, name, n_rows=48, seed=0):
     """Full-size check: dL1, dL2 and T in full; Y and dX on sampled rows."""
     N, K = inp["W"].shape
