@@ -323,6 +323,13 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const u
   char* ws = (char*)workspace;
   uint16_t* T = T_out ? T_out : (uint16_t*)ws;
   float* part = (float*)(ws + w.t_bytes);
+  if (M <= 16 && (r % 4) == 0 && decode_t_ok(M, K, X, L1)) {
+    // decode: the slices of T = X L1, added and rounded inside the decode kernel
+    QL_TRY(launch_lora_part(X, M, K, L1, r, part, s));
+    QL_TRY(launch_qgemv_fwd_tpart(X, M, K, N, codes, c2, c1, part, decode_t_slices(K), T_out, L2, r, lora_scale, Y,
+                                  s));
+    return QL_OK;
+  }
   QL_TRY(launch_lora_skinny(X, M, K, K, L1, true, r, 1.0f, T, part, s));
   if (M <= 16)
     QL_TRY(launch_qgemv_fwd(X, M, K, N, codes, c2, c1, T, L2, r, lora_scale, Y, s));

@@ -136,12 +136,15 @@ struct Step {
   u32x4 xa[kXLds ? 1 : 8];
 };
 
-template <bool kXLds, int kWv, int kXPer>
+// kTPart: T is not given but formed here from the S fp32 slices Tp[s][m][c]
+// (added in order s = 0 .. S-1, rounded once), and written to T (if not null)
+// by work group 0.
+template <bool kXLds, int kWv, int kXPer, bool kTPart>
 __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         int64_t N, int64_t ld, const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ c2,
                                                         const float* __restrict__ c1,
-                                                        const uint16_t* __restrict__ T,
+                                                        uint16_t* __restrict__ T, const float* __restrict__ Tp, int S,
                                                         const uint16_t* __restrict__ L2, int r, float scale,
                                                         uint16_t* __restrict__ Y, Nf4Params p) {
   constexpr int kThr = 64 * kWv;
@@ -185,6 +188,19 @@ __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restri
       xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, o < xbytes ? o : kOOB, 0, 0);
     }
   }
+  // T slices (kTPart) next, ahead of the code stream, so that adding them waits
+  // for these loads and X only
+  const int rb = 16 * w + 4 * g;                   // first of this lane's four LoRA ranks
+  const bool t_ok = rb < r && m_ok;                // r % 4 == 0 with kTPart: the four ranks are all in or all out
+  f32x4 ps[kTPart ? kDecodeTSlices : 1];
+  if (kTPart) {
+    const __amdgpu_buffer_rsrc_t rp = rsrc(Tp, 4 * (uint64_t)S * M * r);
+#pragma unroll
+    for (int s = 0; s < kDecodeTSlices; ++s)
+      ps[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rp, (t_ok && s < S) ? (uint32_t)(4 * (((int64_t)s * M + col) * r + rb)) : kOOB,
+                                            0, 0));
+  }
   __builtin_amdgcn_sched_barrier(0);
   const uint32_t code_row = (uint32_t)(nrow * (K / 2));
   const uint32_t blk_row = (uint32_t)(nrow * kblocks);
@@ -214,18 +230,32 @@ __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restri
   {
     const __amdgpu_buffer_rsrc_t rl = rsrc(L2, 2 * ((uint64_t)(r - 1) * ld + N));
     const __amdgpu_buffer_rsrc_t rt = rsrc(T, 2 * (uint64_t)M * r);
-    const int rb = 16 * w + 4 * g;        // first rank of this lane's four
     uint32_t vl[4], vt[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool rk = rb + j < r;
       const uint32_t ol = (rk && row_ok) ? (uint32_t)(2 * ((int64_t)(rb + j) * ld + nrow)) : kOOB;
-      const uint32_t ot = (rk && m_ok) ? (uint32_t)(2 * (col * r + rb + j)) : kOOB;
       vl[j] = __builtin_amdgcn_raw_buffer_load_b16(rl, ol, 0, 0);
-      vt[j] = __builtin_amdgcn_raw_buffer_load_b16(rt, ot, 0, 0);
+      if (!kTPart) {
+        const uint32_t ot = (rk && m_ok) ? (uint32_t)(2 * (col * r + rb + j)) : kOOB;
+        vt[j] = __builtin_amdgcn_raw_buffer_load_b16(rt, ot, 0, 0);
+      }
     }
     ll[0] = vl[0] | (vl[1] << 16);
     ll[1] = vl[2] | (vl[3] << 16);
+    if (kTPart) {
+      // T[col][rb .. rb + 3]: the slices added in order s = 0 .. S-1, rounded once
+      f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < kDecodeTSlices; ++s)
+        if (s < S) sum += ps[s];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vt[j] = qk::f32_to_bf16(sum[j]);
+      if (T && blockIdx.x == 0 && t_ok) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) T[col * r + rb + j] = (uint16_t)vt[j];
+      }
+    }
     lt[0] = vt[0] | (vt[1] << 16);
     lt[1] = vt[2] | (vt[3] << 16);
   }
@@ -300,35 +330,45 @@ __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restri
   }
 }
 
-template <bool kXLds, int kWv, int kXPer>
-hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* X, int64_t M, int64_t K, int64_t rows, int64_t ld,
-                      const uint8_t* codes, const uint8_t* c2, const float* c1, const uint16_t* T,
-                      const uint16_t* L2, int r, float scale, uint16_t* Y) {
-  hipLaunchKernelGGL((k_qgemv_fwd<kXLds, kWv, kXPer>), grid, dim3(64 * kWv), 0, s, X, M, K, rows, ld, codes, c2, c1,
-                     T, L2, r, scale, Y, nf4_params());
+// One launch's operands besides the shape and the grid.
+struct QgemvArgs {
+  const uint16_t* X;
+  int64_t M, K, rows, ld;
+  const uint8_t* codes;
+  const uint8_t* c2;
+  const float* c1;
+  uint16_t* T;
+  const float* Tp;
+  int S;
+  const uint16_t* L2;
+  int r;
+  float scale;
+  uint16_t* Y;
+};
+
+template <bool kXLds, int kWv, int kXPer, bool kTPart>
+hipError_t launch_one(dim3 grid, hipStream_t s, const QgemvArgs& a) {
+  hipLaunchKernelGGL((k_qgemv_fwd<kXLds, kWv, kXPer, kTPart>), grid, dim3(64 * kWv), 0, s, a.X, a.M, a.K, a.rows,
+                     a.ld, a.codes, a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params());
   return hipGetLastError();
 }
 
 // Small-X variant for kWv waves: the fewest X loads per thread (1, 2 or 4)
 // that cover M * K * 2 bytes.
-template <int kWv>
-hipError_t launch_lds(dim3 grid, hipStream_t s, const uint16_t* X, int64_t M, int64_t K, int64_t rows, int64_t ld,
-                      const uint8_t* codes, const uint8_t* c2, const float* c1, const uint16_t* T,
-                      const uint16_t* L2, int r, float scale, uint16_t* Y) {
-  const int64_t per = (M * K * 2 + 16 * 64 * kWv - 1) / (16 * 64 * kWv);
-  if (per <= 1) return launch_one<true, kWv, 1>(grid, s, X, M, K, rows, ld, codes, c2, c1, T, L2, r, scale, Y);
-  if (per <= 2) return launch_one<true, kWv, 2>(grid, s, X, M, K, rows, ld, codes, c2, c1, T, L2, r, scale, Y);
-  return launch_one<true, kWv, 4>(grid, s, X, M, K, rows, ld, codes, c2, c1, T, L2, r, scale, Y);
+template <int kWv, bool kTPart>
+hipError_t launch_lds(dim3 grid, hipStream_t s, const QgemvArgs& a) {
+  const int64_t per = (a.M * a.K * 2 + 16 * 64 * kWv - 1) / (16 * 64 * kWv);
+  if (per <= 1) return launch_one<true, kWv, 1, kTPart>(grid, s, a);
+  if (per <= 2) return launch_one<true, kWv, 2, kTPart>(grid, s, a);
+  return launch_one<true, kWv, 4, kTPart>(grid, s, a);
 }
 
-}  // namespace
-
-hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
-                            const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
-                            float scale, uint16_t* Y, hipStream_t s) {
+template <bool kTPart>
+hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
   // Buffer offsets are 32-bit: split the rows into chunks whose packed codes stay
   // below 2^31 bytes; chunks start on multiples of 256 rows, so every chunk's
   // blocks start a new double-quantisation group.
+  const int64_t K = a0.K, M = a0.M;
   const int64_t kblocks = K / qk::kBlock;
   if (M * K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   int64_t chunk = ((int64_t(1) << 31) - (int64_t(1) << 20)) / (K / 2);
@@ -336,23 +376,43 @@ hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, 
   if (chunk < 256) return hipErrorInvalidValue;
   const bool xlds = M * K * 2 <= kXBytes;
   for (int64_t r0 = 0; r0 < N; r0 += chunk) {
-    const int64_t rows = N - r0 < chunk ? N - r0 : chunk;
-    const int64_t wgs = (rows + kRows - 1) / kRows;
+    QgemvArgs a = a0;
+    a.rows = N - r0 < chunk ? N - r0 : chunk;
+    a.ld = N;
+    a.codes = a0.codes + r0 * (K / 2);
+    a.c2 = a0.c2 + r0 * kblocks;
+    a.c1 = a0.c1 + r0 * kblocks / 256;
+    a.L2 = a0.L2 + r0;
+    a.Y = a0.Y + r0;
+    if (kTPart && r0 > 0) a.T = nullptr;           // the formed T is written by the first chunk's work group 0
+    const int64_t wgs = (a.rows + kRows - 1) / kRows;
     dim3 grid((unsigned)wgs);
     // 16 waves per work group when the grid alone would leave SIMDs with fewer
     // than two waves, else 8
     const bool wide = wgs <= 384;
-    const uint8_t* cd = codes + r0 * (K / 2);
-    const uint8_t* cc2 = c2 + r0 * kblocks;
-    const float* cc1 = c1 + r0 * kblocks / 256;
     hipError_t e;
     if (xlds)
-      e = wide ? launch_lds<16>(grid, s, X, M, K, rows, N, cd, cc2, cc1, T, L2 + r0, r, scale, Y + r0)
-               : launch_lds<8>(grid, s, X, M, K, rows, N, cd, cc2, cc1, T, L2 + r0, r, scale, Y + r0);
+      e = wide ? launch_lds<16, kTPart>(grid, s, a) : launch_lds<8, kTPart>(grid, s, a);
     else
-      e = wide ? launch_one<false, 16, 1>(grid, s, X, M, K, rows, N, cd, cc2, cc1, T, L2 + r0, r, scale, Y + r0)
-               : launch_one<false, 8, 1>(grid, s, X, M, K, rows, N, cd, cc2, cc1, T, L2 + r0, r, scale, Y + r0);
+      e = wide ? launch_one<false, 16, 1, kTPart>(grid, s, a) : launch_one<false, 8, 1, kTPart>(grid, s, a);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_qgemv_fwd_tpart(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                                  const uint8_t* c2, const float* c1, const float* Tpart, int S, uint16_t* T_out,
+                                  const uint16_t* L2, int r, float scale, uint16_t* Y, hipStream_t s) {
+  if (S < 1 || S > kDecodeTSlices || (r % 4) != 0 || ((uintptr_t)Tpart & 15) != 0) return hipErrorInvalidValue;
+  const QgemvArgs a{X, M, K, 0, N, codes, c2, c1, T_out, Tpart, S, L2, r, scale, Y};
+  return launch_shape<true>(a, N, s);
+}
+
+hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                            const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
+                            float scale, uint16_t* Y, hipStream_t s) {
+  const QgemvArgs a{X, M, K, 0, N, codes, c2, c1, const_cast<uint16_t*>(T), nullptr, 0, L2, r, scale, Y};
+  return launch_shape<false>(a, N, s);
 }

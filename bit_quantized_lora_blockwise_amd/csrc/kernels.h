@@ -49,6 +49,15 @@ SplitPlan plan_rowsplit(int64_t tiles, int64_t R);
 // true, L1 is [R, r]) or B(k, c) = L2[c][k] (false, L2 is [r, R]).  Result
 // scaled by `scale`, rounded to bf16 into out[M, r].  ws holds the fp32 partials.
 size_t lora_skinny_ws(int64_t M, int64_t R, int r);
+// Decode-sized T = X L1 (M <= 16, X rows 16-byte aligned, K % 64 == 0): fp32
+// partial sums part[s][m][c] over S = decode_t_slices(K) <= kDecodeTSlices
+// slices of the reduction.  launch_lora_skinny adds them in order s = 0..S-1 for
+// such shapes, and so does the decode kernel, so T is the same on every path.
+constexpr int kDecodeTSlices = 8;
+int decode_t_slices(int64_t K);
+bool decode_t_ok(int64_t M, int64_t K, const void* X, const void* L1);
+hipError_t launch_lora_part(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float* part,
+                            hipStream_t s);
 hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t lda, const uint16_t* B, bool b_is_kr,
                               int r, float scale, uint16_t* out, float* ws, hipStream_t s);
 
@@ -79,6 +88,12 @@ hipError_t launch_qgemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, 
 hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                             const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
                             float scale, uint16_t* Y, hipStream_t s);
+// Same, with T = bf16(sum over s of Tpart[s]) formed by the kernel from the S
+// fp32 slices of launch_lora_part (r % 4 == 0, Tpart 16-byte aligned); T_out
+// (optional) receives that T.
+hipError_t launch_qgemv_fwd_tpart(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                                  const uint8_t* c2, const float* c1, const float* Tpart, int S, uint16_t* T_out,
+                                  const uint16_t* L2, int r, float scale, uint16_t* Y, hipStream_t s);
 // Large-tile (256 x 256) versions of both GEMMs: dx = false computes the forward
 // (A = X, LA = T, LB = L2, C = Y), dx = true the dX product (A = dY, LA = G,
 // LB = L1, C = dX).  qgemm_big_ok says whether the shapes qualify.  nseg > 1:

@@ -12,6 +12,8 @@
 // order, so results are deterministic.  Within a slice the 64-wide steps are
 // pipelined: the tiles of step st + 2 are loaded into registers while step st
 // multiplies out of one LDS buffer and step st + 1's tiles go into the other.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace {
@@ -232,7 +234,109 @@ int grid_for(int64_t items) {
   return (int)(g < 1 ? 1 : (g > 4096 ? 4096 : g));
 }
 
+// ---------------------------------------------------------------------------
+// T = X L1 at decode-sized M (<= 16): fp32 partial sums over S slices of the
+// reduction, part[s][m][c], each slice covering all r columns so that every
+// 128-byte row of L1 is read by one work group.  Work group (b, s): columns
+// 16 b .. 16 b + 15 of slice s; its 16 waves take 32-row steps in turn with one
+// 16x16x32 MFMA each (lane (g, col): X row col, L1 column 16 b + col, rows
+// 8 g .. 8 g + 7 of the step) and add their results in LDS in a fixed order.
+// The slices are summed in order s = 0 .. S-1 by whoever needs T (the reduce
+// kernel below, or the decode kernel's prologue), so every path gets the same T.
+constexpr int kPartWaves = 16;
+constexpr int kPartCh = 4;
+
+__global__ __launch_bounds__(64 * kPartWaves) void k_lora_part(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                               const uint16_t* __restrict__ L1, int r, int64_t rows,
+                                                               float* __restrict__ part) {
+  __shared__ f32x4 red[kPartWaves * 64];
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int g = l >> 4, col = l & 15;
+  const int c = blockIdx.x * 16 + col;
+  const bool c_ok = c < r;
+  const bool m_ok = col < M;
+  const int64_t k_beg = (int64_t)blockIdx.y * rows;
+  const int64_t k_end = min(K, k_beg + rows);
+  const int64_t nk = k_end > k_beg ? (k_end - k_beg) / 32 : 0;      // rows and K are multiples of 32
+  const int64_t nst = nk > w ? (nk - w + kPartWaves - 1) / kPartWaves : 0;   // uniform
+  const __amdgpu_buffer_rsrc_t ra = rsrc(X, (uint64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(L1, (uint64_t)K * r * 2);
+
+  struct Op {
+    u32x4 a, b;
+  };
+  auto load = [&](int64_t i, Op& o) {
+    const int64_t k0 = k_beg + 32 * (w + i * kPartWaves) + 8 * g;
+    const bool ok = k0 < k_end;
+    o.a = __builtin_amdgcn_raw_buffer_load_b128(ra, (ok && m_ok) ? (uint32_t)((col * K + k0) * 2) : kOOB, 0, 0);
+    // eight 2-byte loads down column c: one base offset per lane (out of range
+    // for an idle lane, so every load returns 0), the row step as a uniform offset
+    const uint32_t bo = (ok && c_ok) ? (uint32_t)((k0 * r + c) * 2) : kOOB;
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, bo, 2 * r * j, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.b[j] = v[2 * j] | (v[2 * j + 1] << 16);
+  };
+  Op ca[kPartCh], cb[kPartCh];
+#pragma unroll
+  for (int j = 0; j < kPartCh; ++j) load(j, ca[j]);
+  f32x4 acc = {0, 0, 0, 0};
+  auto mul = [&](int64_t i0, const Op (&o)[kPartCh]) {
+#pragma unroll
+    for (int j = 0; j < kPartCh; ++j)
+      if (i0 + j < nst)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o[j].a),
+                                                       __builtin_bit_cast(bf16x8, o[j].b), acc, 0, 0, 0);
+  };
+  for (int64_t i0 = 0; i0 < nst; i0 += 2 * kPartCh) {
+    if (i0 + kPartCh < nst) {
+#pragma unroll
+      for (int j = 0; j < kPartCh; ++j) load(i0 + kPartCh + j, cb[j]);
+    }
+    mul(i0, ca);
+    if (i0 + kPartCh >= nst) break;
+    if (i0 + 2 * kPartCh < nst) {
+#pragma unroll
+      for (int j = 0; j < kPartCh; ++j) load(i0 + 2 * kPartCh + j, ca[j]);
+    }
+    mul(i0 + kPartCh, cb);
+  }
+  red[w * 64 + l] = acc;
+  __syncthreads();
+  if (w == 0) {
+    f32x4 sum = red[l];
+#pragma unroll
+    for (int ww = 1; ww < kPartWaves; ++ww) sum += red[ww * 64 + l];
+    // lane l holds C[m = 4 g + i][c]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (m < M && c_ok) part[((int64_t)blockIdx.y * M + m) * r + c] = sum[i];
+    }
+  }
+}
+
 }  // namespace
+
+int decode_t_slices(int64_t K) {
+  const int64_t s = K / 512;
+  return (int)(s < 1 ? 1 : (s > kDecodeTSlices ? kDecodeTSlices : s));
+}
+
+bool decode_t_ok(int64_t M, int64_t K, const void* X, const void* L1) {
+  return M >= 1 && M <= 16 && (K % 64) == 0 && ((uintptr_t)X & 15) == 0 && ((uintptr_t)L1 & 1) == 0;
+}
+
+hipError_t launch_lora_part(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float* part,
+                            hipStream_t s) {
+  const int S = decode_t_slices(K);
+  const int64_t rows = ((K + S - 1) / S + 31) / 32 * 32;
+  dim3 grid((unsigned)((r + 15) / 16), (unsigned)S);
+  hipLaunchKernelGGL(k_lora_part, grid, dim3(64 * kPartWaves), 0, s, X, M, K, L1, r, rows, part);
+  return hipGetLastError();
+}
 
 // Split of a reduction of length R over `tiles` output tiles: about 768 work
 // groups in all, but at most one slice per 512 of reduction, so that the fp32
@@ -250,11 +354,20 @@ SplitPlan plan_rowsplit(int64_t tiles, int64_t R) {
 
 size_t lora_skinny_ws(int64_t M, int64_t R, int r) {
   const SplitPlan sp = plan_rowsplit((M + kTile - 1) / kTile, R);
-  return (size_t)sp.splits * M * r * sizeof(float);
+  const int64_t splits = M <= 16 ? std::max<int64_t>(sp.splits, decode_t_slices(R)) : sp.splits;
+  return (size_t)splits * M * r * sizeof(float);
 }
 
 hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t lda, const uint16_t* B, bool b_is_kr,
                               int r, float scale, uint16_t* out, float* ws, hipStream_t s) {
+  if (b_is_kr && lda == R && decode_t_ok(M, R, A, B)) {
+    // decode-sized T: the slices the decode kernel also sums, added here in the same order
+    hipError_t e = launch_lora_part(A, M, R, B, r, ws, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_skinny_reduce, dim3(grid_for(M * r)), dim3(kThreads), 0, s, ws, decode_t_slices(R),
+                       M * (int64_t)r, scale, out);
+    return hipGetLastError();
+  }
   const int64_t tiles = (M + kTile - 1) / kTile;
   const SplitPlan sp = plan_rowsplit(tiles, R);
   dim3 grid((unsigned)tiles, (unsigned)sp.splits);
