@@ -81,23 +81,47 @@ __device__ __forceinline__ BlockLut make_lut(float s, const Nf4Params& p) {
   return L;
 }
 
-// 16-entry byte lookup of the four index bytes of x (values 0..15).
-__device__ __forceinline__ uint32_t lut16(const uint32_t (&T)[4], uint32_t x, uint32_t x7, uint32_t selc) {
-  const uint32_t a = __builtin_amdgcn_perm(T[1], T[0], x);    // entries 0..7 (bytes of x < 8 are right)
-  const uint32_t b = __builtin_amdgcn_perm(T[3], T[2], x7);   // entries 8..15
-  return __builtin_amdgcn_perm(b, a, selc);                   // byte i from b when x_i >= 8
+// (a & m) | o in one instruction; m and o are kept in VGPRs (a VOP3 encoding
+// takes no literal and at most one SGPR).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
 }
 
-// Eight nibbles (one 32-bit word, element j in bits 4j..4j+3) -> four packed
-// bf16 pairs in element order.
-__device__ __forceinline__ u32x4 dequant8(const BlockLut& L, uint32_t c) {
-  const uint32_t xe = c & 0x0F0F0F0Fu;             // elements 0, 2, 4, 6
-  const uint32_t xo = (c >> 4) & 0x0F0F0F0Fu;      // elements 1, 3, 5, 7
-  const uint32_t se = ((xe >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t so = ((xo >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t xe7 = xe & 0x07070707u, xo7 = xo & 0x07070707u;
-  const uint32_t le = lut16(L.lo, xe, xe7, se), he = lut16(L.hi, xe, xe7, se);
-  const uint32_t lo_ = lut16(L.lo, xo, xo7, so), ho = lut16(L.hi, xo, xo7, so);
+// Constants of the nibble split, held in VGPRs for v_and_or_b32.
+struct SplitConst {
+  uint32_t m4, b0;   // 0x04040404, 0x03020100
+};
+
+// 16-entry byte lookup of four 4-bit indices: x7 holds their low three bits,
+// sel = 0x03020100 + 4 * (bit 3 of each index) picks the entry 8..15 candidate.
+__device__ __forceinline__ uint32_t lut16(const uint32_t (&T)[4], uint32_t x7, uint32_t sel) {
+  const uint32_t a = __builtin_amdgcn_perm(T[1], T[0], x7);   // entries 0..7
+  const uint32_t b = __builtin_amdgcn_perm(T[3], T[2], x7);   // entries 8..15
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+
+// Eight nibbles of one 32-bit word (element j in bits 4j..4j+3): index bytes of
+// the even elements (xe, se) and the odd elements (xo, so).
+struct Split {
+  uint32_t xe, se, xo, so;
+};
+
+__device__ __forceinline__ Split split8(uint32_t c, const SplitConst& k) {
+  Split sp;
+  sp.xe = c & 0x07070707u;               // elements 0, 2, 4, 6: low 3 bits
+  sp.se = and_or(c >> 1, k.m4, k.b0);    //   and their bit 3 as a selector
+  sp.xo = (c >> 4) & 0x07070707u;        // elements 1, 3, 5, 7
+  sp.so = and_or(c >> 5, k.m4, k.b0);
+  return sp;
+}
+
+// Eight nibbles -> four packed bf16 pairs in element order.
+__device__ __forceinline__ u32x4 dequant8(const BlockLut& L, uint32_t c, const SplitConst& k) {
+  const Split sp = split8(c, k);
+  const uint32_t le = lut16(L.lo, sp.xe, sp.se), he = lut16(L.hi, sp.xe, sp.se);
+  const uint32_t lo_ = lut16(L.lo, sp.xo, sp.so), ho = lut16(L.hi, sp.xo, sp.so);
   const uint32_t e02 = __builtin_amdgcn_perm(he, le, 0x05010400u);   // [W'(e0), W'(e2)]
   const uint32_t e46 = __builtin_amdgcn_perm(he, le, 0x07030602u);   // [W'(e4), W'(e6)]
   const uint32_t o13 = __builtin_amdgcn_perm(ho, lo_, 0x05010400u);  // [W'(e1), W'(e3)]
@@ -112,14 +136,11 @@ __device__ __forceinline__ u32x4 dequant8(const BlockLut& L, uint32_t c) {
 
 // Eight nibbles -> the low and high bytes of their bf16 values, each as eight
 // bytes in the element order (0, 2, 4, 6, 1, 3, 5, 7).
-__device__ __forceinline__ void dequant8_planes(const BlockLut& L, uint32_t c, u32x2& lo8, u32x2& hi8) {
-  const uint32_t xe = c & 0x0F0F0F0Fu;
-  const uint32_t xo = (c >> 4) & 0x0F0F0F0Fu;
-  const uint32_t se = ((xe >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t so = ((xo >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t xe7 = xe & 0x07070707u, xo7 = xo & 0x07070707u;
-  lo8 = u32x2{lut16(L.lo, xe, xe7, se), lut16(L.lo, xo, xo7, so)};
-  hi8 = u32x2{lut16(L.hi, xe, xe7, se), lut16(L.hi, xo, xo7, so)};
+__device__ __forceinline__ void dequant8_planes(const BlockLut& L, uint32_t c, const SplitConst& k, u32x2& lo8,
+                                                u32x2& hi8) {
+  const Split sp = split8(c, k);
+  lo8 = u32x2{lut16(L.lo, sp.xe, sp.se), lut16(L.lo, sp.xo, sp.so)};
+  hi8 = u32x2{lut16(L.hi, sp.xe, sp.se), lut16(L.hi, sp.xo, sp.so)};
 }
 
 // Column held in slot `s` of a dX weight tile: within each group of eight the
@@ -171,6 +192,9 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[2 * kBM * kBR];   // activation tiles
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  SplitConst kc;
+  asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
+  asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
   const int rg = w & 3, ch = w >> 2;      // row group (64 rows), column half (128 columns)
   const int64_t P = kDx ? K : N;          // output columns
   const int64_t R = kDx ? N : K;          // reduction length
@@ -332,12 +356,12 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   auto store8 = [&](const BlockLut& L, uint32_t c, LDS_AS uint16_t* buf, int q) {
     if (kDx) {
       u32x2 lo8, hi8;
-      dequant8_planes(L, c, lo8, hi8);
+      dequant8_planes(L, c, kc, lo8, hi8);
       LDS_AS uint8_t* d = (LDS_AS uint8_t*)buf + dq_off + 8 * (q ^ ((t >> 3) & 3));   // chunk swizzle, see frag_planes
       *(LDS_AS u32x2*)d = lo8;
       *(LDS_AS u32x2*)(d + kPlane) = hi8;
     } else {
-      *(LDS_AS u32x4*)(buf + dq_off + 8 * q) = dequant8(L, c);
+      *(LDS_AS u32x4*)(buf + dq_off + 8 * q) = dequant8(L, c, kc);
     }
   };
   auto dequant_store = [&](const HalfCodes& hc, LDS_AS uint16_t* buf) {

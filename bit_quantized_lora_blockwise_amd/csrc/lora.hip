@@ -144,10 +144,39 @@ __global__ __launch_bounds__(kThreads) void k_lora_skinny(const uint16_t* __rest
   }
 }
 
+// Sum of `splits` fp32 partials, part[k * n + i], added in order k = 0, 1, ...
+// starting from 0 (every path that adds these partials uses this order).
+// Four outputs per thread: 16-byte loads, all splits' loads of a group of
+// four issued before the additions.
+__device__ __forceinline__ f32x4 sum_splits4(const f32x4* __restrict__ p4, int splits, int64_t n4, int64_t i4) {
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  int k = 0;
+  for (; k + 4 <= splits; k += 4) {
+    const f32x4 a = p4[(k + 0) * n4 + i4], b = p4[(k + 1) * n4 + i4];
+    const f32x4 c = p4[(k + 2) * n4 + i4], d = p4[(k + 3) * n4 + i4];
+    s += a;
+    s += b;
+    s += c;
+    s += d;
+  }
+  for (; k < splits; ++k) s += p4[k * n4 + i4];
+  return s;
+}
+
 __global__ __launch_bounds__(kThreads) void k_skinny_reduce(const float* __restrict__ part, int splits, int64_t n,
                                                             float scale, uint16_t* __restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if ((n & 3) == 0) {
+    const int64_t n4 = n >> 2;
+    for (int64_t i4 = t0; i4 < n4; i4 += stride) {
+      const f32x4 s = sum_splits4((const f32x4*)part, splits, n4, i4);
+      *(u32x2*)(out + 4 * i4) = u32x2{qk::pack_bf16x2(scale * s[0], scale * s[1]),
+                                      qk::pack_bf16x2(scale * s[2], scale * s[3])};
+    }
+    return;
+  }
+  for (int64_t i = t0; i < n; i += stride) {
     float s = 0.0f;
     for (int k = 0; k < splits; ++k) s += part[k * n + i];
     out[i] = qk::f32_to_bf16(scale * s);
@@ -213,19 +242,55 @@ __global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict
 }
 
 __global__ __launch_bounds__(kThreads) void k_tn_reduce(const float* __restrict__ part, int splits, int64_t P, int r,
-                                                        float scale, bool transpose_out, float* __restrict__ out) {
+                                                        float scale, float* __restrict__ out) {
   const int64_t n = P * r;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if ((n & 3) == 0) {
+    const int64_t n4 = n >> 2;
+    for (int64_t i4 = t0; i4 < n4; i4 += stride) ((f32x4*)out)[i4] = scale * sum_splits4((const f32x4*)part, splits, n4, i4);
+    return;
+  }
+  for (int64_t i = t0; i < n; i += stride) {
     float s = 0.0f;
     for (int k = 0; k < splits; ++k) s += part[k * n + i];
-    s *= scale;
-    if (transpose_out) {
-      const int64_t p = i / r, c = i - p * r;
-      out[c * P + p] = s;
-    } else {
-      out[i] = s;
+    out[i] = scale * s;
+  }
+}
+
+// Same sum written transposed, out[c * P + p] for the partial element p * r + c:
+// a work group takes 16 consecutive p, adds its 16 x r partials (each thread
+// four adjacent c of one p when r % 4 == 0, all loads of a group issued
+// together) into LDS and writes r rows of 16 contiguous outputs.
+constexpr int kTrP = 16;
+
+__global__ __launch_bounds__(kThreads) void k_tn_reduce_t(const float* __restrict__ part, int splits, int64_t P, int r,
+                                                          float scale, float* __restrict__ out) {
+  __shared__ float tile[kTrP][65];
+  const int64_t n = P * r;
+  const int64_t p0 = (int64_t)blockIdx.x * kTrP;
+  const int np = (int)min((int64_t)kTrP, P - p0);
+  if ((r & 3) == 0) {
+    const int r4 = r >> 2;
+    for (int e = threadIdx.x; e < np * r4; e += kThreads) {
+      const int pl = e / r4, c4 = e - pl * r4;
+      const f32x4 v = scale * sum_splits4((const f32x4*)part, splits, n >> 2, ((p0 + pl) * r >> 2) + c4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tile[pl][4 * c4 + j] = v[j];
     }
+  } else {
+    for (int e = threadIdx.x; e < np * r; e += kThreads) {
+      const int pl = e / r, c = e - pl * r;
+      const int64_t i = (p0 + pl) * r + c;
+      float s = 0.0f;
+      for (int k = 0; k < splits; ++k) s += part[k * n + i];
+      tile[pl][c] = scale * s;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < r * kTrP; e += kThreads) {
+    const int c = e / kTrP, pl = e - c * kTrP;
+    if (pl < np) out[(int64_t)c * P + p0 + pl] = tile[pl][c];
   }
 }
 
@@ -364,7 +429,7 @@ hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t l
     // decode-sized T: the slices the decode kernel also sums, added here in the same order
     hipError_t e = launch_lora_part(A, M, R, B, r, ws, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_skinny_reduce, dim3(grid_for(M * r)), dim3(kThreads), 0, s, ws, decode_t_slices(R),
+    hipLaunchKernelGGL(k_skinny_reduce, dim3(grid_for((M * r + 3) / 4)), dim3(kThreads), 0, s, ws, decode_t_slices(R),
                        M * (int64_t)r, scale, out);
     return hipGetLastError();
   }
@@ -389,7 +454,7 @@ hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t l
 #undef QL_SKINNY
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_skinny_reduce, dim3(grid_for(M * r)), dim3(kThreads), 0, s, ws, sp.splits, M * (int64_t)r,
+  hipLaunchKernelGGL(k_skinny_reduce, dim3(grid_for((M * r + 3) / 4)), dim3(kThreads), 0, s, ws, sp.splits, M * (int64_t)r,
                      scale, out);
   return hipGetLastError();
 }
@@ -415,7 +480,11 @@ hipError_t launch_lora_tn(const uint16_t* A, int64_t lda, const uint16_t* B, int
 #undef QL_TN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_tn_reduce, dim3(grid_for(P * r)), dim3(kThreads), 0, s, ws, sp.splits, P, r, scale,
-                     transpose_out, out);
+  if (transpose_out)
+    hipLaunchKernelGGL(k_tn_reduce_t, dim3((unsigned)((P + kTrP - 1) / kTrP)), dim3(kThreads), 0, s, ws, sp.splits, P,
+                       r, scale, out);
+  else
+    hipLaunchKernelGGL(k_tn_reduce, dim3(grid_for((P * r + 3) / 4)), dim3(kThreads), 0, s, ws, sp.splits, P, r, scale,
+                       out);
   return hipGetLastError();
 }
