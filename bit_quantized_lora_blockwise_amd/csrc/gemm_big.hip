@@ -11,11 +11,13 @@
 // wave barely overlaps its own VALU work with its MFMAs on gfx950).  Wave w
 // owns rows 64 (w % 4) .. +64 and columns 128 (w / 4) .. +128 of the tile:
 // 2 x 4 MFMA 32x32x16 tiles, 128 fp32 accumulators per lane.
-//  * Activation tile of a step (256 x 64 bf16): each wave loads 32 of its rows
-//    with coalesced 16-byte loads (eight rows of 128 bytes per load), two steps
-//    ahead, and stores them at the end of the step before into a
-//    double-buffered LDS tile, XOR-swizzled so that fragment reads are free of
-//    bank conflicts.  The two waves of a row group both read from it.
+//  * Activation tile of a step (256 x 64 bf16): at the start of the step
+//    before, each wave sends 32 of its rows (eight rows of 128 bytes per
+//    16-byte-per-lane load) from global memory straight into the other buffer
+//    of a double-buffered LDS tile (buffer loads to LDS: no registers, no LDS
+//    store instructions), XOR-swizzled through the lanes' global offsets so that
+//    fragment reads are free of bank conflicts.  The two waves of a row group
+//    both read from it.
 //  * Weight tile (256 x 64): rebuilt from the packed 4-bit stream once per work
 //    group; each pair of threads owns one first-level block (64 weights) and
 //    each thread converts half of it per step into a double-buffered LDS tile.
@@ -189,7 +191,8 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
                                                      int r, float scale, uint16_t* __restrict__ C,
                                                      Nf4Params p, int nseg, int64_t seg) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_b[2 * kBufElems];   // weight tiles; LoRA operands first
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2 * kBM * kBR];   // activation tiles
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a0[kBM * kBR];      // activation tiles (two buffers,
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a1[kBM * kBR];      //  filled by buffer-to-LDS loads)
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
   SplitConst kc;
@@ -302,7 +305,10 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   // Step st reads through a descriptor based at column 64 st of the tile's first
   // row whose size ends at the end of A: rows past M read as zeros, and a step
   // past the reduction has size 0.
-  auto load_a = [&](int64_t st, u32x4 (&v)[4]) {
+  // Tile st goes straight from global memory into the LDS buffer: each wave's
+  // load j fills rows 64 (w % 4) + 32 (w / 4) + 8 j .. +8 in lane order (lane l:
+  // 16 bytes at 16 l), the lane's global offset carrying the chunk swizzle.
+  auto dma_a = [&](int64_t st, LDS_AS uint16_t* abuf) {
     const int64_t left = R - st * kBR;
     const int rem = __builtin_amdgcn_readfirstlane((int)(left < kBR ? left : kBR));   // columns in this step
     const uint64_t nrec = rem > 0 ? (uint64_t)(M - m0) * R * 2 - (uint64_t)st * kBR * 2 : 0;
@@ -312,13 +318,19 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     const __amdgpu_buffer_rsrc_t ra = rsrc(pa, (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)nrec));
     const bool ok0 = !kTail || 8 * (int)achunk[0] < rem;    // chunks past the reduction read as zeros
     const bool ok1 = !kTail || 8 * (int)achunk[1] < rem;
+    // Issued from inline assembly, which writes no register: the compiler's
+    // own wait counting only over-waits around it, and it does not make every
+    // LDS read of the step wait for these loads (the builtin does, as it cannot
+    // tell the buffers apart); the barrier at the end of the step waits for them.
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      v[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, ((j & 1) ? ok1 : ok0) ? arow_off[j] : kOOB, 0, 0);
-  };
-  auto store_a = [&](const u32x4 (&v)[4], LDS_AS uint16_t* abuf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(LDS_AS u32x4*)(abuf + (64 * rg + 32 * ch + 8 * j) * kBR + 8 * l) = v[j];
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t dst = (uint32_t)(uintptr_t)(abuf + (64 * rg + 32 * ch + 8 * j) * kBR);
+      const uint32_t vo = ((j & 1) ? ok1 : ok0) ? arow_off[j] : kOOB;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(vo), "s"(ra)
+                   : "memory", "m0");
+    }
   };
   // A fragment of sub-step s, tile i: row 64 (w % 4) + 32 i + l % 32, chunk 2 s + l / 32.
   uint32_t afrag_off[4];
@@ -371,20 +383,25 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   };
 
   // ---- main loop.  At the top of step st: LDS holds activation tile st and
-  // weight tile st; registers hold codes(st + 1) and activation tile st + 1.
-  // Step st multiplies, converts codes(st + 1) into the other weight buffer,
-  // loads codes(st + 2) and activation tile st + 2, and stores tile st + 1 into
-  // the other activation buffer at its end.
+  // weight tile st; registers hold codes(st + 1).  Step st sends activation tile
+  // st + 1 into the other activation buffer (free: its last reads ended before
+  // the previous barrier), loads codes(st + 2), multiplies, and converts
+  // codes(st + 1) into the other weight buffer; the barrier at its end waits for
+  // both new tiles.
   LDS_AS uint16_t* b0 = (LDS_AS uint16_t*)lds_b;
   LDS_AS uint16_t* b1 = (LDS_AS uint16_t*)lds_b + kBufElems;
-  LDS_AS uint16_t* a0 = (LDS_AS uint16_t*)lds_a;
-  LDS_AS uint16_t* a1 = (LDS_AS uint16_t*)lds_a + kBM * kBR;
+  LDS_AS uint16_t* a0 = (LDS_AS uint16_t*)lds_a0;
+  LDS_AS uint16_t* a1 = (LDS_AS uint16_t*)lds_a1;
   const int64_t nsteps = (R + kBR - 1) / kBR;
   auto step = [&](int64_t st, const LDS_AS uint16_t* acur, LDS_AS uint16_t* anext, const LDS_AS uint16_t* bcur,
-                  LDS_AS uint16_t* bnext, const HalfCodes& hc_now, HalfCodes& hc_later, const u32x4 (&av_now)[4],
-                  u32x4 (&av_later)[4]) {
+                  LDS_AS uint16_t* bnext, const HalfCodes& hc_now, HalfCodes& hc_later) {
+    // Nothing is in flight here but, on the first step, the loads issued before
+    // the loop: waiting for them explicitly tells the compiler's wait tracking
+    // that the codes of this step have arrived, so that it places no wait after
+    // the loads to LDS below (which it cannot count, and would wait for).
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    dma_a(st + 1, anext);
     hc_later = load_codes(st + 2);
-    load_a(st + 2, av_later);
     __builtin_amdgcn_sched_barrier(0);
     const BlockLut L = make_lut(qk::e4m3fn_to_f32(hc_now.c2b) * hc_now.c1v, p);
     // fragments of sub-step s + 1 are read from LDS while sub-step s runs
@@ -423,29 +440,26 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
       __builtin_amdgcn_sched_group_barrier(0x200, kDx ? 2 : 1, 0);                 // DS write
     }
     __builtin_amdgcn_sched_barrier(0);
-    store_a(av_now, anext);
-    // this wave's LDS stores are done; the barrier hands both new tiles to all
-    // waves (the fragment reads of this step completed before their MFMAs)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // activation tile st + 1 has landed and this wave's LDS stores are done; the
+    // barrier hands both new tiles to all waves
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), seen by the compiler's wait tracking
+    __builtin_amdgcn_s_barrier();
   };
   HalfCodes hA, hB;
-  u32x4 avA[4], avB[4];
   {
+    dma_a(0, a0);
     const HalfCodes h0 = load_codes(0);
     hA = load_codes(1);
-    u32x4 av0[4];
-    load_a(0, av0);
-    load_a(1, avA);
     dequant_store(h0, b0);
-    store_a(av0, a0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), seen by the compiler's wait tracking
+    __builtin_amdgcn_s_barrier();
   }
   // Steps in pairs with no exit between them, so that the loop body is one
   // basic block and the early loads stay where they are issued; an odd step
   // count runs one more step over zeros (codes and activations past the end).
   for (int64_t st = 0; st < nsteps; st += 2) {
-    step(st, a0, a1, b0, b1, hA, hB, avA, avB);
-    step(st + 1, a1, a0, b1, b0, hB, hA, avB, avA);
+    step(st, a0, a1, b0, b1, hA, hB);
+    step(st + 1, a1, a0, b1, b0, hB, hA);
   }
 
   // ---- store C (bf16), lane layout of the 32x32 accumulators
