@@ -393,8 +393,8 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
     hipError_t e;
     if (xlds)
       e = wide ? launch_lds<16, kTPart>(grid, s, a) : launch_lds<8, kTPart>(grid, s, a);
-    else
-      e = wide ? launch_one<false, 16, 1, kTPart>(grid, s, a) : launch_one<false, 8, 1, kTPart>(grid, s, a);
+    else   // X read with each step (127 VGPRs): four waves keep four work groups per CU resident
+      e = wide ? launch_one<false, 16, 1, kTPart>(grid, s, a) : launch_one<false, 4, 1, kTPart>(grid, s, a);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
