@@ -26,6 +26,14 @@ constexpr int kThreads = 256;
 // The eight weights of a thread -> eight packed codes; `a` returns the block's
 // absmax (shared by the 8 lanes of an aligned group through DPP, so all eight
 // lanes of a block must be active together).  tab: the bucket table in LDS.
+// floor(x) as int32 in one instruction (the compiler emits a floor and a
+// conversion); non-finite x gives an out-of-range index that the caller clamps.
+__device__ __forceinline__ int cvt_floor_i32(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t* tab, uint32_t tab_base,
                                             float& a_out) {
   uint32_t m = 0;
@@ -36,30 +44,33 @@ __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t*
   // 16 / a for a normal absmax; an all-zero block gives n' = 0 (codes 7)
   const bool a_normal = m >= 0x00800000u;
   const float y16 = a_normal ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
-  uint32_t packed = 0, redo = (m != 0 && !a_normal) ? 0xFFu : 0u;
+  uint32_t packed = 0;
+  bool redo = m != 0 && !a_normal;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float n16 = w[j] * y16;
-    const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);   // bucket (clamped: non-finite input)
-    const uint32_t addr = tab_base + 8u * (uint32_t)bi;
+    // bucket floor(n16) + 17 in [1, 33] for finite weights; the unsigned min keeps
+    // a non-finite input inside the table
+    const uint32_t bi = min((uint32_t)(cvt_floor_i32(n16) + 17), 33u);
+    const uint32_t addr = tab_base + 8u * bi;
     const float t16 = __uint_as_float(*(const LDS_AS uint32_t*)(uintptr_t)addr);
     const uint32_t mb = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
     const uint32_t c = (mb & 15u) + (n16 >= t16 ? 1u : 0u);
-    redo |= (__builtin_fabsf(n16 - t16) <= __uint_as_float(mb) ? 1u : 0u) << j;
+    redo |= __builtin_fabsf(n16 - t16) <= __uint_as_float(mb);
     packed |= c << (4 * j);
   }
   if (redo) {
-    // correctly rounded quotient for the undecided weights
+    // correctly rounded quotients for the whole octet (the same codes wherever
+    // the approximate one was decided)
+    packed = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if ((redo >> j) & 1u) {
-        const float n = (m == 0) ? 0.0f : w[j] / a;
-        const float n16 = 16.0f * n;                            // exact
-        const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);
-        const float t16 = __uint_as_float(tab[2 * bi]);
-        const uint32_t c = (tab[2 * bi + 1] & 15u) + (n16 >= t16 ? 1u : 0u);
-        packed = (packed & ~(15u << (4 * j))) | (c << (4 * j));
-      }
+      const float n = (m == 0) ? 0.0f : w[j] / a;
+      const float n16 = 16.0f * n;                            // exact
+      const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);
+      const float t16 = __uint_as_float(tab[2 * bi]);
+      const uint32_t c = (tab[2 * bi + 1] & 15u) + (n16 >= t16 ? 1u : 0u);
+      packed |= c << (4 * j);
     }
   }
   a_out = a;
