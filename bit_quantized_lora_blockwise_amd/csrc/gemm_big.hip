@@ -326,10 +326,14 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     for (int j = 0; j < 4; ++j) {
       const uint32_t dst = (uint32_t)(uintptr_t)(abuf + (64 * rg + 32 * ch + 8 * j) * kBR);
       const uint32_t vo = ((j & 1) ? ok1 : ok0) ? arow_off[j] : kOOB;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :
-                   : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(vo), "s"(ra)
-                   : "memory", "m0");
+      // M0 (the LDS address, read when the load issues) is saved and restored
+      // here, since the compiler does not track it across inline assembly
+      uint32_t m0_saved;
+      asm volatile(
+          "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+          : "=&s"(m0_saved)
+          : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(vo), "s"(ra)
+          : "memory");
     }
   };
   // A fragment of sub-step s, tile i: row 64 (w % 4) + 32 i + l % 32, chunk 2 s + l / 32.
