@@ -20,8 +20,9 @@
 // in which the lookups produce the weights (low nibbles, then high nibbles), so
 // the MFMA needs no re-interleaving of the looked-up values.  The staging is
 // finished before the code stream is requested, so the first steps do not wait
-// for X behind the stream.  Larger X is read from global memory together with
-// the step's codes.
+// for X behind the stream.  X of 32 to 128 KB goes to a persistent kernel that
+// stages it in LDS once per CU and walks 16-row tiles in turn; larger X is read
+// from global memory together with the step's codes.
 #include "kernels.h"
 
 namespace {
@@ -330,6 +331,237 @@ __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// X of 32 to 128 KB (e.g. M = 16 at K = 4096): one persistent work group of 16
+// waves per CU stages all of X in LDS once (the same column order as above) and
+// then takes 16-row tiles blockIdx.x, blockIdx.x + gridDim.x, ...; the waves
+// split each tile's K as above.  A wave's (tile, step) items form one stream
+// with the next item's codes in flight while the current one is converted, so
+// the first step of the next tile is requested before the current tile's
+// partial sums are added.  Per-work-group X reads in 16-byte pieces (the path
+// above for larger X) are replaced by one staging pass per CU.
+constexpr int kXPersistBytes = 131072;
+
+// One item of a wave's stream: its block's codes and scales.  The scale byte is
+// kept as a byte so that its widening is not scheduled at the load.
+struct PStep {
+  u32x4 cw[2];
+  uint8_t c2b;
+  float c1v;
+};
+
+template <bool kTPart>
+__global__ __launch_bounds__(1024) void k_qgemv_persist(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                        int64_t N, int64_t ld, const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ c2,
+                                                        const float* __restrict__ c1, uint16_t* __restrict__ T,
+                                                        const float* __restrict__ Tp, int S,
+                                                        const uint16_t* __restrict__ L2, int r, float scale,
+                                                        uint16_t* __restrict__ Y, Nf4Params p) {
+  constexpr int kWv = 16, kThr = 1024, kXPer = kXPersistBytes / (16 * kThr);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kXPersistBytes + kZeroBytes + kWv * 64 * 16];
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int g = l >> 4, col = l & 15;
+  const bool m_ok = col < M;
+  const uint32_t kblocks = (uint32_t)(K / qk::kBlock);
+  const int64_t ntiles = (N + kRows - 1) / kRows;
+  const int64_t my_tiles = ntiles > blockIdx.x ? (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
+  SplitConst kc;
+  asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
+  asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
+  const uint32_t nsteps = (kblocks + 3) / 4;
+  const uint32_t nst = nsteps > (uint32_t)w ? (nsteps - (uint32_t)w + kWv - 1) / kWv : 0u;   // steps per tile, uniform
+  const uint32_t kb0 = 4u * (uint32_t)w + (uint32_t)g;
+  const uint32_t kbstep = 4u * kWv;
+
+  const __amdgpu_buffer_rsrc_t rc = rsrc(codes, (uint64_t)N * (K / 2));
+  const __amdgpu_buffer_rsrc_t r2 = rsrc(c2, (uint64_t)N * kblocks);
+  const __amdgpu_buffer_rsrc_t r1 = rsrc(c1, 4 * (((uint64_t)N * kblocks + 255) / 256));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(X, (uint64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rl = rsrc(L2, 2 * ((uint64_t)(r - 1) * ld + N));
+
+  // ---- X (all of it) first, then the T slices, then the stream
+  LDS_AS uint8_t* xl = (LDS_AS uint8_t*)lds;
+  const uint32_t xbytes = (uint32_t)(M * K * 2);
+  u32x4 xr[kXPer];
+#pragma unroll
+  for (int j = 0; j < kXPer; ++j) {
+    const uint32_t o = 16u * (uint32_t)(t + j * kThr);
+    xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, o < xbytes ? o : kOOB, 0, 0);
+  }
+  const int rb = 16 * w + 4 * g;                   // first of this lane's four LoRA ranks
+  const bool t_ok = rb < r && m_ok;
+  f32x4 ps[kTPart ? kDecodeTSlices : 1];
+  uint16_t vt16[4];                                // T[col][rb .. rb + 3] when T is given
+  if (!kTPart) {
+    const __amdgpu_buffer_rsrc_t rt = rsrc(T, 2 * (uint64_t)M * r);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t ot = (rb + q < r && m_ok) ? (uint32_t)(2 * (col * r + rb + q)) : kOOB;
+      vt16[q] = __builtin_amdgcn_raw_buffer_load_b16(rt, ot, 0, 0);
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rp = rsrc(Tp, 4 * (uint64_t)S * M * r);
+#pragma unroll
+    for (int s = 0; s < kDecodeTSlices; ++s)
+      ps[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rp, (t_ok && s < S) ? (uint32_t)(4 * (((int64_t)s * M + col) * r + rb)) : kOOB,
+                                            0, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint32_t nq = nst * (uint32_t)my_tiles;
+  // item q of this wave: tile j = q / nst of the work group, step i = q % nst.
+  // Items past the end are requested too, at an offset that reads zeros: with no
+  // branch around a load the compiler waits for exactly the step it converts.
+  struct Offs {
+    uint32_t co, o2, o1;
+  };
+  // 32-bit offsets: a launch covers fewer than 2^31 code bytes, and rows past N
+  // (items past the end) stay below 2^32
+  const uint32_t n32 = (uint32_t)N;
+  auto item_offs = [&](uint32_t q) {
+    const uint32_t j = nst ? q / nst : 0u, i = q - j * nst;
+    const uint32_t nrow = (blockIdx.x + j * gridDim.x) * kRows + (uint32_t)col;
+    const uint32_t kb = kb0 + i * kbstep;
+    const bool ok = q < nq && nrow < n32 && kb < kblocks;
+    // block index b; its 32 code bytes start at 32 b.  The product is written out
+    // because the compiler's 64-bit multiply-add form borrows a register that may
+    // still be waiting for a load.
+    uint32_t nk;
+    asm("v_mul_lo_u32 %0, %1, %2" : "=v"(nk) : "v"(nrow), "s"(kblocks));
+    const uint32_t b = nk + kb;
+    return Offs{ok ? 32u * b : kOOB, ok ? b : kOOB, ok ? 4 * (b >> 8) : kOOB};
+  };
+  auto issue = [&](const Offs& o, PStep& st) {
+    st.cw[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, o.co, 0, 0);
+    st.cw[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, o.co + 16, 0, 0);
+    st.c2b = __builtin_amdgcn_raw_buffer_load_b8(r2, o.o2, 0, 0);
+    st.c1v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, o.o1, 0, 0));
+  };
+  auto load_item = [&](uint32_t q, PStep& st) { issue(item_offs(q), st); };
+  // LoRA L2 fragment of tile j (wave w covers ranks 16 w .. 16 w + 15), kept as
+  // loaded until the tile's LoRA product so that nothing waits for it earlier
+  uint16_t vl[4];
+  auto load_l2 = [&](int64_t j) {
+    const int64_t nrow = ((int64_t)blockIdx.x + j * gridDim.x) * kRows + col;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t ol = (rb + q < r && nrow < N && j < my_tiles) ? (uint32_t)(2 * ((int64_t)(rb + q) * ld + nrow)) : kOOB;
+      vl[q] = __builtin_amdgcn_raw_buffer_load_b16(rl, ol, 0, 0);
+    }
+  };
+  // The first tile's L2 fragment is requested before its first codes (a wait for
+  // it then leaves the codes in flight), their offsets formed before either.
+  PStep sa, sb;
+  const Offs o0 = item_offs(0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_l2(0);
+  issue(o0, sa);
+
+  // ---- T fragment (the same for every tile)
+  uint32_t lt[2];
+  {
+    uint32_t vt[4];
+    if (kTPart) {
+      f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < kDecodeTSlices; ++s)
+        if (s < S) sum += ps[s];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vt[q] = qk::f32_to_bf16(sum[q]);
+      if (T && blockIdx.x == 0 && t_ok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) T[col * r + rb + q] = (uint16_t)vt[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vt[q] = vt16[q];
+    }
+    lt[0] = vt[0] | (vt[1] << 16);
+    lt[1] = vt[2] | (vt[3] << 16);
+  }
+
+  // ---- X into LDS, eight-column groups as (0, 2, 4, 6, 1, 3, 5, 7)
+#pragma unroll
+  for (int j = 0; j < kXPer; ++j) {
+    const uint32_t o = 16u * (uint32_t)(t + j * kThr);
+    const u32x4 v = xr[j];
+    u32x4 e;
+    e[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+    e[1] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+    e[2] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+    e[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+    if (o < xbytes) *(LDS_AS u32x4*)(xl + o) = e;
+  }
+  if (t < kZeroBytes / 16) *(LDS_AS u32x4*)(xl + kXPersistBytes + 16 * t) = u32x4{0, 0, 0, 0};
+  __syncthreads();
+
+  f32x4* red = (f32x4*)(lds + kXPersistBytes + kZeroBytes);
+  f32x4 acc = {0, 0, 0, 0};
+  // tile j done by this wave: LoRA term, partial sums of the 16 waves added in
+  // LDS in a fixed order, output row written; the next tile's L2 fragment requested
+  auto finish_tile = [&](int64_t j) {
+    // the two bf16 pairs of the L2 fragment, formed here: the empty volatile asm
+    // keeps the first use of the loaded values (and the wait for them) at this point
+    uint16_t a0 = vl[0], a1 = vl[1], a2 = vl[2], a3 = vl[3];
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    const uint32_t ll0 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+    const uint32_t ll1 = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+    f32x4 zl = {0, 0, 0, 0};
+    zl = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{lt[0], lt[1]}),
+                                                   __builtin_bit_cast(s16x4, u32x2{ll0, ll1}), zl, 0, 0, 0);
+    acc += scale * zl;
+    red[w * 64 + l] = acc;
+    acc = f32x4{0, 0, 0, 0};
+    __syncthreads();
+    if (w == 0) {
+      f32x4 sum = red[l];
+#pragma unroll
+      for (int ww = 1; ww < kWv; ++ww) sum += red[ww * 64 + l];
+      const int64_t nrow = ((int64_t)blockIdx.x + j * gridDim.x) * kRows + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if (m < M && nrow < N) Y[(int64_t)m * ld + nrow] = qk::f32_to_bf16(sum[i]);
+      }
+    }
+    __syncthreads();                               // red is reused by the next tile
+    load_l2(j + 1);
+  };
+  auto process = [&](uint32_t q, const PStep& st) {
+    const uint32_t j = q / nst, i = q - j * nst;
+    const uint32_t kb = kb0 + i * kbstep;
+    const BlockLut L = make_lut(qk::e4m3fn_to_f32(st.c2b) * st.c1v, p);
+    const bool xok = m_ok && kb < kblocks;
+    const LDS_AS u32x4* xs =
+        (const LDS_AS u32x4*)(xl + (xok ? ((uint32_t)col * (uint32_t)K + 64u * kb) * 2u : (uint32_t)kXPersistBytes));
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const u32x4 bv = dequant8_eo(L, st.cw[d >> 2][d & 3], kc);
+      acc = mfma16(__builtin_bit_cast(bf16x8, xs[d]), __builtin_bit_cast(bf16x8, bv), acc);
+    }
+    if (i + 1 == nst) finish_tile((int64_t)j);
+  };
+  if (nst == 0) {
+    for (int64_t j = 0; j < my_tiles; ++j) finish_tile(j);   // no steps here: the LoRA ranks and the barriers
+  } else {
+    // items in pairs (no exit between the two halves, so the compiler's wait
+    // before each conversion covers exactly that item), then the odd last one
+    uint32_t q = 0;
+    for (; q + 2 <= nq; q += 2) {
+      load_item(q + 1, sb);
+      __builtin_amdgcn_sched_barrier(0);         // requested before this item's work is scheduled
+      process(q, sa);
+      load_item(q + 2, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      process(q + 1, sb);
+    }
+    if (q < nq) process(q, sa);
+  }
+}
+
 // One launch's operands besides the shape and the grid.
 struct QgemvArgs {
   const uint16_t* X;
@@ -375,6 +607,14 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
   chunk = chunk / 256 * 256;
   if (chunk < 256) return hipErrorInvalidValue;
   const bool xlds = M * K * 2 <= kXBytes;
+  const bool xpersist = !xlds && M * K * 2 <= kXPersistBytes;
+  int cus = 0;
+  if (xpersist) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess || cus < 1)
+      cus = 256;
+  }
   for (int64_t r0 = 0; r0 < N; r0 += chunk) {
     QgemvArgs a = a0;
     a.rows = N - r0 < chunk ? N - r0 : chunk;
@@ -391,7 +631,12 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
     // than two waves, else 8
     const bool wide = wgs <= 384;
     hipError_t e;
-    if (xlds)
+    if (xpersist) {
+      const unsigned pg = (unsigned)(wgs < cus ? wgs : cus);
+      hipLaunchKernelGGL((k_qgemv_persist<kTPart>), dim3(pg), dim3(1024), 0, s, a.X, a.M, a.K, a.rows, a.ld, a.codes,
+                         a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params());
+      e = hipGetLastError();
+    } else if (xlds)
       e = wide ? launch_lds<16, kTPart>(grid, s, a) : launch_lds<8, kTPart>(grid, s, a);
     else   // X read with each step (127 VGPRs): four waves keep four work groups per CU resident
       e = wide ? launch_one<false, 16, 1, kTPart>(grid, s, a) : launch_one<false, 4, 1, kTPart>(grid, s, a);

@@ -132,8 +132,9 @@ def test_decode_llama7b_up_full(M):
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_decode_llama7b_down_full(M):
     """Decode-sized forward at the 11008 -> 4096 shape (few work groups, so the
-    kernel splits K over more waves; X staged in LDS at M = 1, read from global
-    memory above), every output compared."""
+    kernel splits K over more waves; X staged in LDS per work group at M = 1, once
+    per CU by the persistent kernel at M = 4, read from global memory at M = 16),
+    every output compared."""
     inp = WL.layer_inputs(4096, 11008, M, 64, seed_base=7100 + M)
     print(f"[decode] M={M} K=11008 N=4096", flush=True)
     q = qlib()
@@ -181,7 +182,9 @@ def test_decode_graph_replay_matches_eager():
 
 
 # decode shapes whose step counts do not divide evenly over the waves: 8-wave
-# work groups (over 384 of them) and 16-wave ones, X in LDS and in global memory
+# work groups (over 384 of them) and 16-wave ones, X in LDS per work group, and
+# the persistent kernel (M = 9 and 12: X of 32-128 KB; at K = 1600 nine of its
+# sixteen waves have no steps)
 DECODE_SPLIT = [(3, 2880, 6200, 8), (2, 2368, 100, 64), (9, 4160, 6500, 16), (12, 1600, 40, 20)]
 
 
