@@ -132,7 +132,7 @@ __device__ __forceinline__ u32x4 dequant8_eo(const BlockLut& L, uint32_t c, cons
 template <bool kXLds>
 struct Step {
   u32x4 cw[2];
-  uint32_t c2b;
+  uint8_t c2b;                                     // kept a byte: its widening is not scheduled at the load
   float c1v;
   u32x4 xa[kXLds ? 1 : 8];
 };
@@ -140,8 +140,11 @@ struct Step {
 // kTPart: T is not given but formed here from the S fp32 slices Tp[s][m][c]
 // (added in order s = 0 .. S-1, rounded once), and written to T (if not null)
 // by work group 0.
+// Eight-wave work groups are held to six waves per SIMD (three work groups per
+// CU, at most 80 VGPRs): given the registers, the compiler would otherwise keep
+// more values live and fit only two.
 template <bool kXLds, int kWv, int kXPer, bool kTPart>
-__global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+__global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         int64_t N, int64_t ld, const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ c2,
                                                         const float* __restrict__ c1,
@@ -170,6 +173,12 @@ __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restri
   const uint32_t kb0 = 4u * (uint32_t)w + (uint32_t)g;
   const uint32_t kbstep = 4u * kWv;
   const uint32_t kb_lim = row_ok ? kblocks : 0u;   // blocks valid for the lane's weight row
+  // row offsets formed before any load is issued and made opaque: refolded into
+  // a later add, the compiler's 64-bit multiply-add may take a register that a
+  // pending load writes as its don't-care high half, and then wait for that load
+  uint32_t code_row = (uint32_t)(nrow * (K / 2));
+  uint32_t blk_row = (uint32_t)(nrow * kblocks);
+  asm volatile("" : "+v"(code_row), "+v"(blk_row));
 
   const __amdgpu_buffer_rsrc_t rc = rsrc(codes, (uint64_t)N * (K / 2));
   const __amdgpu_buffer_rsrc_t r2 = rsrc(c2, (uint64_t)N * kblocks);
@@ -202,9 +211,28 @@ __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restri
                                             rp, (t_ok && s < S) ? (uint32_t)(4 * (((int64_t)s * M + col) * r + rb)) : kOOB,
                                             0, 0));
   }
+  // The LoRA operands next, still ahead of the code stream: L2[rb .. rb + 3][nrow]
+  // and (T given) T[col][rb .. rb + 3], kept as loaded (16-bit) until their use at
+  // the end, so that no wait for them covers the code stream.
+  uint16_t vl[4], vt16[4];
+  {
+    const __amdgpu_buffer_rsrc_t rl = rsrc(L2, 2 * ((uint64_t)(r - 1) * ld + N));
+    const __amdgpu_buffer_rsrc_t rt = rsrc(T, 2 * (uint64_t)M * r);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool rk = rb + j < r;
+      const uint32_t ol = (rk && row_ok) ? (uint32_t)(2 * ((int64_t)(rb + j) * ld + nrow)) : kOOB;
+      vl[j] = __builtin_amdgcn_raw_buffer_load_b16(rl, ol, 0, 0);
+      if (!kTPart) {
+        const uint32_t ot = (rk && m_ok) ? (uint32_t)(2 * (col * r + rb + j)) : kOOB;
+        vt16[j] = __builtin_amdgcn_raw_buffer_load_b16(rt, ot, 0, 0);
+      }
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
-  const uint32_t code_row = (uint32_t)(nrow * (K / 2));
-  const uint32_t blk_row = (uint32_t)(nrow * kblocks);
+  // Step i >= nst lies past the wave's last step (kb >= kblocks): its loads read
+  // zeros, so they are issued without a branch (a branch around a load makes the
+  // compiler wait for it where the paths join).
   auto load_step = [&](uint32_t i, Step<kXLds>& st) {
     const uint32_t kb = kb0 + i * kbstep;
     const bool ok = kb < kb_lim;
@@ -225,27 +253,12 @@ __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restri
   load_step(0, sa);                                // all-zero (out-of-range offsets) when the wave has no step
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- LoRA term operands, one 16x16x16 MFMA per wave: wave w covers ranks
-  // 16 w .. 16 w + 15, lane group g ranks 16 w + 4 g .. + 3.
-  uint32_t ll[2], lt[2];
+  // ---- T fragment: lane group g holds T[col][rb .. rb + 3]
+  uint32_t lt[2];
   {
-    const __amdgpu_buffer_rsrc_t rl = rsrc(L2, 2 * ((uint64_t)(r - 1) * ld + N));
-    const __amdgpu_buffer_rsrc_t rt = rsrc(T, 2 * (uint64_t)M * r);
-    uint32_t vl[4], vt[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool rk = rb + j < r;
-      const uint32_t ol = (rk && row_ok) ? (uint32_t)(2 * ((int64_t)(rb + j) * ld + nrow)) : kOOB;
-      vl[j] = __builtin_amdgcn_raw_buffer_load_b16(rl, ol, 0, 0);
-      if (!kTPart) {
-        const uint32_t ot = (rk && m_ok) ? (uint32_t)(2 * (col * r + rb + j)) : kOOB;
-        vt[j] = __builtin_amdgcn_raw_buffer_load_b16(rt, ot, 0, 0);
-      }
-    }
-    ll[0] = vl[0] | (vl[1] << 16);
-    ll[1] = vl[2] | (vl[3] << 16);
+    uint32_t vt[4];
     if (kTPart) {
-      // T[col][rb .. rb + 3]: the slices added in order s = 0 .. S-1, rounded once
+      // the slices added in order s = 0 .. S-1, rounded once
       f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < kDecodeTSlices; ++s)
@@ -256,9 +269,9 @@ __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < 4; ++j) T[col * r + rb + j] = (uint16_t)vt[j];
       }
+      lt[0] = vt[0] | (vt[1] << 16);
+      lt[1] = vt[2] | (vt[3] << 16);
     }
-    lt[0] = vt[0] | (vt[1] << 16);
-    lt[1] = vt[2] | (vt[3] << 16);
   }
 
   if (kXLds) {
@@ -299,20 +312,37 @@ __global__ __launch_bounds__(64 * kWv) void k_qgemv_fwd(const uint16_t* __restri
       }
     }
   };
-  // steps in pairs: the next step's loads are issued before the current one is
-  // converted
-  for (uint32_t i = 0; i < nst; i += 2) {
-    if (i + 1 < nst) load_step(i + 1, sb);
+  // steps in pairs, the next step's loads issued before the current one is
+  // converted (no exit between the halves: the compiler's wait before each
+  // conversion then covers exactly that step), then the odd last step
+  uint32_t i = 0;
+  for (; i + 2 <= nst; i += 2) {
+    load_step(i + 1, sb);
+    __builtin_amdgcn_sched_barrier(0);
     compute_step(i, sa);
-    if (i + 1 >= nst) break;
-    if (i + 2 < nst) load_step(i + 2, sa);
+    load_step(i + 2, sa);
+    __builtin_amdgcn_sched_barrier(0);
     compute_step(i + 1, sb);
   }
+  if (i < nst) compute_step(i, sa);
 
   {
+    // the L2 (and given T) values are first used here: the empty volatile asm
+    // keeps the wait for them at this point; the pairs are formed with the perm
+    // builtin so that the compiler sees the VALU write ahead of the MFMA
+    uint16_t a0 = vl[0], a1 = vl[1], a2 = vl[2], a3 = vl[3];
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    const uint32_t ll0 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+    const uint32_t ll1 = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+    if (!kTPart) {
+      uint16_t b0 = vt16[0], b1 = vt16[1], b2 = vt16[2], b3 = vt16[3];
+      asm volatile("" : "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));
+      lt[0] = __builtin_amdgcn_perm(b1, b0, 0x05040100u);
+      lt[1] = __builtin_amdgcn_perm(b3, b2, 0x05040100u);
+    }
     f32x4 zl = {0, 0, 0, 0};
     zl = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{lt[0], lt[1]}),
-                                                   __builtin_bit_cast(s16x4, u32x2{ll[0], ll[1]}), zl, 0, 0, 0);
+                                                   __builtin_bit_cast(s16x4, u32x2{ll0, ll1}), zl, 0, 0, 0);
     acc += scale * zl;
   }
   f32x4* red = (f32x4*)(lds + (kXLds ? kXBytes + kZeroBytes : 0));
