@@ -45,7 +45,12 @@ __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t*
   const bool a_normal = m >= 0x00800000u;
   const float y16 = a_normal ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
   uint32_t packed = 0;
-  bool redo = m != 0 && !a_normal;
+  // a weight is near its bucket's threshold when |n16 - t16| <= margin, i.e. when
+  // fl(|n16 - t16| - margin) <= 0 (exact: the difference of two floats is
+  // non-positive exactly when the first is not larger); the octet is redone when
+  // the smallest of the eight is.  A NaN difference never counts as near, as
+  // before, since the minimum passes over it.
+  float emin = __builtin_inff();
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float n16 = w[j] * y16;
@@ -56,9 +61,10 @@ __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t*
     const float t16 = __uint_as_float(*(const LDS_AS uint32_t*)(uintptr_t)addr);
     const uint32_t mb = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
     const uint32_t c = (mb & 15u) + (n16 >= t16 ? 1u : 0u);
-    redo |= __builtin_fabsf(n16 - t16) <= __uint_as_float(mb);
+    emin = __builtin_fminf(emin, __builtin_fabsf(n16 - t16) - __uint_as_float(mb));
     packed |= c << (4 * j);
   }
+  const bool redo = (m != 0 && !a_normal) || emin <= 0.0f;
   if (redo) {
     // correctly rounded quotients for the whole octet (the same codes wherever
     // the approximate one was decided)
