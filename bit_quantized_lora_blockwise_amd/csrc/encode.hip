@@ -20,9 +20,9 @@ constexpr int kThreads = 256;
 // bucket in a 34-entry LDS table (one 8-byte read: the bucket's threshold, a
 // margin and the count of thresholds below the bucket), and compares once.
 // Weights whose n' lies within the margin of the bucket's threshold -- and
-// all weights of blocks whose absmax is not a normal number -- are redone
-// with the correctly rounded division, so the codes are exactly those of the
-// definition.
+// all weights of blocks with a nonzero finite absmax outside [2^-123, 2^125),
+// where 16 / absmax would not be a finite normal number -- are redone with the
+// correctly rounded division, so the codes are exactly those of the definition.
 // The eight weights of a thread -> eight packed codes; `a` returns the block's
 // absmax (shared by the 8 lanes of an aligned group through DPP, so all eight
 // lanes of a block must be active together).  tab: the bucket table in LDS.
@@ -41,9 +41,12 @@ __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t*
   for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(w[j]) & 0x7FFFFFFFu);
   m = qk::dpp_max8(m);
   const float a = __uint_as_float(m);
-  // 16 / a for a normal absmax; an all-zero block gives n' = 0 (codes 7)
-  const bool a_normal = m >= 0x00800000u;
-  const float y16 = a_normal ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
+  // 16 / a when it is a finite normal number, i.e. a in [2^-123, 2^125) (and, as
+  // for any other input, for an infinite or NaN absmax); every other nonzero
+  // absmax -- subnormal, or at either end of the normal range -- takes the exact
+  // division below.  An all-zero block gives n' = 0 (codes 7).
+  const bool a_fast = (m >= 0x02000000u && m < 0x7E000000u) || m >= 0x7F800000u;
+  const float y16 = a_fast ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
   uint32_t packed = 0;
   // a weight is near its bucket's threshold when |n16 - t16| <= margin, i.e. when
   // fl(|n16 - t16| - margin) <= 0 (exact: the difference of two floats is
@@ -64,7 +67,7 @@ __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t*
     emin = __builtin_fminf(emin, __builtin_fabsf(n16 - t16) - __uint_as_float(mb));
     packed |= c << (4 * j);
   }
-  const bool redo = (m != 0 && !a_normal) || emin <= 0.0f;
+  const bool redo = (m != 0 && !a_fast) || emin <= 0.0f;
   if (redo) {
     // correctly rounded quotients for the whole octet (the same codes wherever
     // the approximate one was decided)

@@ -73,6 +73,10 @@ def _edge_matrix():
     rows.append(neg0)                                                             # signed zeros
     rows.append((rng.standard_normal(256) * 3e4).astype(np.float32))             # large magnitudes
     rows.append(np.where(rng.random(256) < 0.5, 1.0, -1.0).astype(np.float32))   # +-absmax only
+    # absmax at the ends of the normal range (16 / absmax overflows below 2^-124,
+    # and its reciprocal is subnormal above 2^126): codebook values x 2^e
+    for e in (-126, -125, -124, -123, 125, 126, 127):
+        rows.append(np.array([np.float32(q[(5 * i) % 16]) * np.float32(2.0 ** e) for i in range(256)], np.float32))
     return np.stack(rows)
 
 
