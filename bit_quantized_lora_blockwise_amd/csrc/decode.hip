@@ -6,8 +6,8 @@
 // Layer formula: nlp-lineage milestone page on QLoRA, "The idea", notation
 // paragraph; dequantisation on the fly: examadda page, "The Core Idea".
 //
-// Work group: 16 weight rows x all of K, split over 8 waves (16 when the grid
-// has few work groups) that take 256-column steps in turn; in a step, lane
+// Work group: 16 weight rows x all of K, split over 8 waves (16 or 4 when X is
+// read from global memory) that take 256-column steps in turn; in a step, lane
 // (g = l / 16, row = l % 16) holds one block (64 weights, 32 bytes of codes): it
 // builds the block's 16-entry bf16 table in registers (two byte planes) and
 // looks each nibble up with v_perm_b32.  Each wave keeps one step in flight
@@ -657,8 +657,8 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
     if (kTPart && r0 > 0) a.T = nullptr;           // the formed T is written by the first chunk's work group 0
     const int64_t wgs = (a.rows + kRows - 1) / kRows;
     dim3 grid((unsigned)wgs);
-    // 16 waves per work group when the grid alone would leave SIMDs with fewer
-    // than two waves, else 8
+    // X read from global memory: 16 waves per work group when the grid alone
+    // would leave SIMDs with fewer than two waves, else 4
     const bool wide = wgs <= 384;
     hipError_t e;
     if (xpersist) {
@@ -667,7 +667,7 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
                          a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params());
       e = hipGetLastError();
     } else if (xlds)
-      e = wide ? launch_lds<16, kTPart>(grid, s, a) : launch_lds<8, kTPart>(grid, s, a);
+      e = launch_lds<8, kTPart>(grid, s, a);     // 8 waves: measured ahead of 16 on small grids too
     else   // X read with each step (127 VGPRs): four waves keep four work groups per CU resident
       e = wide ? launch_one<false, 16, 1, kTPart>(grid, s, a) : launch_one<false, 4, 1, kTPart>(grid, s, a);
     if (e != hipSuccess) return e;
