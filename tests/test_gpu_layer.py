@@ -194,6 +194,28 @@ def test_decode_uneven_wave_split(M, K, N, r):
     full_case(inp, 1.25, "decode split")
 
 
+# the persistent decode kernel (X of 32-128 KB) with T formed elsewhere: a rank
+# that is not a multiple of 4 (T by the separate product and its reduce), and T
+# handed to the stage entry point
+DECODE_PERSIST_GIVEN_T = [(9, 4160, 6500, 7), (16, 2048, 1000, 33), (5, 6400, 300, 64)]
+
+
+@pytest.mark.parametrize("M,K,N,r", DECODE_PERSIST_GIVEN_T)
+def test_decode_persistent_given_T(M, K, N, r):
+    inp = WL.layer_inputs(N, K, M, r, seed_base=M * 17 + K + N * 3 + r, l2_std=0.3)
+    full_case(inp, 0.8, "decode persistent")
+    q = qlib()
+    gq, rq = quantize_both(inp["W"])
+    X, L1, L2 = (inp[k].to(DEV) for k in ("X", "L1", "L2"))
+    T = q.qlora_lora_down(X, L1)
+    Y = q.qlora_linear_fwd_t(X, *gq, N, T, L2, 0.8)
+    torch.cuda.synchronize()
+    Wq = O.nf4_dequantize(*rq, N, K)
+    rY, rT = O.qlora_forward(bits(inp["X"]), Wq, bits(inp["L1"]), bits(inp["L2"]), 0.8)
+    assert_close(bits(T), rT, f"decode persistent given T: T M={M} K={K} r={r}")
+    assert_close(bits(Y), rY, f"decode persistent given T: Y M={M} K={K} r={r}")
+
+
 def _sampled_case(inp, name, n_rows=48, seed=0):
     """Full-size check: dL1, dL2 and T in full; Y and dX on sampled rows."""
     N, K = inp["W"].shape
