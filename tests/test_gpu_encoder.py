@@ -176,6 +176,101 @@ def test_nearest_code_sweep():
     assert_bitexact(codes.cpu().numpy(), r_codes, "sweep codes")
 
 
+def _bit_range_chunks(total, chunk):
+    for lo in range(0, total, chunk):
+        yield lo, min(total, lo + chunk)
+
+
+def test_nearest_code_exhaustive():
+    """Every fp32 n in [-1, 1] (2 x 1,065,353,217 values): blocks of 64 whose
+    first element is 1.0 (absmax 1, so n = w exactly) and 63 consecutive fp32
+    bit patterns; the code of each must be the oracle's nearest-level rule.  The
+    inputs are built on the GPU from the bit patterns; the expected codes come
+    from the oracle on the CPU, one chunk per thread."""
+    from concurrent.futures import ThreadPoolExecutor
+    import bit_quantized_lora_blockwise_amd as q
+    one = int(np.float32(1.0).view(np.uint32))
+    total = one + 1                                                   # bit patterns 0 .. one
+    per, nblk = 63, 1 << 20
+    chunk = per * nblk
+
+    def expect(lo, hi, sign):
+        v = np.arange(lo, hi, dtype=np.uint32) | np.uint32(sign)
+        return O.nf4_nearest_code(v.view(np.float32))
+
+    def check(got, lo, hi, sign):
+        exp = expect(lo, hi, sign)
+        assert got.size == exp.size == hi - lo
+        bad = np.flatnonzero(got != exp)
+        return (lo, sign, bad.size, bad[:4], got[bad[:4]], exp[bad[:4]], exp.size)
+
+    results = []
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        futs = []
+        for sign in (0, 0x80000000):
+            for lo, hi in _bit_range_chunks(total, chunk):
+                n = hi - lo
+                nb = (n + per - 1) // per
+                bits = torch.arange(lo, lo + nb * per, dtype=torch.int64, device=DEV)
+                bits = torch.where(bits < hi, bits, torch.zeros_like(bits))
+                vals = bits.to(torch.int32).view(torch.float32).view(nb, per)
+                if sign:
+                    vals = -vals                                      # sets the sign bit, -0.0 included
+                W = torch.cat([torch.ones((nb, 1), dtype=torch.float32, device=DEV), vals], dim=1)
+                codes, _ = q.nf4_quantize(W)
+                c = codes.view(nb, 32)
+                el = torch.stack([c & 15, c >> 4], dim=2).view(nb, 64)[:, 1:].reshape(-1)[:n]
+                got = el.cpu().numpy()
+                futs.append(pool.submit(check, got, lo, hi, sign))
+                print(f"[nearest exhaustive] sign {sign:#x} bits {lo}..{hi} on the GPU", flush=True)
+                if len(futs) >= 8:
+                    results.append(futs.pop(0).result())
+        results += [f.result() for f in futs]
+    assert sum(r[6] for r in results) == 2 * total                  # every value of both halves checked
+    bad = [r for r in results if r[2]]
+    assert not bad, f"code mismatches (lo, sign, count, first, got, expected): {bad[:3]}"
+
+
+def test_e4m3fn_scale_exhaustive():
+    """Every fp32 t in [0, 1] (1,065,353,218 values) as a block scale in groups of
+    256 whose first scale is 1.0 (c1 = 1, so t = a exactly): each E4M3FN code must
+    be the oracle's round-to-nearest-even encoding."""
+    from concurrent.futures import ThreadPoolExecutor
+    import bit_quantized_lora_blockwise_amd as q
+    one = int(np.float32(1.0).view(np.uint32))
+    total = one + 1
+    per, ngrp = 255, 1 << 18
+    chunk = per * ngrp
+
+    def check(got, lo, hi):
+        exp = O.e4m3fn_encode(np.arange(lo, hi, dtype=np.uint32).view(np.float32))
+        assert got.size == exp.size == hi - lo
+        bad = np.flatnonzero(got != exp)
+        return (lo, bad.size, bad[:4], got[bad[:4]], exp[bad[:4]], exp.size)
+
+    results = []
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        futs = []
+        for lo, hi in _bit_range_chunks(total, chunk):
+            n = hi - lo
+            ng = (n + per - 1) // per
+            bits = torch.arange(lo, lo + ng * per, dtype=torch.int64, device=DEV)
+            bits = torch.where(bits < hi, bits, torch.zeros_like(bits))
+            vals = bits.to(torch.int32).view(torch.float32).view(ng, per)
+            a = torch.cat([torch.ones((ng, 1), dtype=torch.float32, device=DEV), vals], dim=1).reshape(-1)
+            c2, c1 = q.nf4_double_quant(a)
+            got = c2.view(ng, 256)[:, 1:].reshape(-1)[:n].cpu().numpy()
+            assert torch.all(c1 == 1.0)
+            futs.append(pool.submit(check, got, lo, hi))
+            print(f"[e4m3fn exhaustive] bits {lo}..{hi} on the GPU", flush=True)
+            if len(futs) >= 8:
+                results.append(futs.pop(0).result())
+        results += [f.result() for f in futs]
+    assert sum(r[5] for r in results) == total                       # every value checked
+    bad = [r for r in results if r[1]]
+    assert not bad, f"E4M3FN mismatches (lo, count, first, got, expected): {bad[:3]}"
+
+
 @pytest.mark.parametrize("rows,cols,dtype", [(512, 512, "fp32"), (11008, 4096, "bf16"), (3, 320, "fp32"),
                                              (257, 64, "bf16"), (5, 64 * 51, "bf16")])
 def test_fused_quantize_and_double_quant(rows, cols, dtype):
