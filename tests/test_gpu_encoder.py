@@ -231,6 +231,28 @@ def test_nearest_code_exhaustive():
     assert not bad, f"code mismatches (lo, sign, count, first, got, expected): {bad[:3]}"
 
 
+def test_nearest_code_all_bf16():
+    """Every bf16 n in [-1, 1] through the bf16-input encoder (blocks with absmax
+    1.0), and the same values scaled by the bf16 absmax 0.0371 rounded to bf16,
+    against the oracle (which takes the exact fp32 values of the bf16 inputs)."""
+    import bit_quantized_lora_blockwise_amd as q
+    one16 = 0x3F80
+    pos = (np.arange(0, one16 + 1, dtype=np.uint32) << 16).view(np.float32)
+    vals = np.concatenate([pos, -pos])
+    W1 = _blocks_with_absmax(vals, np.float32(1.0))
+    a = torch.tensor([0.0371]).to(torch.bfloat16).float().numpy()[0]
+    scaled = torch.from_numpy(vals * a).to(torch.bfloat16).float().numpy()
+    scaled = scaled[np.abs(scaled) <= a]
+    Wa = _blocks_with_absmax(scaled, a)
+    W = torch.from_numpy(np.concatenate([W1, Wa])).to(torch.bfloat16)
+    Wf = W.float().numpy()
+    codes, absmax = q.nf4_quantize(W.to(DEV))
+    torch.cuda.synchronize()
+    r_codes, r_absmax = O.nf4_quantize(Wf)
+    assert_bitexact(absmax.cpu().numpy().view(np.uint32), r_absmax.view(np.uint32), "bf16 sweep absmax")
+    assert_bitexact(codes.cpu().numpy(), r_codes, "bf16 sweep codes")
+
+
 def test_e4m3fn_scale_exhaustive():
     """Every fp32 t in [0, 1] (1,065,353,218 values) as a block scale in groups of
     256 whose first scale is 1.0 (c1 = 1, so t = a exactly): each E4M3FN code must
