@@ -15,6 +15,8 @@ Also reported (not part of `value`):
   * decode: packed-weight GB/s of the M = 1 forward kernel at 4096 -> 11008,
     rotating over 24 copies of the packed layer (> 512 MB) so that every call
     streams from HBM rather than the 256 MB Infinity Cache; M = 4 and 16 too;
+    and the rate of a plain streaming read of the same number of bytes (the
+    read ceiling the packed-weight rate is also compared with);
   * encode throughput over the 7 linears of one LLaMA-65B block (809.5 M weights);
   * the CPU oracle timed on a bounded sample of the headline step.
 
@@ -281,6 +283,23 @@ def decode_bench(dev, reps=200):
     res["packed_bytes"] = packed
     res["copies_rotated"] = copies
     del layers
+    # the read ceiling: one plain streaming read of the same number of bytes per
+    # call, over as many rotated copies, graph-replayed like the kernel timing
+    nbytes = (packed + 15) // 16 * 16
+    bufs = [torch.empty((nbytes,), dtype=torch.uint8, device=dev) for _ in range(copies)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.zeros((1,), dtype=torch.int32, device=dev)
+    it = [0]
+
+    def probe():
+        q.read_probe(bufs[it[0] % copies], sink)
+        it[0] += 1
+
+    pms = time_graph_launches(probe, copies * 2, max(4, reps // (copies * 2)))
+    res["read_ceiling"] = {"us": pms * 1e3, "gbps": nbytes / (pms * 1e-3) / 1e9, "bytes": nbytes,
+                           "kernel": "k_read_probe (ql_read_probe)"}
+    del bufs
     torch.cuda.empty_cache()
     return res
 
@@ -653,9 +672,11 @@ def main():
 
     dec = decode_bench(dev)
     m1 = dec["M1"]
+    ceil = dec["read_ceiling"]
     dec_roof = {"kernel": "k_qgemv_fwd", "bound": "hbm", "achieved": m1["alg_gbps"], "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": m1["alg_gbps"] / PEAK_HBM_GBPS, "traffic": None,
-                "avg_launch_us": m1["kernel_us"]}
+                "avg_launch_us": m1["kernel_us"], "read_ceiling_gbps": ceil["gbps"],
+                "packed_frac_of_read_ceiling": m1["packed_gbps"] / ceil["gbps"]}
     enc = encode_bench(dev)
     mrg = merge_bench(dev)
     study = quant_study(dev)

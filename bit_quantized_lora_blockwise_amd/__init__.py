@@ -11,5 +11,5 @@ from ._lib import (  # noqa: F401
     qlora_lora_down, qlora_linear_fwd_t, qlora_lora_grad_in, qlora_linear_dx,
     qlora_merge,
     CODEBOOKS, SCALE_CODES, q4_quantize, q4_double_quant, q4_dequantize, q4_levels,
-    qlora_group_fwd, qlora_group_bwd, qlora_adamw_step,
+    qlora_group_fwd, qlora_group_bwd, qlora_adamw_step, read_probe,
 )

@@ -27,7 +27,7 @@ EXPORTS = ("nf4_quantize", "nf4_quantize_dq", "nf4_double_quant", "nf4_dequantiz
            "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx", "qlora_merge",
            "q4_quantize", "q4_double_quant", "q4_dequantize", "q4_levels",
            "qlora_group_fwd_workspace", "qlora_group_fwd", "qlora_group_bwd_workspace", "qlora_group_bwd",
-           "qlora_adamw_step")
+           "qlora_adamw_step", "ql_read_probe")
 
 
 class QloraError(RuntimeError):
@@ -72,6 +72,7 @@ def lib():
             "qlora_group_bwd_workspace": ([I64, I64, I64, I32, I32], SZ),
             "qlora_group_bwd": ([P, P, I64, I64, I64, I32, P, P, P, P, P, I32, F32, P, P, P, P, P, SZ, P], I32),
             "qlora_adamw_step": ([P, P, P, P, P, I64, F32, F32, F32, F32, F32, I64, P], I32),
+            "ql_read_probe": ([P, I64, P, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -154,6 +155,16 @@ def nf4_double_quant(absmax, c2=None, c1=None, stream=None):
     c1 = _empty(((nb + 255) // 256,), torch.float32, absmax) if c1 is None else _need(c1, "c1", torch.float32)
     _check("nf4_double_quant", lib().nf4_double_quant(_ptr(absmax), nb, _ptr(c2), _ptr(c1), _stream(stream)))
     return c2, c1
+
+
+def read_probe(data, sink, stream=None):
+    """One streaming read of the bytes of `data` (a measurement helper: the
+    read-bandwidth ceiling for the decode forward); `sink` is an int32 [1]."""
+    _need(sink, "sink", torch.int32)
+    if not isinstance(data, torch.Tensor) or data.device.type != "cuda" or not data.is_contiguous():
+        raise ValueError("data must be a contiguous GPU tensor")
+    _check("ql_read_probe", lib().ql_read_probe(_ptr(data), data.numel() * data.element_size(), _ptr(sink),
+                                                _stream(stream)))
 
 
 def nf4_dequantize(codes, c2, c1, rows, cols, out=None, stream=None):

@@ -287,6 +287,14 @@ int qlora_group_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K,
   return QL_OK;
 }
 
+int ql_read_probe(const void* data, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!data || !sink) return QL_ERR_NULL;
+  if (bytes <= 0 || (bytes % 16) != 0 || bytes > (int64_t(1) << 40)) return QL_ERR_SHAPE;
+  if (!aligned16(data) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return QL_ERR_ALIGN;
+  QL_TRY(launch_read_probe(data, bytes, sink, (hipStream_t)stream));
+  return QL_OK;
+}
+
 int qlora_adamw_step(float* param, float* exp_avg, float* exp_avg_sq, const float* grad, uint16_t* param_bf16,
                      int64_t n, float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step,
                      void* stream) {

@@ -271,6 +271,16 @@ int q4_dequantize(const uint8_t* codes, int64_t rows, int64_t cols, int codebook
  * an unknown id).                                                               */
 int q4_levels(int codebook, float* out16);
 
+/* Measurement helper (not a step of the method): reads `bytes` bytes at the
+ * device pointer `data` once, as a plain streaming read (16-byte loads, each
+ * wave instruction covering 1 KB contiguous), so that the decode forward's
+ * packed-weight rate can be compared with the rate this GPU reaches for reading
+ * the same number of bytes.  bytes > 0 and a multiple of 16; data 16-byte
+ * aligned; sink a device pointer to one uint32 (4-byte aligned) that may receive
+ * an unspecified value.  Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_ALIGN,
+ * QL_ERR_HIP; asynchronous on `stream`.                                          */
+int ql_read_probe(const void* data, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Host-only helpers (no GPU needed). */
 /* The 16 NF4 levels (fp32, ascending) that the kernels use, copied to out[16].  */
 int qlora_nf4_levels(float* out16);

@@ -216,3 +216,14 @@ def test_fused_quantize_validation():
     assert L.nf4_quantize_dq(A, 5, 4, 64, A, None, A, A, None) == -3
     assert L.nf4_quantize_dq(A, 1, 4, 96, A, None, A, A, None) == -2
     assert L.nf4_quantize_dq(A, 1, 4, 64, A, MIS, A, A, None) == -4
+
+
+def test_read_probe_validation():
+    """The read-bandwidth probe rejects null pointers, sizes that are not a
+    positive multiple of 16 and misaligned pointers before touching the GPU."""
+    _, L = _lib()
+    assert L.ql_read_probe(None, 64, A, None) == -1
+    assert L.ql_read_probe(A, 64, None, None) == -1
+    assert L.ql_read_probe(A, 0, A, None) == -2
+    assert L.ql_read_probe(A, 40, A, None) == -2
+    assert L.ql_read_probe(MIS, 64, A, None) == -4

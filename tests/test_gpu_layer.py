@@ -265,3 +265,14 @@ def test_stage_entry_points_match_fused_calls(M):
     dX = q.qlora_linear_dx(dY, *gq, 256, G, L1)
     torch.cuda.synchronize()
     assert torch.equal(T, a["T"]) and torch.equal(Y, a["Y"]) and torch.equal(dX, a["dX"])
+
+
+def test_read_probe_runs():
+    """The read-bandwidth probe (a measurement helper) reads a buffer whose XOR is
+    not its trigger word, so the sink keeps its value; a ragged tail is accepted."""
+    q = qlib()
+    buf = torch.zeros((1 << 20) + 48, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    q.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
