@@ -72,6 +72,7 @@ def test_config1_full():
 RAGGED = [
     (37, 192, 200, 5), (17, 64, 33, 1), (130, 256, 136, 16), (64, 320, 96, 64), (200, 128, 260, 24),
     (1, 128, 50, 3), (2, 64, 8, 64), (3, 192, 77, 7), (4, 256, 130, 12), (16, 512, 260, 64), (15, 64, 129, 33),
+    (257, 320, 300, 64), (300, 1088, 520, 13),
 ]
 
 
