@@ -105,19 +105,20 @@ class Linear:
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_qgemm_llama7b_m4096.md")
 GEMM_SOURCE = os.path.join(ROOT, "bit_quantized_lora_blockwise_amd", "csrc", "gemm_big.hip")
+DECODE_SOURCE = os.path.join(ROOT, "bit_quantized_lora_blockwise_amd", "csrc", "decode.hip")
 
 
-def recorded_traffic(kernel):
+def recorded_traffic(kernel, source=GEMM_SOURCE):
     """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
-    summary, or None when the GEMM source has changed since those counters were
-    taken (the summary records the source's sha256)."""
+    summary, or None when the kernel's source file has changed since those
+    counters were taken (the summary records each source's sha256)."""
     import hashlib
     try:
         text = open(TRAFFIC_PROFILE).read()
-        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
     except OSError:
         return None
-    if f"gemm_big.hip sha256 {sha}" not in text:
+    if f"{os.path.basename(source)} sha256 {sha}" not in text:
         return None
     for line in text.splitlines():
         parts = line.split()
@@ -591,8 +592,9 @@ def cpu_baseline(min_seconds=10.0, max_passes=4):
 
 def pmc_probe(lins, reps=3):
     """Launches for hardware-counter runs: fused forward and dX GEMMs of both
-    headline linears, then one copy of 512 MiB (bytes read = bytes written =
-    2^29), the known-size reference for the traffic counters."""
+    headline linears, the M = 1 decode forward at 4096 -> 11008 (T given), then
+    one copy of 512 MiB (bytes read = bytes written = 2^29), the known-size
+    reference for the traffic counters."""
     import torch
     q = lins[0].q
     for L in lins:
@@ -602,13 +604,20 @@ def pmc_probe(lins, reps=3):
         for L in lins:
             q.qlora_linear_fwd_t(L.X, L.codes, L.c2, L.c1, L.N, L.T, L.L2, 1.0, Y=L.Y)
             q.qlora_linear_dx(L.dY, L.codes, L.c2, L.c1, L.K, L.G, L.L1, dX=L.dX)
+    up = lins[0]
+    X1 = up.X[:1].contiguous()
+    T1 = q.qlora_lora_down(X1, up.L1)
+    Y1 = torch.empty((1, up.N), dtype=torch.bfloat16, device=X1.device)
+    for _ in range(reps):
+        q.qlora_linear_fwd_t(X1, up.codes, up.c2, up.c1, up.N, T1, up.L2, 1.0, Y=Y1)
     torch.cuda.synchronize()
     src = torch.empty((1 << 28,), dtype=torch.int16, device=lins[0].X.device).fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_probe": "done", "gemm_launches_per_kind": reps * len(lins), "copy_bytes": 1 << 29}))
+    print(json.dumps({"pmc_probe": "done", "gemm_launches_per_kind": reps * len(lins), "decode_launches": reps,
+                      "copy_bytes": 1 << 29}))
 
 
 def main():
@@ -674,7 +683,8 @@ def main():
     m1 = dec["M1"]
     ceil = dec["read_ceiling"]
     dec_roof = {"kernel": "k_qgemv_fwd", "bound": "hbm", "achieved": m1["alg_gbps"], "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": m1["alg_gbps"] / PEAK_HBM_GBPS, "traffic": None,
+                "unit": "GB/s", "frac": m1["alg_gbps"] / PEAK_HBM_GBPS,
+                "traffic": recorded_traffic("k_qgemv_fwd", DECODE_SOURCE),
                 "avg_launch_us": m1["kernel_us"], "read_ceiling_gbps": ceil["gbps"],
                 "packed_frac_of_read_ceiling": m1["packed_gbps"] / ceil["gbps"]}
     enc = encode_bench(dev)
