@@ -321,3 +321,22 @@ def test_fused_quantize_and_double_quant(rows, cols, dtype):
         assert_bitexact(codes.cpu().numpy(), rc, "fused codes")
         assert_bitexact(c2.cpu().numpy(), rc2, "fused c2")
         assert_bitexact(c1.cpu().numpy().view(np.uint32), rc1.view(np.uint32), "fused c1")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fused_encoder_edge_cases(dtype):
+    """The one-pass encoder with double quantization on the edge-case matrix
+    (zero blocks, codebook values x 2^e up to both ends of the normal range,
+    midpoint neighbours, subnormals, signed zeros, large magnitudes): codes, c2
+    and c1 equal the oracle's bit for bit."""
+    import bit_quantized_lora_blockwise_amd as q
+    W = torch.from_numpy(_edge_matrix())
+    if dtype == "bf16":
+        W = W.to(torch.bfloat16)
+    codes, c2, c1, _ = q.nf4_quantize_dq(W.to(DEV))
+    torch.cuda.synchronize()
+    rc, ra = O.nf4_quantize(W.float().numpy())
+    rc2, rc1 = O.nf4_double_quant(ra)
+    assert_bitexact(codes.cpu().numpy(), rc, f"fused edge codes {dtype}")
+    assert_bitexact(c2.cpu().numpy(), rc2, f"fused edge c2 {dtype}")
+    assert_bitexact(c1.cpu().numpy().view(np.uint32), rc1.view(np.uint32), f"fused edge c1 {dtype}")
