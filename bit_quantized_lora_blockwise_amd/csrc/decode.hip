@@ -362,14 +362,15 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
 }
 
 // ---------------------------------------------------------------------------
-// X of 32 to 128 KB (e.g. M = 16 at K = 4096): one persistent work group of 16
+// X of 32 to 128 KB (e.g. M = 16 at K = 4096): one persistent work group of 8
 // waves per CU stages all of X in LDS once (the same column order as above) and
 // then takes 16-row tiles blockIdx.x, blockIdx.x + gridDim.x, ...; the waves
 // split each tile's K as above.  A wave's (tile, step) items form one stream
 // with the next item's codes in flight while the current one is converted, so
 // the first step of the next tile is requested before the current tile's
 // partial sums are added.  Per-work-group X reads in 16-byte pieces (the path
-// above for larger X) are replaced by one staging pass per CU.
+// above for larger X) are replaced by one staging pass per CU.  Eight waves
+// (two steps each per tile at K = 4096) measured 3-11% ahead of sixteen (one).
 constexpr int kXPersistBytes = 131072;
 
 // One item of a wave's stream: its block's codes and scales.  The scale byte is
@@ -381,14 +382,14 @@ struct PStep {
 };
 
 template <bool kTPart>
-__global__ __launch_bounds__(1024) void k_qgemv_persist(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+__global__ __launch_bounds__(512) void k_qgemv_persist(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         int64_t N, int64_t ld, const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ c2,
                                                         const float* __restrict__ c1, uint16_t* __restrict__ T,
                                                         const float* __restrict__ Tp, int S,
                                                         const uint16_t* __restrict__ L2, int r, float scale,
                                                         uint16_t* __restrict__ Y, Nf4Params p) {
-  constexpr int kWv = 16, kThr = 1024, kXPer = kXPersistBytes / (16 * kThr);
+  constexpr int kWv = 8, kThr = 512, kXPer = kXPersistBytes / (16 * kThr);
   __shared__ __attribute__((aligned(16))) uint8_t lds[kXPersistBytes + kZeroBytes + kWv * 64 * 16];
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
@@ -530,7 +531,7 @@ __global__ __launch_bounds__(1024) void k_qgemv_persist(const uint16_t* __restri
 
   f32x4* red = (f32x4*)(lds + kXPersistBytes + kZeroBytes);
   f32x4 acc = {0, 0, 0, 0};
-  // tile j done by this wave: LoRA term, partial sums of the 16 waves added in
+  // tile j done by this wave: LoRA term, partial sums of the 8 waves added in
   // LDS in a fixed order, output row written; the next tile's L2 fragment requested
   auto finish_tile = [&](int64_t j) {
     // the two bf16 pairs of the L2 fragment, formed here: the empty volatile asm
@@ -663,7 +664,7 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
     hipError_t e;
     if (xpersist) {
       const unsigned pg = (unsigned)(wgs < cus ? wgs : cus);
-      hipLaunchKernelGGL((k_qgemv_persist<kTPart>), dim3(pg), dim3(1024), 0, s, a.X, a.M, a.K, a.rows, a.ld, a.codes,
+      hipLaunchKernelGGL((k_qgemv_persist<kTPart>), dim3(pg), dim3(512), 0, s, a.X, a.M, a.K, a.rows, a.ld, a.codes,
                          a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params());
       e = hipGetLastError();
     } else if (xlds)
