@@ -21,8 +21,9 @@
 // the MFMA needs no re-interleaving of the looked-up values.  The staging is
 // finished before the code stream is requested, so the first steps do not wait
 // for X behind the stream.  X of 32 to 128 KB goes to a persistent kernel that
-// stages it in LDS once per CU and walks 16-row tiles in turn; larger X is read
-// from global memory together with the step's codes.
+// stages it in LDS once per CU and walks 16-row tiles in turn; larger X is staged
+// slice by slice when there is at most one tile per CU, and otherwise read from
+// global memory together with the step's codes.
 #include "kernels.h"
 
 namespace {
@@ -593,6 +594,202 @@ __global__ __launch_bounds__(512) void k_qgemv_persist(const uint16_t* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// X above 128 KB with at most one 16-row tile per CU (e.g. M = 16 at 11008 -> 4096):
+// one work group of 8 waves per tile stages X in LDS slice by slice (ksl
+// columns at a time, a multiple of 4096, so that each wave has an even number
+// of steps per slice) and walks the slice's steps as above; the next step's
+// codes are in flight across slice changes.  The tile is finished after the last
+// slice, by every wave at the same point.
+template <bool kTPart>
+__global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                      int64_t N, int64_t ld, const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ c2,
+                                                      const float* __restrict__ c1, uint16_t* __restrict__ T,
+                                                      const float* __restrict__ Tp, int S,
+                                                      const uint16_t* __restrict__ L2, int r, float scale,
+                                                      uint16_t* __restrict__ Y, int64_t ksl, Nf4Params p) {
+  constexpr int kWv = 8, kThr = 512, kXPer = kXPersistBytes / (16 * kThr);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kXPersistBytes + kZeroBytes + kWv * 64 * 16];
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int g = l >> 4, col = l & 15;
+  const bool m_ok = col < M;
+  const uint32_t kblocks = (uint32_t)(K / qk::kBlock);
+  const uint32_t nrow = blockIdx.x * kRows + (uint32_t)col;
+  const bool row_ok = nrow < (uint32_t)N;
+  SplitConst kc;
+  asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
+  asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
+  const uint32_t nsteps = (kblocks + 3) / 4;
+  const uint32_t nst = nsteps > (uint32_t)w ? (nsteps - (uint32_t)w + kWv - 1) / kWv : 0u;   // uniform
+  const uint32_t kb0 = 4u * (uint32_t)w + (uint32_t)g;
+  const uint32_t kbstep = 4u * kWv;
+  const uint32_t per_slice = (uint32_t)(ksl / (256 * kWv));     // steps of a wave per slice (even)
+  const int nsl = (int)((K + ksl - 1) / ksl);
+
+  const __amdgpu_buffer_rsrc_t rc = rsrc(codes, (uint64_t)N * (K / 2));
+  const __amdgpu_buffer_rsrc_t r2 = rsrc(c2, (uint64_t)N * kblocks);
+  const __amdgpu_buffer_rsrc_t r1 = rsrc(c1, 4 * (((uint64_t)N * kblocks + 255) / 256));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(X, (uint64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rl = rsrc(L2, 2 * ((uint64_t)(r - 1) * ld + N));
+  LDS_AS uint8_t* xl = (LDS_AS uint8_t*)lds;
+
+  // slice sl of X: row m's columns [sl ksl, sl ksl + ksl) at m ksl * 2 bytes; chunk
+  // c of the thread-linear order holds row c / (ksl / 8), columns 8 (c % (ksl / 8)) ..
+  const uint32_t cpr = (uint32_t)(ksl / 8);                       // 16-byte chunks per row
+  const uint32_t nchunk = (uint32_t)M * cpr;
+  auto load_x = [&](int sl, u32x4 (&xr)[kXPer]) {
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j) {
+      const uint32_t c = (uint32_t)(t + j * kThr);
+      const uint32_t m = c / cpr, cg = c - m * cpr;
+      const int64_t kc0 = (int64_t)sl * ksl + 8 * (int64_t)cg;
+      const bool ok = c < nchunk && kc0 < K;
+      xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)((m * K + kc0) * 2) : kOOB, 0, 0);
+    }
+  };
+  auto store_x = [&](const u32x4 (&xr)[kXPer]) {
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j) {
+      const uint32_t c = (uint32_t)(t + j * kThr);
+      const u32x4 v = xr[j];
+      u32x4 e;
+      e[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+      e[1] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+      e[2] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+      e[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+      if (c < nchunk) *(LDS_AS u32x4*)(xl + 16 * c) = e;
+    }
+  };
+  u32x4 xr[kXPer];
+  load_x(0, xr);
+  const int rb = 16 * w + 4 * g;                   // first of this lane's four LoRA ranks
+  const bool t_ok = rb < r && m_ok;
+  f32x4 ps[kTPart ? kDecodeTSlices : 1];
+  uint16_t vt16[4], vl[4];
+  if (!kTPart) {
+    const __amdgpu_buffer_rsrc_t rt = rsrc(T, 2 * (uint64_t)M * r);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t ot = (rb + q < r && m_ok) ? (uint32_t)(2 * (col * r + rb + q)) : kOOB;
+      vt16[q] = __builtin_amdgcn_raw_buffer_load_b16(rt, ot, 0, 0);
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rp = rsrc(Tp, 4 * (uint64_t)S * M * r);
+#pragma unroll
+    for (int s = 0; s < kDecodeTSlices; ++s)
+      ps[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rp, (t_ok && s < S) ? (uint32_t)(4 * (((int64_t)s * M + col) * r + rb)) : kOOB,
+                                            0, 0));
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t ol = (rb + q < r && row_ok) ? (uint32_t)(2 * ((int64_t)(rb + q) * ld + nrow)) : kOOB;
+    vl[q] = __builtin_amdgcn_raw_buffer_load_b16(rl, ol, 0, 0);
+  }
+  // row offsets before the code stream, opaque (see the main kernel)
+  uint32_t blk_row = nrow * kblocks;
+  asm volatile("" : "+v"(blk_row));
+  __builtin_amdgcn_sched_barrier(0);
+  auto load_item = [&](uint32_t i, PStep& st) {     // step i of this wave (past nst: zeros)
+    const uint32_t kb = kb0 + i * kbstep;
+    const bool ok = i < nst && row_ok && kb < kblocks;
+    const uint32_t b = blk_row + kb;
+    const uint32_t co = ok ? 32u * b : kOOB;
+    st.cw[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
+    st.cw[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, co + 16, 0, 0);
+    st.c2b = __builtin_amdgcn_raw_buffer_load_b8(r2, ok ? b : kOOB, 0, 0);
+    st.c1v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ok ? 4 * (b >> 8) : kOOB, 0, 0));
+  };
+  PStep sa, sb;
+  load_item(0, sa);
+
+  uint32_t lt[2];
+  {
+    uint32_t vt[4];
+    if (kTPart) {
+      f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < kDecodeTSlices; ++s)
+        if (s < S) sum += ps[s];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vt[q] = qk::f32_to_bf16(sum[q]);
+      if (T && blockIdx.x == 0 && t_ok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) T[col * r + rb + q] = (uint16_t)vt[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vt[q] = vt16[q];
+    }
+    lt[0] = vt[0] | (vt[1] << 16);
+    lt[1] = vt[2] | (vt[3] << 16);
+  }
+  store_x(xr);
+  if (t < kZeroBytes / 16) *(LDS_AS u32x4*)(xl + kXPersistBytes + 16 * t) = u32x4{0, 0, 0, 0};
+  __syncthreads();
+
+  f32x4 acc = {0, 0, 0, 0};
+  auto process = [&](uint32_t i, int sl, const PStep& st) {
+    const uint32_t kb = kb0 + i * kbstep;
+    const BlockLut L = make_lut(qk::e4m3fn_to_f32(st.c2b) * st.c1v, p);
+    const bool xok = m_ok && kb < kblocks && i < nst;
+    const uint32_t kl = kb - (uint32_t)sl * (uint32_t)(ksl / 64);  // block within the slice
+    const LDS_AS u32x4* xs = (const LDS_AS u32x4*)(xl + (xok ? ((uint32_t)col * (uint32_t)ksl + 64u * kl) * 2u
+                                                             : (uint32_t)kXPersistBytes));
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const u32x4 bv = dequant8_eo(L, st.cw[d >> 2][d & 3], kc);
+      acc = mfma16(__builtin_bit_cast(bf16x8, xs[d]), __builtin_bit_cast(bf16x8, bv), acc);
+    }
+  };
+  for (int sl = 0; sl < nsl; ++sl) {
+    if (sl > 0) {
+      load_x(sl, xr);
+      __syncthreads();                             // every wave is done with slice sl - 1
+      store_x(xr);
+      __syncthreads();
+    }
+    // this wave's steps of the slice, in pairs (per_slice is even); the pair
+    // after the slice's last is already requested into sa
+    const uint32_t i_end = (uint32_t)(sl + 1) * per_slice;
+    for (uint32_t i = (uint32_t)sl * per_slice; i < i_end; i += 2) {
+      load_item(i + 1, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      process(i, sl, sa);
+      load_item(i + 2, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      process(i + 1, sl, sb);
+    }
+  }
+
+  // the tile: LoRA term, the 8 waves' partial sums added in a fixed order
+  f32x4* red = (f32x4*)(lds + kXPersistBytes + kZeroBytes);
+  {
+    uint16_t a0 = vl[0], a1 = vl[1], a2 = vl[2], a3 = vl[3];
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    const uint32_t ll0 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+    const uint32_t ll1 = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+    f32x4 zl = {0, 0, 0, 0};
+    zl = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{lt[0], lt[1]}),
+                                                   __builtin_bit_cast(s16x4, u32x2{ll0, ll1}), zl, 0, 0, 0);
+    acc += scale * zl;
+  }
+  red[w * 64 + l] = acc;
+  __syncthreads();
+  if (w == 0) {
+    f32x4 sum = red[l];
+#pragma unroll
+    for (int ww = 1; ww < kWv; ++ww) sum += red[ww * 64 + l];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (m < M && row_ok) Y[(int64_t)m * ld + nrow] = qk::f32_to_bf16(sum[i]);
+    }
+  }
+}
+
 // One launch's operands besides the shape and the grid.
 struct QgemvArgs {
   const uint16_t* X;
@@ -640,7 +837,7 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
   const bool xlds = M * K * 2 <= kXBytes;
   const bool xpersist = !xlds && M * K * 2 <= kXPersistBytes;
   int cus = 0;
-  if (xpersist) {
+  if (!xlds) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                 hipSuccess || cus < 1)
@@ -662,7 +859,12 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
     // would leave SIMDs with fewer than two waves, else 4
     const bool wide = wgs <= 384;
     hipError_t e;
-    if (xpersist) {
+    const int64_t ksl = (kXPersistBytes / (2 * M)) / 4096 * 4096;   // slice width: a multiple of 4096 columns
+    if (!xlds && !xpersist && wgs <= cus && ksl >= 4096) {
+      hipLaunchKernelGGL((k_qgemv_slices<kTPart>), dim3((unsigned)wgs), dim3(512), 0, s, a.X, a.M, a.K, a.rows, a.ld,
+                         a.codes, a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, ksl, nf4_params());
+      e = hipGetLastError();
+    } else if (xpersist) {
       const unsigned pg = (unsigned)(wgs < cus ? wgs : cus);
       hipLaunchKernelGGL((k_qgemv_persist<kTPart>), dim3(pg), dim3(512), 0, s, a.X, a.M, a.K, a.rows, a.ld, a.codes,
                          a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params());

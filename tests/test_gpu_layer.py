@@ -134,8 +134,8 @@ def test_decode_llama7b_up_full(M):
 def test_decode_llama7b_down_full(M):
     """Decode-sized forward at the 11008 -> 4096 shape (few work groups, so the
     kernel splits K over more waves; X staged in LDS per work group at M = 1, once
-    per CU by the persistent kernel at M = 4, read from global memory at M = 16),
-    every output compared."""
+    per CU by the persistent kernel at M = 4, slice by slice at M = 16), every
+    output compared."""
     inp = WL.layer_inputs(4096, 11008, M, 64, seed_base=7100 + M)
     print(f"[decode] M={M} K=11008 N=4096", flush=True)
     q = qlib()
