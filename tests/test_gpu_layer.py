@@ -217,6 +217,29 @@ def test_decode_persistent_given_T(M, K, N, r):
     assert_close(bits(Y), rY, f"decode persistent given T: Y M={M} K={K} r={r}")
 
 
+# the slice-staged decode kernel (X above 128 KB, at most one 16-row tile per CU):
+# M odd, N not a multiple of 16, a rank that is not a multiple of 4, a last slice
+# of 128 columns; and three full slices
+DECODE_SLICES = [(11, 8320, 1000, 13), (16, 12288, 2048, 64)]
+
+
+@pytest.mark.parametrize("M,K,N,r", DECODE_SLICES)
+def test_decode_slices(M, K, N, r):
+    assert M * K * 2 > 131072
+    inp = WL.layer_inputs(N, K, M, r, seed_base=M * 23 + K + N * 5 + r, l2_std=0.3)
+    full_case(inp, 0.9, "decode slices")
+    q = qlib()
+    gq, rq = quantize_both(inp["W"])
+    X, L1, L2 = (inp[k].to(DEV) for k in ("X", "L1", "L2"))
+    T = q.qlora_lora_down(X, L1)
+    Y = q.qlora_linear_fwd_t(X, *gq, N, T, L2, 0.9)
+    torch.cuda.synchronize()
+    Wq = O.nf4_dequantize(*rq, N, K)
+    rY, rT = O.qlora_forward(bits(inp["X"]), Wq, bits(inp["L1"]), bits(inp["L2"]), 0.9)
+    assert_close(bits(T), rT, f"decode slices given T: T M={M} K={K} r={r}")
+    assert_close(bits(Y), rY, f"decode slices given T: Y M={M} K={K} r={r}")
+
+
 def _sampled_case(inp, name, n_rows=48, seed=0):
     """Full-size check: dL1, dL2 and T in full; Y and dX on sampled rows."""
     N, K = inp["W"].shape
