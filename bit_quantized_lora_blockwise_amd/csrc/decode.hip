@@ -595,13 +595,14 @@ __global__ __launch_bounds__(512) void k_qgemv_persist(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// X above 128 KB with at most one 16-row tile per CU (e.g. M = 16 at 11008 -> 4096):
-// one work group of 8 waves per tile stages X in LDS slice by slice (ksl
-// columns at a time, a multiple of 4096, so that each wave has an even number
-// of steps per slice) and walks the slice's steps as above; the next step's
-// codes are in flight across slice changes.  The tile is finished after the last
-// slice, by every wave at the same point.
-template <bool kTPart>
+// X above 128 KB (e.g. M = 16 at 11008 -> 4096, or at 8192 -> 22016): one work
+// group of 8 waves per CU stages X in LDS slice by slice (ksl columns at a time,
+// a multiple of 4096, so that each wave has an even number of steps per slice)
+// and, for each of its tiles b, b + G, .. (at most kT; G work groups), walks the
+// slice's steps as above into that tile's own accumulator.  The next item's
+// codes are in flight across tile and slice changes.  The tiles are finished
+// after the last slice, by every wave at the same points.
+template <int kT, bool kTPart>
 __global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                       int64_t N, int64_t ld, const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ c2,
@@ -616,8 +617,12 @@ __global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict
   const int g = l >> 4, col = l & 15;
   const bool m_ok = col < M;
   const uint32_t kblocks = (uint32_t)(K / qk::kBlock);
-  const uint32_t nrow = blockIdx.x * kRows + (uint32_t)col;
-  const bool row_ok = nrow < (uint32_t)N;
+  const uint32_t ntiles = (uint32_t)((N + kRows - 1) / kRows);
+  // 1 .. kT (the grid has at most ntiles work groups); a constant for kT = 1,
+  // so that no branch surrounds that kernel's step loop
+  const uint32_t my_tiles = kT == 1 ? 1u : (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const uint32_t nrow0 = blockIdx.x * kRows + (uint32_t)col;          // this lane's row in its first tile
+  const uint32_t trows = gridDim.x * kRows;                           // rows from one of its tiles to the next
   SplitConst kc;
   asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
   asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
@@ -667,7 +672,7 @@ __global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict
   const int rb = 16 * w + 4 * g;                   // first of this lane's four LoRA ranks
   const bool t_ok = rb < r && m_ok;
   f32x4 ps[kTPart ? kDecodeTSlices : 1];
-  uint16_t vt16[4], vl[4];
+  uint16_t vt16[4], vl[kT][4];
   if (!kTPart) {
     const __amdgpu_buffer_rsrc_t rt = rsrc(T, 2 * (uint64_t)M * r);
 #pragma unroll
@@ -684,18 +689,23 @@ __global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict
                                             0, 0));
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t ol = (rb + q < r && row_ok) ? (uint32_t)(2 * ((int64_t)(rb + q) * ld + nrow)) : kOOB;
-    vl[q] = __builtin_amdgcn_raw_buffer_load_b16(rl, ol, 0, 0);
+  for (int jt = 0; jt < kT; ++jt) {
+    const uint32_t nrow = nrow0 + (uint32_t)jt * trows;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t ol = (rb + q < r && nrow < (uint32_t)N) ? (uint32_t)(2 * ((int64_t)(rb + q) * ld + nrow)) : kOOB;
+      vl[jt][q] = __builtin_amdgcn_raw_buffer_load_b16(rl, ol, 0, 0);
+    }
   }
   // row offsets before the code stream, opaque (see the main kernel)
-  uint32_t blk_row = nrow * kblocks;
+  uint32_t blk_row = nrow0 * kblocks;
   asm volatile("" : "+v"(blk_row));
+  const uint32_t tblk = trows * kblocks;           // blocks from one tile's row to the next tile's
   __builtin_amdgcn_sched_barrier(0);
-  auto load_item = [&](uint32_t i, PStep& st) {     // step i of this wave (past nst: zeros)
+  auto load_item = [&](uint32_t jn, uint32_t i, PStep& st) {   // tile jn's step i of this wave (past nst: zeros)
     const uint32_t kb = kb0 + i * kbstep;
-    const bool ok = i < nst && row_ok && kb < kblocks;
-    const uint32_t b = blk_row + kb;
+    const bool ok = i < nst && nrow0 + jn * trows < (uint32_t)N && kb < kblocks;
+    const uint32_t b = blk_row + jn * tblk + kb;
     const uint32_t co = ok ? 32u * b : kOOB;
     st.cw[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
     st.cw[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, co + 16, 0, 0);
@@ -703,7 +713,7 @@ __global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict
     st.c1v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ok ? 4 * (b >> 8) : kOOB, 0, 0));
   };
   PStep sa, sb;
-  load_item(0, sa);
+  load_item(0, 0, sa);
 
   uint32_t lt[2];
   {
@@ -730,8 +740,10 @@ __global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict
   if (t < kZeroBytes / 16) *(LDS_AS u32x4*)(xl + kXPersistBytes + 16 * t) = u32x4{0, 0, 0, 0};
   __syncthreads();
 
-  f32x4 acc = {0, 0, 0, 0};
-  auto process = [&](uint32_t i, int sl, const PStep& st) {
+  f32x4 acc[kT];
+#pragma unroll
+  for (int jt = 0; jt < kT; ++jt) acc[jt] = f32x4{0, 0, 0, 0};
+  auto process = [&](f32x4& ac, uint32_t i, int sl, const PStep& st) {
     const uint32_t kb = kb0 + i * kbstep;
     const BlockLut L = make_lut(qk::e4m3fn_to_f32(st.c2b) * st.c1v, p);
     const bool xok = m_ok && kb < kblocks && i < nst;
@@ -741,7 +753,7 @@ __global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const u32x4 bv = dequant8_eo(L, st.cw[d >> 2][d & 3], kc);
-      acc = mfma16(__builtin_bit_cast(bf16x8, xs[d]), __builtin_bit_cast(bf16x8, bv), acc);
+      ac = mfma16(__builtin_bit_cast(bf16x8, xs[d]), __builtin_bit_cast(bf16x8, bv), ac);
     }
   };
   for (int sl = 0; sl < nsl; ++sl) {
@@ -751,41 +763,56 @@ __global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict
       store_x(xr);
       __syncthreads();
     }
-    // this wave's steps of the slice, in pairs (per_slice is even); the pair
-    // after the slice's last is already requested into sa
-    const uint32_t i_end = (uint32_t)(sl + 1) * per_slice;
-    for (uint32_t i = (uint32_t)sl * per_slice; i < i_end; i += 2) {
-      load_item(i + 1, sb);
-      __builtin_amdgcn_sched_barrier(0);
-      process(i, sl, sa);
-      load_item(i + 2, sa);
-      __builtin_amdgcn_sched_barrier(0);
-      process(i + 1, sl, sb);
+    // for each tile, this wave's steps of the slice in pairs (per_slice is
+    // even); the item after a tile's last is the next tile's first of the
+    // slice, or tile 0's first of the next slice, already requested into sa
+    const uint32_t i0 = (uint32_t)sl * per_slice, i_end = i0 + per_slice;
+#pragma unroll
+    for (int jt = 0; jt < kT; ++jt) {
+      if ((uint32_t)jt < my_tiles) {
+        const bool last_t = (uint32_t)jt + 1 >= my_tiles;
+        const uint32_t nj = last_t ? 0u : (uint32_t)jt + 1, ni = last_t ? i_end : i0;
+        for (uint32_t i = i0; i < i_end; i += 2) {
+          load_item((uint32_t)jt, i + 1, sb);
+          __builtin_amdgcn_sched_barrier(0);
+          process(acc[jt], i, sl, sa);
+          const bool wrap = i + 2 >= i_end;
+          load_item(wrap ? nj : (uint32_t)jt, wrap ? ni : i + 2, sa);
+          __builtin_amdgcn_sched_barrier(0);
+          process(acc[jt], i + 1, sl, sb);
+        }
+      }
     }
   }
 
-  // the tile: LoRA term, the 8 waves' partial sums added in a fixed order
+  // each tile: LoRA term, the 8 waves' partial sums added in a fixed order
   f32x4* red = (f32x4*)(lds + kXPersistBytes + kZeroBytes);
-  {
-    uint16_t a0 = vl[0], a1 = vl[1], a2 = vl[2], a3 = vl[3];
-    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
-    const uint32_t ll0 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-    const uint32_t ll1 = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-    f32x4 zl = {0, 0, 0, 0};
-    zl = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{lt[0], lt[1]}),
-                                                   __builtin_bit_cast(s16x4, u32x2{ll0, ll1}), zl, 0, 0, 0);
-    acc += scale * zl;
-  }
-  red[w * 64 + l] = acc;
-  __syncthreads();
-  if (w == 0) {
-    f32x4 sum = red[l];
 #pragma unroll
-    for (int ww = 1; ww < kWv; ++ww) sum += red[ww * 64 + l];
+  for (int jt = 0; jt < kT; ++jt) {
+    if ((uint32_t)jt < my_tiles) {
+      uint16_t a0 = vl[jt][0], a1 = vl[jt][1], a2 = vl[jt][2], a3 = vl[jt][3];
+      asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+      const uint32_t ll0 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+      const uint32_t ll1 = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+      f32x4 zl = {0, 0, 0, 0};
+      zl = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{lt[0], lt[1]}),
+                                                     __builtin_bit_cast(s16x4, u32x2{ll0, ll1}), zl, 0, 0, 0);
+      f32x4 a = acc[jt];
+      a += scale * zl;
+      red[w * 64 + l] = a;
+      __syncthreads();
+      const uint32_t nrow = nrow0 + (uint32_t)jt * trows;
+      if (w == 0) {
+        f32x4 sum = red[l];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * g + i;
-      if (m < M && row_ok) Y[(int64_t)m * ld + nrow] = qk::f32_to_bf16(sum[i]);
+        for (int ww = 1; ww < kWv; ++ww) sum += red[ww * 64 + l];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * g + i;
+          if (m < M && nrow < (uint32_t)N) Y[(int64_t)m * ld + nrow] = qk::f32_to_bf16(sum[i]);
+        }
+      }
+      __syncthreads();                             // red is reused by the next tile
     }
   }
 }
@@ -805,6 +832,23 @@ struct QgemvArgs {
   float scale;
   uint16_t* Y;
 };
+
+template <bool kTPart>
+hipError_t launch_slices(int kt, unsigned grid, int64_t ksl, hipStream_t s, const QgemvArgs& a) {
+#define QL_SLICES(KT)                                                                                              \
+  hipLaunchKernelGGL((k_qgemv_slices<KT, kTPart>), dim3(grid), dim3(512), 0, s, a.X, a.M, a.K, a.rows, a.ld, a.codes, \
+                     a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, ksl, nf4_params())
+  if (kt <= 1)
+    QL_SLICES(1);
+  else if (kt <= 2)
+    QL_SLICES(2);
+  else if (kt <= 4)
+    QL_SLICES(4);
+  else
+    QL_SLICES(8);
+#undef QL_SLICES
+  return hipGetLastError();
+}
 
 template <bool kXLds, int kWv, int kXPer, bool kTPart>
 hipError_t launch_one(dim3 grid, hipStream_t s, const QgemvArgs& a) {
@@ -859,11 +903,16 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
     // would leave SIMDs with fewer than two waves, else 4
     const bool wide = wgs <= 384;
     hipError_t e;
-    const int64_t ksl = (kXPersistBytes / (2 * M)) / 4096 * 4096;   // slice width: a multiple of 4096 columns
-    if (!xlds && !xpersist && wgs <= cus && ksl >= 4096) {
-      hipLaunchKernelGGL((k_qgemv_slices<kTPart>), dim3((unsigned)wgs), dim3(512), 0, s, a.X, a.M, a.K, a.rows, a.ld,
-                         a.codes, a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, ksl, nf4_params());
-      e = hipGetLastError();
+    // X above 128 KB: the slice kernel, one work group per CU (cus >= 1 here)
+    // with at most tpw tiles each, slices a multiple of 4096 columns wide.
+    // Several tiles per work group are measured ahead of X read from global
+    // memory from M = 6 (8192 <-> 22016), behind it at M = 4.
+    const bool big = !xlds && !xpersist;
+    const int64_t ksl = big ? (kXPersistBytes / (2 * M)) / 4096 * 4096 : 0;
+    const int64_t sg = big ? (wgs < cus ? wgs : cus) : 1;
+    const int64_t tpw = (wgs + sg - 1) / sg;
+    if (big && ksl >= 4096 && (tpw == 1 || (tpw <= 8 && M >= 6))) {
+      e = launch_slices<kTPart>((int)tpw, (unsigned)sg, ksl, s, a);
     } else if (xpersist) {
       const unsigned pg = (unsigned)(wgs < cus ? wgs : cus);
       hipLaunchKernelGGL((k_qgemv_persist<kTPart>), dim3(pg), dim3(512), 0, s, a.X, a.M, a.K, a.rows, a.ld, a.codes,

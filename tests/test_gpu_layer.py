@@ -220,7 +220,11 @@ def test_decode_persistent_given_T(M, K, N, r):
 # the slice-staged decode kernel (X above 128 KB, at most one 16-row tile per CU):
 # M odd, N not a multiple of 16, a rank that is not a multiple of 4, a last slice
 # of 128 columns; and three full slices
-DECODE_SLICES = [(11, 8320, 1000, 13), (16, 12288, 2048, 64)]
+# one tile per work group; then more 16-row tiles than the 256 CUs of an MI355X,
+# so that each work group keeps 2, 3 or 5 tiles' sums across the slices (the
+# last slice 256, 2304, 4096 or 64 columns wide)
+DECODE_SLICES = [(11, 8320, 1000, 13), (16, 12288, 2048, 64),
+                 (16, 4352, 12000, 64), (11, 6400, 9000, 13), (6, 12288, 4200, 16), (16, 4160, 16400, 64)]
 
 
 @pytest.mark.parametrize("M,K,N,r", DECODE_SLICES)
