@@ -285,21 +285,35 @@ def decode_bench(dev, reps=200):
     res["copies_rotated"] = copies
     del layers
     # the read ceiling: one plain streaming read of the same number of bytes per
-    # call, over as many rotated copies, graph-replayed like the kernel timing
+    # call, over as many rotated copies, graph-replayed like the kernel timing;
+    # every load depth of the probe is tried and the fastest is the ceiling
+    import bit_quantized_lora_blockwise_amd.probe as P
     nbytes = (packed + 15) // 16 * 16
     bufs = [torch.empty((nbytes,), dtype=torch.uint8, device=dev) for _ in range(copies)]
     for b in bufs:
         b.fill_(1)
     sink = torch.zeros((1,), dtype=torch.int32, device=dev)
-    it = [0]
+    by_loads = {}
+    for loads in (1, 2, 4, 8, 16):
+        it = [0]
 
-    def probe():
-        q.read_probe(bufs[it[0] % copies], sink)
-        it[0] += 1
+        def probe(loads=loads):
+            P.read_probe(bufs[it[0] % copies], sink, loads)
+            it[0] += 1
 
-    pms = time_graph_launches(probe, copies * 2, max(4, reps // (copies * 2)))
-    res["read_ceiling"] = {"us": pms * 1e3, "gbps": nbytes / (pms * 1e-3) / 1e9, "bytes": nbytes,
-                           "kernel": "k_read_probe (ql_read_probe)"}
+        by_loads[loads] = time_graph_launches(probe, copies * 2, max(4, reps // (copies * 2))) * 1e3
+    best = min(by_loads, key=by_loads.get)
+    pus = by_loads[best]
+    # the floor of an empty grid as large as the M = 1 decode kernel's (16 rows
+    # of W per work group of 512 threads)
+    groups = (N + 15) // 16
+    eus = time_graph_launches(lambda: P.empty_probe(groups, 512), copies * 2,
+                              max(4, reps // (copies * 2))) * 1e3
+    res["read_ceiling"] = {"us": pus, "gbps": nbytes / (pus * 1e-6) / 1e9, "bytes": nbytes,
+                           "loads_per_thread": best, "us_by_loads": {str(k): round(v, 3) for k, v in by_loads.items()},
+                           "kernel": "k_read_probe (libqlprobe.so ql_read_probe)"}
+    res["empty_grid_floor"] = {"us": eus, "groups": groups, "threads": 512,
+                               "kernel": "k_empty_probe (libqlprobe.so ql_empty_probe)"}
     del bufs
     torch.cuda.empty_cache()
     return res

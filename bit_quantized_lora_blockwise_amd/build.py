@@ -1,4 +1,5 @@
-"""Build libqlora.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
+"""Build libqlora.so (the gfx950 HIP kernels and the C ABI) and libqlprobe.so
+(the benchmark's measurement helpers) in-tree with hipcc.
 
     python -m bit_quantized_lora_blockwise_amd.build
 """
@@ -13,6 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlora.so")
+PROBE_SRC = os.path.join(PKG, "probe", "probe.hip")
+PROBE_LIB = os.path.join(PKG, "libqlprobe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -30,8 +33,8 @@ def _sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, tag: str = "") -> str:
+    obj = os.path.join(BUILD, tag + os.path.basename(src) + ".o")
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -39,19 +42,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = _sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = _sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        probe = ex.submit(_compile, PROBE_SRC, "probe_")
+        objs = list(ex.map(_compile, srcs))
+        probe_obj = probe.result()
+    _link(objs, LIB)
+    _link([probe_obj], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

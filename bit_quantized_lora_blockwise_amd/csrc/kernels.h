@@ -73,9 +73,6 @@ hipError_t launch_lora_tn(const uint16_t* A, int64_t lda, const uint16_t* B, int
 hipError_t launch_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t N, int64_t K,
                         const uint16_t* L1, const uint16_t* L2, int r, float scale, uint16_t* W, hipStream_t s);
 
-// --- measurement helper (probe.hip) -------------------------------------------
-hipError_t launch_read_probe(const void* data, int64_t bytes, uint32_t* sink, hipStream_t s);
-
 // --- adapter optimizer (adamw.hip) -------------------------------------------
 // One AdamW step over n fp32 weights (decoupled decay), optional bf16 copy.
 hipError_t launch_adamw(float* param, float* exp_avg, float* exp_avg_sq, const float* grad, uint16_t* param_bf16,

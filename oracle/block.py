@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .qlora_oracle import _f64, bf16_bits, fp32, qlora_backward, qlora_forward
+from .qlora_oracle import _f64, bf16_bits, qlora_backward, qlora_forward
 
 
 def qlora_group_forward(X, Wq_list, L1_list, L2_list, lora_scale: float = 1.0):
@@ -72,8 +72,3 @@ def adamw_step(theta, m, v, grad, lr: float, beta1: float, beta2: float, eps: fl
     v_hat = v / (1.0 - beta2 ** step)
     theta = theta - lr * m_hat / (np.sqrt(v_hat) + eps)
     return theta, m, v
-
-
-def adapter_bf16(theta) -> np.ndarray:
-    """The bf16 bits of a master copy (what the layer multiplies with)."""
-    return bf16_bits(fp32(theta))

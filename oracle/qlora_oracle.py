@@ -259,27 +259,6 @@ def nf4_dequantize(codes, c2, c1, rows: int, cols: int) -> np.ndarray:
     return dequantize_blocks(c, c2, c1[np.arange(c2.size) // GROUP]).reshape(rows, cols)
 
 
-def nf4_dequantize_rows(codes, c2, c1, cols: int, row_idx) -> np.ndarray:
-    """Rows `row_idx` of the dequantized weight, bf16 bits [len(row_idx), cols]."""
-    codes = np.asarray(codes, dtype=np.uint8).reshape(-1, cols // 2)
-    row_idx = np.asarray(row_idx, dtype=np.int64)
-    bpr = cols // BLOCK
-    b = (row_idx[:, None] * bpr + np.arange(bpr)[None, :]).reshape(-1)
-    c = unpack_codes(codes[row_idx]).reshape(-1, BLOCK)
-    c1 = np.asarray(c1, dtype=np.float32).reshape(-1)
-    return dequantize_blocks(c, np.asarray(c2).reshape(-1)[b], c1[b // GROUP]).reshape(len(row_idx), cols)
-
-
-def nf4_dequantize_colblock(codes, c2, c1, rows: int, cols: int, kb: int) -> np.ndarray:
-    """Columns [64 kb, 64 kb + 64) of the dequantized weight, bf16 bits [rows, 64]."""
-    codes = np.asarray(codes, dtype=np.uint8).reshape(rows, cols // 2)
-    bpr = cols // BLOCK
-    b = np.arange(rows, dtype=np.int64) * bpr + kb
-    c = unpack_codes(codes[:, kb * BLOCK // 2:(kb + 1) * BLOCK // 2])
-    c1 = np.asarray(c1, dtype=np.float32).reshape(-1)
-    return dequantize_blocks(c, np.asarray(c2).reshape(-1)[b], c1[b // GROUP])
-
-
 # ----------------------------------------------------------------------------
 # The layer  ([lineage] notation paragraph: Y = X doubleDequant(c1, c2, W_NF4) + X L1 L2;
 #             [examadda] "Practical Notes": bf16 compute)

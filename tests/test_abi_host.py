@@ -1,7 +1,9 @@
-"""Host-only checks of the C ABI: the library loads, exports every entry point
-declared in include/qlora.h, carries the NF4 table the oracle derives, and
-rejects bad arguments with the documented status before touching the GPU.
-Nothing here launches a kernel (every call below fails validation first)."""
+"""Host-only checks of the C ABI: the libraries load, export every entry point
+declared in include/qlora.h and include/qlprobe.h, carry the NF4 table the
+oracle derives, and reject bad arguments with the documented status before
+touching the GPU; the Python binding rejects wrongly sized tensors before
+calling the library.  Nothing here launches a kernel (every call below fails
+validation first)."""
 import ctypes
 import os
 import re
@@ -13,6 +15,7 @@ import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qlora.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "qlprobe.h")
 
 pytestmark = pytest.mark.skipif(
     not os.path.exists(os.path.join(ROOT, "bit_quantized_lora_blockwise_amd", "libqlora.so")),
@@ -24,8 +27,8 @@ def _lib():
     return q, q.lib()
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
 
@@ -37,6 +40,21 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(q.EXPORTS)
+
+
+def test_probe_library_exports_every_declared_symbol():
+    """The measurement helpers live in their own library and nowhere in the
+    layer library."""
+    import bit_quantized_lora_blockwise_amd.probe as P
+    _, L = _lib()
+    names = header_functions(PROBE_HEADER)
+    assert set(names) == set(P.EXPORTS) == {"ql_read_probe", "ql_empty_probe"}
+    PL = P.lib()
+    for n in names:
+        assert hasattr(PL, n), n
+    for n in names:
+        assert not hasattr(L, n), n
+    assert not set(names) & set(header_functions())
 
 
 def test_nf4_table_matches_oracle_bitwise():
@@ -219,11 +237,100 @@ def test_fused_quantize_validation():
 
 
 def test_read_probe_validation():
-    """The read-bandwidth probe rejects null pointers, sizes that are not a
-    positive multiple of 16 and misaligned pointers before touching the GPU."""
-    _, L = _lib()
-    assert L.ql_read_probe(None, 64, A, None) == -1
-    assert L.ql_read_probe(A, 64, None, None) == -1
-    assert L.ql_read_probe(A, 0, A, None) == -2
-    assert L.ql_read_probe(A, 40, A, None) == -2
-    assert L.ql_read_probe(MIS, 64, A, None) == -4
+    """The probes reject null pointers, sizes that are not a positive multiple
+    of 16, unsupported load counts, bad grids and misaligned pointers before
+    touching the GPU."""
+    import bit_quantized_lora_blockwise_amd.probe as P
+    L = P.lib()
+    assert L.ql_read_probe(None, 64, 4, A, None) == -1
+    assert L.ql_read_probe(A, 64, 4, None, None) == -1
+    assert L.ql_read_probe(A, 0, 4, A, None) == -2
+    assert L.ql_read_probe(A, 40, 4, A, None) == -2
+    assert L.ql_read_probe(A, 64, 3, A, None) == -2
+    assert L.ql_read_probe(A, 64, 32, A, None) == -2
+    assert L.ql_read_probe(MIS, 64, 4, A, None) == -4
+    assert L.ql_empty_probe(0, 256, None) == -2
+    assert L.ql_empty_probe(4, 0, None) == -2
+    assert L.ql_empty_probe(4, 1025, None) == -2
+
+
+# ---- the binding's size checks (CPU tensors: every check below fires before
+#      the device check, so nothing reaches the library)
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_rejects_wrong_sized_outputs():
+    import torch
+    q, _ = _lib()
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    W = _t((4, 128), bf)
+    with pytest.raises(ValueError, match="codes must hold 256"):
+        q.nf4_quantize(W, codes=_t((255,), u8), absmax=_t((8,), f32))
+    with pytest.raises(ValueError, match="absmax must hold 8"):
+        q.nf4_quantize(W, codes=_t((4, 64), u8), absmax=_t((7,), f32))
+    with pytest.raises(ValueError, match="c1 must hold 1"):
+        q.nf4_quantize_dq(W, codes=_t((256,), u8), c2=_t((8,), u8), c1=_t((2,), f32))
+    with pytest.raises(ValueError, match="c2 must hold 9"):
+        q.nf4_double_quant(_t((9,), f32), c2=_t((8,), u8))
+    codes, c2, c1 = _t((64, 64), u8), _t((128,), u8), _t((1,), f32)      # W [64, 128]
+    with pytest.raises(ValueError, match="out must hold 8192"):
+        q.nf4_dequantize(codes, c2, c1, 64, 128, out=_t((64, 127), bf))
+    X, L1, L2 = _t((5, 128), bf), _t((128, 8), bf), _t((8, 64), bf)
+    with pytest.raises(ValueError, match="Y must hold 320"):
+        q.qlora_linear_fwd(X, codes, c2, c1, 64, L1, L2, Y=_t((5, 63), bf))
+    with pytest.raises(ValueError, match="T_out must hold 40"):
+        q.qlora_linear_fwd(X, codes, c2, c1, 64, L1, L2, Y=_t((5, 64), bf), T_out=_t((5, 7), bf))
+    dY = _t((5, 64), bf)
+    with pytest.raises(ValueError, match="dX must hold 640"):
+        q.qlora_linear_bwd(X, dY, codes, c2, c1, L1, L2, dX=_t((5, 64), bf))
+    with pytest.raises(ValueError, match="dL1 must hold 1024"):
+        q.qlora_linear_bwd(X, dY, codes, c2, c1, L1, L2, dX=None, dL1=_t((128, 7), f32))
+    with pytest.raises(ValueError, match="dL2 must hold 512"):
+        q.qlora_linear_bwd(X, dY, codes, c2, c1, L1, L2, dX=None, dL1=_t((128, 8), f32), dL2=_t((8, 65), f32))
+    with pytest.raises(ValueError, match="Y must hold 320"):
+        q.qlora_linear_fwd_t(X, codes, c2, c1, 64, _t((5, 8), bf), L2, Y=_t((320 + 1,), bf))
+    with pytest.raises(ValueError, match="dX must hold 640"):
+        q.qlora_linear_dx(dY, codes, c2, c1, 128, _t((5, 8), bf), L1, dX=_t((5, 127), bf))
+    with pytest.raises(ValueError, match="G must hold 40"):
+        q.qlora_lora_grad_in(dY, L2, G=_t((5, 9), bf))
+    with pytest.raises(ValueError, match="T must hold 40"):
+        q.qlora_lora_down(X, L1, T=_t((4, 8), bf))
+    with pytest.raises(ValueError, match="out must hold 8192"):
+        q.qlora_merge(codes, c2, c1, 64, 128, L1, L2, out=_t((64, 64), bf))
+    with pytest.raises(ValueError, match="workspace must hold at least"):
+        q.qlora_linear_fwd(X, codes, c2, c1, 64, L1, L2, Y=_t((5, 64), bf), workspace=_t((16,), u8))
+
+
+def test_binding_rejects_wrong_sized_inputs():
+    import torch
+    q, _ = _lib()
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    codes, c2, c1 = _t((64, 64), u8), _t((128,), u8), _t((1,), f32)      # W [64, 128]
+    X, L1, L2 = _t((5, 128), bf), _t((128, 8), bf), _t((8, 64), bf)
+    with pytest.raises(ValueError, match="codes must hold 4096"):
+        q.qlora_linear_fwd(X, _t((64, 63), u8), c2, c1, 64, L1, L2)
+    with pytest.raises(ValueError, match="c2 must hold 128"):
+        q.qlora_linear_fwd(X, codes, _t((127,), u8), c1, 64, L1, L2)
+    with pytest.raises(ValueError, match="c1 must hold 1"):
+        q.qlora_linear_fwd(X, codes, c2, _t((0,), f32), 64, L1, L2)
+    with pytest.raises(ValueError, match="L1 must have 128 rows"):
+        q.qlora_linear_fwd(X, codes, c2, c1, 64, _t((64, 8), bf), L2)
+    with pytest.raises(ValueError, match=r"L2 must have shape \(8, 64\)"):
+        q.qlora_linear_fwd(X, codes, c2, c1, 64, L1, _t((8, 65), bf))
+    with pytest.raises(ValueError, match="dY must have 5 rows"):
+        q.qlora_linear_bwd(X, _t((4, 64), bf), codes, c2, c1, L1, L2)
+    with pytest.raises(ValueError, match="T must hold 40"):
+        q.qlora_linear_bwd(X, _t((5, 64), bf), codes, c2, c1, L1, L2, T=_t((5, 4), bf))
+    with pytest.raises(ValueError, match="multiple of 64"):
+        q.nf4_dequantize(codes, c2, c1, 64, 100)
+    with pytest.raises(ValueError, match="grad must hold 10"):
+        q.qlora_adamw_step(_t((10,), f32), _t((10,), f32), _t((10,), f32), _t((9,), f32), 1, 1e-3)
+    with pytest.raises(ValueError, match=r"L2 must have shape \(3, 8, 256\)"):
+        q.qlora_group_fwd(X, _t((768, 64), u8), _t((1536,), u8), _t((6,), f32), 256, 3, _t((3, 128, 8), bf),
+                          _t((3, 8, 255), bf))
+    # a correctly sized CPU tensor passes the size checks and is refused as not on the GPU
+    with pytest.raises(ValueError, match="on the GPU"):
+        q.qlora_linear_fwd(X, codes, c2, c1, 64, L1, L2)

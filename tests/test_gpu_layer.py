@@ -295,12 +295,15 @@ def test_stage_entry_points_match_fused_calls(M):
     assert torch.equal(T, a["T"]) and torch.equal(Y, a["Y"]) and torch.equal(dX, a["dX"])
 
 
-def test_read_probe_runs():
-    """The read-bandwidth probe (a measurement helper) reads a buffer whose XOR is
-    not its trigger word, so the sink keeps its value; a ragged tail is accepted."""
-    q = qlib()
+@pytest.mark.parametrize("loads", [1, 2, 4, 8, 16])
+def test_read_probe_runs(loads):
+    """The read-bandwidth probe (a measurement helper in its own library) reads a
+    buffer whose XOR is not its trigger word, so the sink keeps its value; a
+    ragged tail is accepted; the empty grid runs."""
+    import bit_quantized_lora_blockwise_amd.probe as P
     buf = torch.zeros((1 << 20) + 48, dtype=torch.uint8, device=DEV)
     sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
-    q.read_probe(buf, sink)
+    P.read_probe(buf, sink, loads)
+    P.empty_probe(1024, 256)
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
