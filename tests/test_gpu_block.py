@@ -8,8 +8,9 @@ import pytest
 import torch
 
 import oracle as O
+import oracle_pool
 import workloads as WL
-from gpu_util import assert_close, bits, f32np
+from gpu_util import assert_bitexact, assert_close, bits, f32np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -81,6 +82,50 @@ def test_stacked_equals_separate_and_oracle(M, K, N, G, r):
     for g in range(G):
         assert_close(f32np(dL1[g]), rdL1[g], f"stacked dL1[{g}]")
         assert_close(f32np(dL2[g]), rdL2[g], f"stacked dL2[{g}]")
+
+
+@pytest.mark.parametrize("names", [("q", "k", "v"), ("gate", "up")])
+def test_stacked_llama65b_full(names):
+    """The stacked q|k|v and gate|up of a LLaMA-65B block at M = 2048 tokens
+    (r = 64 on every segment): the stack's codes, c2 and c1 equal the
+    concatenation of the oracle's per-matrix encodings bit for bit, and Y, T,
+    dX, dL1 and dL2 match the block oracle in every element."""
+    q = qlib()
+    G = len(names)
+    inps = [WL.config4_linear(n) for n in names]
+    N, K = inps[0]["W"].shape
+    M = inps[0]["X"].shape[0]
+    print(f"[group full] {'|'.join(names)} M={M} K={K} N={N} G={G}", flush=True)
+    X = inps[0]["X"]
+    dY = WL.normal((M, G * N), 1e-2, 7000 + G)
+    L1 = torch.stack([i["L1"] for i in inps])
+    L2 = torch.stack([i["L2"] for i in inps])
+    codes, absmax = q.nf4_quantize(torch.cat([i["W"] for i in inps]).to(DEV))
+    c2, c1 = q.nf4_double_quant(absmax)
+    del absmax
+    Xd, dYd, L1d, L2d = X.to(DEV), dY.to(DEV), L1.to(DEV), L2.to(DEV)
+    Y, T = q.qlora_group_fwd(Xd, codes, c2, c1, N, G, L1d, L2d, 1.0, T_out=True)
+    dX, dL1, dL2 = q.qlora_group_bwd(Xd, dYd, codes, c2, c1, G, L1d, L2d, 1.0, T=T)
+    torch.cuda.synchronize()
+    ref = [oracle_pool.quantize(bits(i["W"])) for i in inps]
+    assert_bitexact(codes.cpu().numpy().reshape(-1), np.concatenate([r[0].reshape(-1) for r in ref]), "stack codes")
+    assert_bitexact(c2.cpu().numpy(), np.concatenate([r[2] for r in ref]), "stack c2")
+    assert_bitexact(c1.cpu().numpy().view(np.uint32), np.concatenate([r[3] for r in ref]).view(np.uint32),
+                    "stack c1")
+    Wq = [r[4] for r in ref]
+    del ref
+    L1b = [bits(L1[g]) for g in range(G)]
+    L2b = [bits(L2[g]) for g in range(G)]
+    rY, rT = B.qlora_group_forward(bits(X), Wq, L1b, L2b, 1.0)
+    assert_close(bits(Y), rY, "stacked Y")
+    del rY
+    for g in range(G):
+        assert_close(bits(T[g]), rT[g], f"stacked T{g}")
+    rdX, rdL1, rdL2, _ = B.qlora_group_backward(bits(X), bits(dY), Wq, L1b, L2b, 1.0, T_list=rT)
+    assert_close(bits(dX), rdX, "stacked dX")
+    for g in range(G):
+        assert_close(f32np(dL1[g]), rdL1[g], f"stacked dL1 {names[g]}")
+        assert_close(f32np(dL2[g]), rdL2[g], f"stacked dL2 {names[g]}")
 
 
 @pytest.mark.parametrize("n", [4096 * 33, 1001])

@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import oracle as O
+import oracle_pool
 import workloads as WL
 from gpu_util import assert_bitexact, bits
 
@@ -315,12 +316,37 @@ def test_fused_quantize_and_double_quant(rows, cols, dtype):
     assert torch.equal(c2, c2_s) and torch.equal(c2_n, c2_s)
     assert torch.equal(c1.view(torch.int32), c1_s.view(torch.int32)) and torch.equal(c1_n.view(torch.int32),
                                                                                        c1_s.view(torch.int32))
-    if rows * cols <= 1 << 20:
-        rc, ra = O.nf4_quantize(W.float().numpy())
-        rc2, rc1 = O.nf4_double_quant(ra)
-        assert_bitexact(codes.cpu().numpy(), rc, "fused codes")
-        assert_bitexact(c2.cpu().numpy(), rc2, "fused c2")
-        assert_bitexact(c1.cpu().numpy().view(np.uint32), rc1.view(np.uint32), "fused c1")
+    rc, ra, rc2, rc1, _ = oracle_pool.quantize(W.float().numpy(), dequant=False)
+    assert_bitexact(codes.cpu().numpy().reshape(-1), rc.reshape(-1), "fused codes")
+    assert_bitexact(absmax.cpu().numpy().view(np.uint32), ra.view(np.uint32), "fused absmax")
+    assert_bitexact(c2.cpu().numpy(), rc2, "fused c2")
+    assert_bitexact(c1.cpu().numpy().view(np.uint32), rc1.view(np.uint32), "fused c1")
+
+
+@pytest.mark.parametrize("variant", ["gauss", "t5"])
+@pytest.mark.parametrize("layer", [0, 1, 40, 79])
+def test_fused_encoder_llama65b_layers(layer, variant):
+    """The encoding workload of 80 LLaMA-65B blocks, sampled at layers 0, 1, 40
+    and 79 of both weight distributions: the three distinct matrix shapes of a
+    layer (q 8192 x 8192, gate 22016 x 8192, down 8192 x 22016), drawn on the
+    GPU with the layer's seeds, go through the one-pass encoder; codes, c2 and
+    c1 equal the oracle's bit for bit over the whole matrix, and so does the
+    dequantized weight of the q matrix."""
+    import bit_quantized_lora_blockwise_amd as q
+    for name in ("q", "gate", "down"):
+        W = WL.config5_weight(layer, name, variant, device=DEV)
+        print(f"[fused encode 65B] layer {layer} {variant} {name} {tuple(W.shape)}", flush=True)
+        codes, c2, c1, _ = q.nf4_quantize_dq(W)
+        deq = q.nf4_dequantize(codes, c2, c1, *W.shape) if name == "q" else None
+        torch.cuda.synchronize()
+        rc, _, rc2, rc1, rq = oracle_pool.quantize(bits(W), dequant=deq is not None)
+        tag = f"layer {layer} {variant} {name}"
+        assert_bitexact(codes.cpu().numpy().reshape(-1), rc.reshape(-1), f"{tag} codes")
+        assert_bitexact(c2.cpu().numpy(), rc2, f"{tag} c2")
+        assert_bitexact(c1.cpu().numpy().view(np.uint32), rc1.view(np.uint32), f"{tag} c1")
+        if deq is not None:
+            assert_bitexact(bits(deq), rq, f"{tag} dequant")
+        del W, codes, c2, c1, deq
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])

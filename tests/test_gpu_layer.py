@@ -1,7 +1,8 @@
 """GPU parity of the quantized LoRA linear (forward and backward) against the
-CPU oracle: small and ragged shapes compared element by element, the
-decode-sized and training-sized workloads compared in full where the oracle
-can afford it and on sampled rows / columns otherwise.
+CPU oracle: small and ragged shapes, the decode-sized workloads and the
+training-sized LLaMA-7B and LLaMA-65B linears, every output compared element by
+element (the large weights go through the oracle's encoder in worker processes,
+on group-aligned row slabs).
 
 Tolerance (Y, dX, dL1, dL2 and T): relative L2 <= 2e-3 and
 max |err| <= 1e-2 * max |ref|, with the oracle rounding T, Y, G and dX to bf16
@@ -12,7 +13,8 @@ import torch
 
 import oracle as O
 import workloads as WL
-from gpu_util import assert_close, bits, f32np
+import oracle_pool
+from gpu_util import assert_bitexact, assert_close, bits, f32np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -244,39 +246,46 @@ def test_decode_slices(M, K, N, r):
     assert_close(bits(Y), rY, f"decode slices given T: Y M={M} K={K} r={r}")
 
 
-def _sampled_case(inp, name, n_rows=48, seed=0):
-    """Full-size check: dL1, dL2 and T in full; Y and dX on sampled rows."""
+def _big_case(inp, name):
+    """Full-size check, every output element compared: the GPU encoder's codes,
+    absmax, c2 and c1 bit-exact against the oracle's (computed on group-aligned
+    row slabs in worker processes), then T, Y, dX, dL1 and dL2 of the layer
+    against the oracle's float64 layer on the oracle's own dequantized weight."""
+    q = qlib()
     N, K = inp["W"].shape
     M = inp["X"].shape[0]
-    print(f"[layer sampled] {name} M={M} K={K} N={N}", flush=True)
-    gq, rq = quantize_both(inp["W"])
-    g = run_gpu(inp, 1.0, gq)
-    rows = np.sort(np.random.default_rng(seed).choice(M, n_rows, replace=False))
-    rows[0], rows[-1] = 0, M - 1
-    Wq = O.nf4_dequantize(*rq, N, K)
+    print(f"[layer full] {name} M={M} K={K} N={N}", flush=True)
+    W = inp["W"].to(DEV)
+    codes, absmax = q.nf4_quantize(W)
+    c2, c1 = q.nf4_double_quant(absmax)
+    g = run_gpu(inp, 1.0, (codes, c2, c1))
+    rc, ra, rc2, rc1, Wq = oracle_pool.quantize(bits(inp["W"]))
+    assert_bitexact(codes.cpu().numpy().reshape(-1), rc.reshape(-1), f"{name} codes")
+    assert_bitexact(absmax.cpu().numpy().view(np.uint32), ra.view(np.uint32), f"{name} absmax")
+    assert_bitexact(c2.cpu().numpy(), rc2, f"{name} c2")
+    assert_bitexact(c1.cpu().numpy().view(np.uint32), rc1.view(np.uint32), f"{name} c1")
     X, L1, L2, dY = (bits(inp[k]) for k in ("X", "L1", "L2", "dY"))
-    Y_s, T_s = O.qlora_forward(X[rows], Wq, L1, L2, 1.0)
-    assert_close(bits(g["Y"])[rows], Y_s, f"{name} Y rows")
-    T_full = O.bf16_bits(O.bf16_value(X) @ O.bf16_value(L1))
-    assert_close(bits(g["T"]), T_full, f"{name} T")
-    dX_s, _, _, _, _ = O.qlora_backward(X[rows], dY[rows], Wq, L1, L2, 1.0, T=T_full[rows])
-    assert_close(bits(g["dX"])[rows], dX_s, f"{name} dX rows")
-    _, dL1, dL2, _, _ = O.qlora_backward(X, dY, None, L1, L2, 1.0, T=T_full, compute_dx=False)
+    Y, T = O.qlora_forward(X, Wq, L1, L2, 1.0)
+    assert_close(bits(g["T"]), T, f"{name} T")
+    assert_close(bits(g["Y"]), Y, f"{name} Y")
+    del Y
+    dX, dL1, dL2, _, _ = O.qlora_backward(X, dY, Wq, L1, L2, 1.0, T=T)
+    assert_close(bits(g["dX"]), dX, f"{name} dX")
     assert_close(f32np(g["dL1"]), dL1, f"{name} dL1")
     assert_close(f32np(g["dL2"]), dL2, f"{name} dL2")
 
 
 @pytest.mark.parametrize("which", ["up", "down"])
-def test_llama7b_mlp_m4096_sampled(which):
+def test_llama7b_mlp_m4096_full(which):
     c = WL.config3()[which]
-    _sampled_case(c, f"llama7b {which} M=4096")
+    _big_case(c, f"llama7b {which} M=4096")
 
 
 @pytest.mark.parametrize("name", ["q", "gate", "down"])
-def test_llama65b_block_linear_sampled(name):
+def test_llama65b_block_linear_full(name):
     """One linear of each distinct shape of the 65B block (k, v, o share q's shape,
-    up shares gate's) at M = 2048."""
-    _sampled_case(WL.config4_linear(name), f"llama65b {name} M=2048", n_rows=24)
+    up shares gate's) at M = 2048, every output compared."""
+    _big_case(WL.config4_linear(name), f"llama65b {name} M=2048")
 
 
 @pytest.mark.parametrize("M", [8, 96])
