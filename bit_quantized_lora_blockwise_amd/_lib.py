@@ -28,7 +28,7 @@ EXPORTS = ("nf4_quantize", "nf4_quantize_dq", "nf4_double_quant", "nf4_dequantiz
            "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx", "qlora_merge",
            "q4_quantize", "q4_double_quant", "q4_dequantize", "q4_levels",
            "qlora_group_fwd_workspace", "qlora_group_fwd", "qlora_group_bwd_workspace", "qlora_group_bwd",
-           "qlora_adamw_step")
+           "qlora_adamw_step", "qlora_linear_fwd_noalloc")
 
 
 class QloraError(RuntimeError):
@@ -73,6 +73,7 @@ def lib():
             "qlora_group_bwd_workspace": ([I64, I64, I64, I32, I32], SZ),
             "qlora_group_bwd": ([P, P, I64, I64, I64, I32, P, P, P, P, P, I32, F32, P, P, P, P, P, SZ, P], I32),
             "qlora_adamw_step": ([P, P, P, P, P, I64, F32, F32, F32, F32, F32, I64, P], I32),
+            "qlora_linear_fwd_noalloc": ([P, I64, I64, I64, P, P, P, P, P, I32, F32, P, P, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -328,6 +329,26 @@ def qlora_linear_fwd(X, codes, c2, c1, N, L1, L2, lora_scale=1.0, Y=None, T_out=
     _check("qlora_linear_fwd", lib().qlora_linear_fwd(
         _ptr(X), M, K, N, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(L1), _ptr(L2), r, float(lora_scale),
         _ptr(Y), _ptr(T_out), _ptr(ws), ws.numel(), _stream(stream)))
+    return Y, T_out
+
+
+NOALLOC_SCRATCH_BYTES = 16777216      # QL_NOALLOC_SCRATCH_BYTES of include/qlora.h
+
+
+def qlora_linear_fwd_noalloc(X, codes, c2, c1, N, L1, L2, lora_scale=1.0, Y=None, T_out=None, stream=None):
+    """qlora_linear_fwd with its scratch in the library's per-GPU static array
+    (for callers that cannot allocate; calls that overlap on one GPU race).
+    Returns (Y, T_out or None); Y and T_out must be supplied to allocate nothing."""
+    _need(X, "X", torch.bfloat16, ndim=2)
+    M, K = X.shape
+    _packed(codes, c2, c1, N, K)
+    r = _rank(L1, K)
+    _need(L2, "L2", torch.bfloat16, shape=(r, N))
+    Y = _out(Y, "Y", torch.bfloat16, (M, N), X)
+    T_out = _opt_out(T_out, "T_out", torch.bfloat16, (M, r), X)
+    _check("qlora_linear_fwd_noalloc", lib().qlora_linear_fwd_noalloc(
+        _ptr(X), M, K, N, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(L1), _ptr(L2), r, float(lora_scale),
+        _ptr(Y), _ptr(T_out), _stream(stream)))
     return Y, T_out
 
 

@@ -108,6 +108,8 @@ GroupWs group_ws(int64_t M, int64_t K, int64_t N, int G, int r) {
 
 }  // namespace
 
+int ql_record_hip_error(hipError_t e) { return e == hipSuccess ? QL_OK : hip_status(e); }
+
 extern "C" {
 
 int nf4_quantize(const void* W, int w_dtype, int64_t rows, int64_t cols, uint8_t* codes, float* absmax,

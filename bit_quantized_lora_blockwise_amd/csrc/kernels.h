@@ -8,6 +8,9 @@
 
 #include "common.h"
 
+// Keeps a HIP error for ql_status_string and returns QL_ERR_HIP (abi.cpp).
+int ql_record_hip_error(hipError_t e);
+
 const Nf4Params& nf4_params();
 const Nf4Buckets& nf4_buckets();
 // Level table of a 4-bit code book: 0 NF4, 1 4-bit float (E2M1 / 6), 2 4-bit

@@ -121,6 +121,28 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
                      uint16_t* Y, uint16_t* T_out,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * qlora_linear_fwd without a workspace argument: same formulas, kernels and
+ * results, bit for bit. Its scratch is a file-scope device array of
+ * QL_NOALLOC_SCRATCH_BYTES per GPU (allocated by the HIP runtime when the
+ * library's code is loaded on that GPU and held until the process ends); the
+ * first call on each GPU looks up that array's address (hipGetSymbolAddress,
+ * with that GPU current), so a caller that captures graphs makes one call
+ * outside capture first. The call itself allocates nothing. Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from several threads) race and give unspecified
+ * results. The array needs no clearing: each call writes every scratch
+ * element it reads. `stream` must belong to the current GPU.
+ * Errors as qlora_linear_fwd, plus QL_ERR_WORKSPACE when
+ * qlora_linear_fwd_workspace(M, K, N, r) exceeds QL_NOALLOC_SCRATCH_BYTES
+ * (checked before anything is enqueued).                                       */
+#define QL_NOALLOC_SCRATCH_BYTES 16777216u
+int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                             const uint8_t* codes, const uint8_t* c2, const float* c1,
+                             const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
+                             uint16_t* Y, uint16_t* T_out, void* stream);
+
 /* Workspace (bytes) that qlora_linear_bwd needs for these sizes.               */
 size_t qlora_linear_bwd_workspace(int64_t M, int64_t K, int64_t N, int r);
 

@@ -334,3 +334,17 @@ def test_binding_rejects_wrong_sized_inputs():
     # a correctly sized CPU tensor passes the size checks and is refused as not on the GPU
     with pytest.raises(ValueError, match="on the GPU"):
         q.qlora_linear_fwd(X, codes, c2, c1, 64, L1, L2)
+
+
+def test_noalloc_forward_validation():
+    """The forward that allocates nothing refuses sizes whose scratch exceeds its
+    static array, and bad arguments, on the host (before any HIP call)."""
+    q, L = _lib()
+    M, K, N, r = 32768, 16384, 256, 64
+    assert L.qlora_linear_fwd_workspace(M, K, N, r) > q.NOALLOC_SCRATCH_BYTES
+    assert L.qlora_linear_fwd_noalloc(A, M, K, N, A, A, A, A, A, r, 1.0, A, None, None) == -5
+    assert L.qlora_linear_fwd_noalloc(None, 64, 512, 256, A, A, A, A, A, 8, 1.0, A, None, None) == -1
+    assert L.qlora_linear_fwd_noalloc(A, 64, 500, 256, A, A, A, A, A, 8, 1.0, A, None, None) == -2
+    assert L.qlora_linear_fwd_noalloc(A, 64, 512, 256, A, A, A, A, A, 65, 1.0, A, None, None) == -2
+    assert L.qlora_linear_fwd_noalloc(A, 64, 512, 256, A, A, A, A, A, 8, 1.0, MIS, None, None) == -4
+    assert L.qlora_linear_fwd_noalloc(A, 64, 512, 256, A, A, A, A, A, 8, 1.0, A, MIS, None) == -4
