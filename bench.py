@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the per-kernel roofline timings (fused GEMMs and the decode forward), printed as "
+                         "one JSON line: the run that the committed kernel trace profiles")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only launch each fused GEMM a few times on the headline shapes, then a plain "
                          "512 MiB device copy (the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -168,8 +171,12 @@ def time_graph_launches(fn, calls, reps):
     return a.elapsed_time(b) / (reps * calls)
 
 
-def kernel_rooflines(lins, reps):
-    """Fused forward GEMM and fused dX GEMM, each launched alone (stage entry points)."""
+def kernel_rooflines(lins, reps, warm_launches=60):
+    """Fused forward GEMM and fused dX GEMM, each launched alone (stage entry
+    points).  The core clock settles over the first tens of milliseconds of
+    sustained MFMA work, so `warm_launches` launches of both kernels run first;
+    then each shape alone and both shapes back to back are timed with HIP
+    events (avg_ms: the back-to-back average per launch)."""
     q = lins[0].q
     out = {}
     for L in lins:
@@ -184,16 +191,19 @@ def kernel_rooflines(lins, reps):
                 f()
         return run
 
+    for _ in range(warm_launches // (2 * len(lins))):
+        both(fwd_fns)()
+        both(dx_fns)()
     for name, fns, flops in (
             ("k_qgemm_fwd", fwd_fns, [2 * L.M * L.K * L.N + 2 * L.M * L.r * L.N for L in lins]),
             ("k_qgemm_dx", dx_fns, [2 * L.M * L.K * L.N + 2 * L.M * L.r * L.K for L in lins])):
-        ms = time_launches(both(fns), reps) / len(fns)       # average per launch over the shape mix
-        avg_flops = sum(flops) / len(flops)
-        tf = avg_flops / (ms * 1e-3) / 1e12
         per_shape = {}
         for L, f, fl in zip(lins, fns, flops):
             sms = time_launches(f, reps)
             per_shape[f"{L.K}->{L.N}"] = {"ms": sms, "tflops": fl / (sms * 1e-3) / 1e12}
+        ms = time_launches(both(fns), reps) / len(fns)       # average per launch over the shape mix
+        avg_flops = sum(flops) / len(flops)
+        tf = avg_flops / (ms * 1e-3) / 1e12
         out[name] = {"avg_ms": ms, "flops_per_launch": avg_flops, "tflops": tf, "per_shape": per_shape}
     return out
 
@@ -280,6 +290,7 @@ def decode_bench(dev, reps=200):
         res[f"M{M}"] = {"kernel_us": kms * 1e3, "packed_gbps": packed / (kms * 1e-3) / 1e9,
                         "alg_gbps": alg / (kms * 1e-3) / 1e9, "full_call_us": fms * 1e3,
                         "full_call_packed_gbps": packed / (fms * 1e-3) / 1e9,
+                        "full_call_alg_gbps": (alg + K * r * 2) / (fms * 1e-3) / 1e9,
                         "eager_kernel_us": kms_eager * 1e3, "eager_full_call_us": fms_eager * 1e3}
     res["packed_bytes"] = packed
     res["copies_rotated"] = copies
@@ -349,12 +360,68 @@ def encode_bench(dev, reps=3):
     alg_bytes = weights * (2 + 0.5 + 4 / 64 + 4 / 64 + 1 / 64) + 4 * weights / 16384
     alg_bytes_fused = weights * (2 + 0.5 + 1 / 64) + 4 * weights / 16384
     res = {"block_weights": weights, "ms_per_block": ms, "weights_per_s": weights / (ms * 1e-3),
-           "alg_gbps": alg_bytes_fused / (ms * 1e-3) / 1e9, "est_80_blocks_ms": 80 * ms,
+           "alg_gbps": alg_bytes_fused / (ms * 1e-3) / 1e9,
            "kernel": "k_nf4_encode_dq (one pass)", "ms_per_block_two_calls": ms_two,
            "alg_gbps_two_calls": alg_bytes / (ms_two * 1e-3) / 1e9}
     del mats
     torch.cuda.empty_cache()
     return res
+
+
+def encode_model_bench(dev, layers=80):
+    """The encoding workload of a whole LLaMA-65B-shaped model: the seven linear
+    weights of each of `layers` blocks (64.76e9 weights at 80), drawn on the GPU
+    with each layer's seeds in both weight distributions (N(0, 0.02) and
+    0.02 * t_5).  For each distribution every weight is resident in HBM (129.5 GB
+    of bf16) and every output buffer too (codes, c2, c1: 33.4 GB) before the
+    timed region, which runs the one-pass encoder over all 7 * layers matrices
+    back to back.  The codes of layers 0, 1, 40 and 79 of both distributions are
+    compared with the CPU oracle bit for bit by the GPU test suite
+    (test_gpu_encoder.py, test_fused_encoder_llama65b_layers), from the same
+    generators and seeds."""
+    import torch
+    import bit_quantized_lora_blockwise_amd as q
+    import workloads as WL
+    names = list(WL.LLAMA65B_BLOCK)
+    mats = []
+    for layer in range(layers):
+        for name in names:
+            N, K = WL.LLAMA65B_BLOCK[name]
+            nb = N * K // 64
+            mats.append((layer, name, torch.empty((N, K), dtype=torch.bfloat16, device=dev),
+                         torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+                         torch.empty((nb,), dtype=torch.uint8, device=dev),
+                         torch.empty(((nb + 255) // 256,), dtype=torch.float32, device=dev)))
+    weights = sum(m[2].numel() for m in mats)
+    alg_bytes = weights * (2 + 0.5 + 1 / 64) + 4 * sum(m[5].numel() for m in mats)
+    out = {"layers": layers, "matrices": len(mats), "weights": weights, "alg_bytes": alg_bytes,
+           "kernel": "k_nf4_encode_dq (nf4_quantize_dq)",
+           "bitexact_vs_oracle": "layers 0, 1, 40, 79 x both distributions: tests/test_gpu_encoder.py"}
+    for variant in ("gauss", "t5"):
+        g0 = time.perf_counter()
+        for layer, name, W, _, _, _ in mats:
+            W.copy_(WL.config5_weight(layer, name, variant, device=dev))
+        torch.cuda.synchronize()
+        gen_s = time.perf_counter() - g0
+
+        def run():
+            for _, _, W, cd, c2, c1 in mats:
+                q.nf4_quantize_dq(W, codes=cd, c2=c2, c1=c1)
+
+        run()                                   # warm-up pass over every matrix
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        gbps = alg_bytes / (ms * 1e-3) / 1e9
+        out[variant] = {"ms": round(ms, 3), "weights_per_s": weights / (ms * 1e-3), "alg_gbps": round(gbps, 1),
+                        "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "generate_s": round(gen_s, 2)}
+    del mats
+    torch.cuda.empty_cache()
+    return out
 
 
 def merge_bench(dev, reps=20):
@@ -599,9 +666,24 @@ def cpu_baseline(min_seconds=10.0, max_passes=4):
         dt += time.perf_counter() - t0
         passes += 1
     return {"value": flops_step * passes / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "seconds": round(dt, 3), "steps": passes,
             "sample": f"{passes} whole step(s) of the headline workload (llama7b MLP up + down, M=4096, r=64): "
                       "encode + double quant + dequant + fwd + bwd, float64 NumPy oracle on the host"}
+
+
+def cpu_model():
+    """Model name of the host CPU (from /proc/cpuinfo), with the number of
+    logical CPUs this process may run on."""
+    name = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return f"{name} ({len(os.sched_getaffinity(0))} logical CPUs available)"
 
 
 def pmc_probe(lins, reps=3):
@@ -634,6 +716,22 @@ def pmc_probe(lins, reps=3):
                       "copy_bytes": 1 << 29}))
 
 
+def decode_roofline(dec):
+    """The M = 1 decode forward at 4096 -> 11008 against 8 TB/s: the decode
+    kernel alone (stage entry point, T given) and the full qlora_linear_fwd call
+    (T = X L1 formed first by a separate launch)."""
+    m1 = dec["M1"]
+    ceil = dec["read_ceiling"]
+    return {"kernel": "k_qgemv_fwd", "stage": "qlora_linear_fwd_t (decode kernel alone, T given)",
+            "bound": "hbm", "achieved": m1["alg_gbps"], "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": m1["alg_gbps"] / PEAK_HBM_GBPS,
+            "traffic": recorded_traffic("k_qgemv_fwd", DECODE_SOURCE),
+            "avg_launch_us": m1["kernel_us"], "read_ceiling_gbps": ceil["gbps"],
+            "packed_frac_of_read_ceiling": m1["packed_gbps"] / ceil["gbps"],
+            "full_call_us": m1["full_call_us"], "full_call_frac": m1["full_call_alg_gbps"] / PEAK_HBM_GBPS,
+            "empty_grid_floor_us": dec["empty_grid_floor"]["us"]}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -655,6 +753,17 @@ def main():
         for L in lins:
             L.encode()
         pmc_probe(lins)
+        return
+    if args.roofline_only:
+        for L in lins:
+            L.encode()
+        kern = kernel_rooflines(lins, args.kernel_reps)
+        dom = max(kern, key=lambda k: kern[k]["avg_ms"])
+        del lins
+        torch.cuda.empty_cache()
+        dec = decode_bench(dev)
+        print(json.dumps({"roofline_only": True, "kernels": kern, "dominant": dom,
+                          "roofline_decode": decode_roofline(dec), "decode": dec}))
         return
 
     def step():
@@ -685,23 +794,18 @@ def main():
     fb_ms = phases["forward_ms"] + phases["backward_ms"]
 
     kern = kernel_rooflines(lins, args.kernel_reps)
-    comp = comparators(lins, max(3, args.kernel_reps // 4))
     dom = max(kern, key=lambda k: kern[k]["avg_ms"])
     roof = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": kern[dom]["tflops"] / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(dom),
             "avg_launch_ms": kern[dom]["avg_ms"], "flops_per_launch": kern[dom]["flops_per_launch"]}
+    comp = comparators(lins, max(3, args.kernel_reps // 4))
     del lins
     torch.cuda.empty_cache()
 
     dec = decode_bench(dev)
-    m1 = dec["M1"]
-    ceil = dec["read_ceiling"]
-    dec_roof = {"kernel": "k_qgemv_fwd", "bound": "hbm", "achieved": m1["alg_gbps"], "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": m1["alg_gbps"] / PEAK_HBM_GBPS,
-                "traffic": recorded_traffic("k_qgemv_fwd", DECODE_SOURCE),
-                "avg_launch_us": m1["kernel_us"], "read_ceiling_gbps": ceil["gbps"],
-                "packed_frac_of_read_ceiling": m1["packed_gbps"] / ceil["gbps"]}
+    dec_roof = decode_roofline(dec)
     enc = encode_bench(dev)
+    enc["model_80_layers"] = encode_model_bench(dev)
     mrg = merge_bench(dev)
     study = quant_study(dev)
     blk = block_bench(dev)
@@ -718,7 +822,7 @@ def main():
         "comparators": comp,
         "roofline": roof,
         "kernels": kern,
-        "decode_m1_packed_gbps": round(m1["packed_gbps"], 1),
+        "decode_m1_packed_gbps": round(dec["M1"]["packed_gbps"], 1),
         "decode": dec,
         "roofline_decode": dec_roof,
         "encode": enc,
