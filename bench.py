@@ -209,12 +209,16 @@ def kernel_rooflines(lins, reps, warm_launches=60):
 
 
 def comparators(lins, reps):
-    """Same fwd + bwd of both linears by two other strategies, for context (the
-    headline is the fused 4-bit path).  The bf16 GEMMs are torch's (hipBLASLt).
-      lora_bf16_base: LoRA over a bf16 base (the dequantised weights kept in HBM):
-        torch GEMMs for the base, this library's kernels for the adapter products;
+    """The same fwd + bwd of both linears by other strategies, for context (the
+    headline is the fused 4-bit path):
+      lora_bf16_base: LoRA over a bf16 base (the dequantised weights kept in HBM)
+        with this library's own GEMM kernels (lora_linear_fwd / lora_linear_bwd);
       dequant_then_gemm: the 4-bit base dequantised to bf16 in HBM each step
-        (nf4_dequantize), then the same torch GEMMs."""
+        (nf4_dequantize), then the same bf16-base kernels;
+      *_hipblaslt: the same two with torch's bf16 GEMMs (hipBLASLt) for the base
+        products and this library's adapter products.
+    Also the bf16-weight GEMM kernels alone (kernels_bf16), to set against the
+    fused 4-bit GEMMs (the cost of the on-the-fly dequantisation)."""
     import torch
     q = lins[0].q
     prep = []
@@ -222,7 +226,15 @@ def comparators(lins, reps):
         Wd = q.nf4_dequantize(L.codes, L.c2, L.c1, L.N, L.K)           # [N, K] bf16
         prep.append({"L": L, "W": Wd, "Wbuf": torch.empty_like(Wd)})
 
-    def lora_step(p, dequant):
+    def own_step(p, dequant):
+        L = p["L"]
+        W = p["Wbuf"] if dequant else p["W"]
+        if dequant:
+            q.nf4_dequantize(L.codes, L.c2, L.c1, L.N, L.K, out=W)
+        q.lora_linear_fwd(L.X, W, L.L1, L.L2, 1.0, Y=L.Y, T_out=L.T, workspace=L.ws_f)
+        q.lora_linear_bwd(L.X, L.dY, W, L.L1, L.L2, 1.0, T=L.T, dX=L.dX, dL1=L.dL1, dL2=L.dL2, workspace=L.ws_b)
+
+    def torch_step(p, dequant):
         L = p["L"]
         W = p["Wbuf"] if dequant else p["W"]
         if dequant:
@@ -239,9 +251,26 @@ def comparators(lins, reps):
 
     out = {}
     flops = sum(L.flops() for L in lins)
-    for name, dq in (("lora_bf16_base", False), ("dequant_then_gemm", True)):
-        ms = time_launches(lambda: [lora_step(p, dq) for p in prep], reps)
+    for name, fn, dq in (("lora_bf16_base", own_step, False), ("dequant_then_gemm", own_step, True),
+                         ("lora_bf16_base_hipblaslt", torch_step, False),
+                         ("dequant_then_gemm_hipblaslt", torch_step, True)):
+        ms = time_launches(lambda: [fn(p, dq) for p in prep], reps)
         out[name] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+    kb = {}
+    for kind in ("fwd", "dx"):
+        per = {}
+        for p in prep:
+            L = p["L"]
+            if kind == "fwd":
+                fl = 2 * L.M * L.K * L.N + 2 * L.M * L.r * L.N
+                f = lambda L=L, W=p["W"]: q.lora_linear_fwd_t(L.X, W, L.T, L.L2, 1.0, Y=L.Y)
+            else:
+                fl = 2 * L.M * L.K * L.N + 2 * L.M * L.r * L.K
+                f = lambda L=L, W=p["W"]: q.lora_linear_dx(L.dY, W, L.G, L.L1, dX=L.dX)
+            ms = time_launches(f, reps)
+            per[f"{L.K}->{L.N}"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+        kb["k_bgemm_" + kind] = per
+    out["kernels_bf16"] = kb
     del prep
     torch.cuda.empty_cache()
     return out

@@ -12,4 +12,5 @@ from ._lib import (  # noqa: F401
     qlora_merge,
     CODEBOOKS, SCALE_CODES, q4_quantize, q4_double_quant, q4_dequantize, q4_levels,
     qlora_group_fwd, qlora_group_bwd, qlora_adamw_step, qlora_linear_fwd_noalloc, NOALLOC_SCRATCH_BYTES,
+    lora_linear_fwd, lora_linear_bwd, lora_linear_fwd_t, lora_linear_dx,
 )

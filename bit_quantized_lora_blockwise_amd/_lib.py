@@ -28,7 +28,8 @@ EXPORTS = ("nf4_quantize", "nf4_quantize_dq", "nf4_double_quant", "nf4_dequantiz
            "qlora_lora_grad_in_workspace", "qlora_lora_grad_in", "qlora_linear_dx", "qlora_merge",
            "q4_quantize", "q4_double_quant", "q4_dequantize", "q4_levels",
            "qlora_group_fwd_workspace", "qlora_group_fwd", "qlora_group_bwd_workspace", "qlora_group_bwd",
-           "qlora_adamw_step", "qlora_linear_fwd_noalloc")
+           "qlora_adamw_step", "qlora_linear_fwd_noalloc",
+           "lora_linear_fwd", "lora_linear_bwd", "lora_linear_fwd_t", "lora_linear_dx")
 
 
 class QloraError(RuntimeError):
@@ -74,6 +75,10 @@ def lib():
             "qlora_group_bwd": ([P, P, I64, I64, I64, I32, P, P, P, P, P, I32, F32, P, P, P, P, P, SZ, P], I32),
             "qlora_adamw_step": ([P, P, P, P, P, I64, F32, F32, F32, F32, F32, I64, P], I32),
             "qlora_linear_fwd_noalloc": ([P, I64, I64, I64, P, P, P, P, P, I32, F32, P, P, P], I32),
+            "lora_linear_fwd": ([P, I64, I64, I64, P, P, P, I32, F32, P, P, P, SZ, P], I32),
+            "lora_linear_bwd": ([P, P, I64, I64, I64, P, P, P, I32, F32, P, P, P, P, P, SZ, P], I32),
+            "lora_linear_fwd_t": ([P, I64, I64, I64, P, P, P, I32, F32, P, P], I32),
+            "lora_linear_dx": ([P, I64, I64, I64, P, P, P, I32, P, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -511,4 +516,88 @@ def qlora_linear_dx(dY, codes, c2, c1, K, G, L1, dX=None, stream=None):
     dX = _out(dX, "dX", torch.bfloat16, (M, K), dY)
     _check("qlora_linear_dx", lib().qlora_linear_dx(
         _ptr(dY), M, K, N, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(G), _ptr(L1), r, _ptr(dX), _stream(stream)))
+    return dX
+
+
+# --- LoRA over a bf16 base (same GEMM kernels, bf16 weight) --------------------
+
+def _bf16_weight(W, N, K):
+    return _need(W, "W", torch.bfloat16, shape=(N, K))
+
+
+def lora_linear_fwd(X, W, L1, L2, lora_scale=1.0, Y=None, T_out=None, workspace=None, stream=None):
+    """Y = bf16(X W^T + s T L2), T = bf16(X L1) with a bf16 base W [N, K]."""
+    _need(X, "X", torch.bfloat16, ndim=2)
+    M, K = X.shape
+    _need(W, "W", torch.bfloat16, ndim=2)
+    N = W.shape[0]
+    _bf16_weight(W, N, K)
+    r = _rank(L1, K)
+    _need(L2, "L2", torch.bfloat16, shape=(r, N))
+    Y = _out(Y, "Y", torch.bfloat16, (M, N), X)
+    T_out = _opt_out(T_out, "T_out", torch.bfloat16, (M, r), X)
+    ws = _workspace(qlora_linear_fwd_workspace(M, K, N, r), X, workspace)
+    _check("lora_linear_fwd", lib().lora_linear_fwd(
+        _ptr(X), M, K, N, _ptr(W), _ptr(L1), _ptr(L2), r, float(lora_scale), _ptr(Y), _ptr(T_out), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return Y, T_out
+
+
+def lora_linear_bwd(X, dY, W, L1, L2, lora_scale=1.0, T=None, dX=True, dL1=None, dL2=None, workspace=None,
+                    stream=None):
+    """(dX or None, dL1 fp32 [K, r], dL2 fp32 [r, N]) with a bf16 base W [N, K] (no gradient for W)."""
+    _need(X, "X", torch.bfloat16, ndim=2)
+    M, K = X.shape
+    _need(dY, "dY", torch.bfloat16, ndim=2)
+    if dY.shape[0] != M:
+        raise ValueError(f"dY must have {M} rows, got {tuple(dY.shape)}")
+    N = dY.shape[1]
+    _bf16_weight(W, N, K)
+    r = _rank(L1, K)
+    _need(L2, "L2", torch.bfloat16, shape=(r, N))
+    if T is not None:
+        _need(T, "T", torch.bfloat16, numel=M * r)
+    dX = _opt_out(dX, "dX", torch.bfloat16, (M, K), X)
+    dL1 = _out(dL1, "dL1", torch.float32, (K, r), X)
+    dL2 = _out(dL2, "dL2", torch.float32, (r, N), X)
+    ws = _workspace(qlora_linear_bwd_workspace(M, K, N, r), X, workspace)
+    _check("lora_linear_bwd", lib().lora_linear_bwd(
+        _ptr(X), _ptr(dY), M, K, N, _ptr(W), _ptr(L1), _ptr(L2), r, float(lora_scale), _ptr(T), _ptr(dX),
+        _ptr(dL1), _ptr(dL2), _ptr(ws), ws.numel(), _stream(stream)))
+    return dX, dL1, dL2
+
+
+def lora_linear_fwd_t(X, W, T, L2, lora_scale=1.0, Y=None, stream=None):
+    """Y = bf16(X W^T + s T L2) given T, bf16 base W [N, K] (one kernel)."""
+    _need(X, "X", torch.bfloat16, ndim=2)
+    M, K = X.shape
+    _need(W, "W", torch.bfloat16, ndim=2)
+    N = W.shape[0]
+    _bf16_weight(W, N, K)
+    _need(T, "T", torch.bfloat16, ndim=2)
+    if T.shape[0] != M:
+        raise ValueError(f"T must have {M} rows, got {tuple(T.shape)}")
+    r = T.shape[1]
+    _need(L2, "L2", torch.bfloat16, shape=(r, N))
+    Y = _out(Y, "Y", torch.bfloat16, (M, N), X)
+    _check("lora_linear_fwd_t", lib().lora_linear_fwd_t(
+        _ptr(X), M, K, N, _ptr(W), _ptr(T), _ptr(L2), r, float(lora_scale), _ptr(Y), _stream(stream)))
+    return Y
+
+
+def lora_linear_dx(dY, W, G, L1, dX=None, stream=None):
+    """dX = bf16(dY W + G L1^T) given G, bf16 base W [N, K] (one kernel)."""
+    _need(dY, "dY", torch.bfloat16, ndim=2)
+    M, N = dY.shape
+    _need(W, "W", torch.bfloat16, ndim=2)
+    K = W.shape[1]
+    _bf16_weight(W, N, K)
+    _need(G, "G", torch.bfloat16, ndim=2)
+    if G.shape[0] != M:
+        raise ValueError(f"G must have {M} rows, got {tuple(G.shape)}")
+    r = G.shape[1]
+    _need(L1, "L1", torch.bfloat16, shape=(K, r))
+    dX = _out(dX, "dX", torch.bfloat16, (M, K), dY)
+    _check("lora_linear_dx", lib().lora_linear_dx(
+        _ptr(dY), M, K, N, _ptr(W), _ptr(G), _ptr(L1), r, _ptr(dX), _stream(stream)))
     return dX

@@ -434,6 +434,71 @@ int qlora_linear_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const u
   return QL_OK;
 }
 
+// ---- LoRA over a bf16 base (the same GEMM kernels with a bf16 weight) -------
+int lora_linear_fwd_t(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* W, const uint16_t* T,
+                      const uint16_t* L2, int r, float lora_scale, uint16_t* Y, void* stream) {
+  if (!X || !W || !T || !L2 || !Y) return QL_ERR_NULL;
+  if (!shapes_ok(M, K, N, r) || !bgemm_ok(false, M, K, N)) return QL_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(T) || !aligned16(L2) || !aligned16(Y)) return QL_ERR_ALIGN;
+  QL_TRY(launch_bgemm_big(false, X, M, K, N, W, T, L2, r, lora_scale, Y, (hipStream_t)stream));
+  return QL_OK;
+}
+
+int lora_linear_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint16_t* W, const uint16_t* G,
+                   const uint16_t* L1, int r, uint16_t* dX, void* stream) {
+  if (!dY || !W || !G || !L1 || !dX) return QL_ERR_NULL;
+  if (!shapes_ok(M, K, N, r) || !bgemm_ok(true, M, K, N)) return QL_ERR_SHAPE;
+  if (!aligned16(dY) || !aligned16(W) || !aligned16(G) || !aligned16(L1) || !aligned16(dX)) return QL_ERR_ALIGN;
+  QL_TRY(launch_bgemm_big(true, dY, M, K, N, W, G, L1, r, 1.0f, dX, (hipStream_t)stream));
+  return QL_OK;
+}
+
+int lora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* W, const uint16_t* L1,
+                    const uint16_t* L2, int r, float lora_scale, uint16_t* Y, uint16_t* T_out, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  if (!X || !W || !L1 || !L2 || !Y) return QL_ERR_NULL;
+  if (!shapes_ok(M, K, N, r) || !bgemm_ok(false, M, K, N)) return QL_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) ||
+      (T_out && !aligned16(T_out)))
+    return QL_ERR_ALIGN;
+  const FwdWs w = fwd_ws(M, K, N, r);
+  if (!workspace || ws_bytes < w.total) return QL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  uint16_t* T = T_out ? T_out : (uint16_t*)ws;
+  QL_TRY(launch_lora_skinny(X, M, K, K, L1, true, r, 1.0f, T, (float*)(ws + w.t_bytes), s));
+  QL_TRY(launch_bgemm_big(false, X, M, K, N, W, T, L2, r, lora_scale, Y, s));
+  return QL_OK;
+}
+
+int lora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint16_t* W,
+                    const uint16_t* L1, const uint16_t* L2, int r, float lora_scale, const uint16_t* T, uint16_t* dX,
+                    float* dL1, float* dL2, void* workspace, size_t ws_bytes, void* stream) {
+  if (!X || !dY || !W || !L1 || !L2 || !dL1 || !dL2) return QL_ERR_NULL;
+  if (!shapes_ok(M, K, N, r) || !bgemm_ok(true, M, K, N)) return QL_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(W) || !aligned16(L1) || !aligned16(L2) || !aligned16(dL1) ||
+      !aligned16(dL2) || (T && !aligned16(T)) || (dX && !aligned16(dX)))
+    return QL_ERR_ALIGN;
+  const BwdWs w = bwd_ws(M, K, N, r);
+  if (!workspace || ws_bytes < w.total) return QL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  uint16_t* Tw = (uint16_t*)ws;
+  uint16_t* G = (uint16_t*)(ws + w.t_bytes);
+  float* part = (float*)(ws + w.t_bytes + w.g_bytes);
+  if (!T) {
+    QL_TRY(launch_lora_skinny(X, M, K, K, L1, true, r, 1.0f, Tw, part, s));
+    T = Tw;
+  }
+  QL_TRY(launch_lora_skinny(dY, M, N, N, L2, false, r, lora_scale, G, part, s));
+  if (dX) QL_TRY(launch_bgemm_big(true, dY, M, K, N, W, G, L1, r, 1.0f, dX, s));
+  QL_TRY(launch_lora_tn(X, K, G, M, K, r, 1.0f, false, dL1, part, s));
+  QL_TRY(launch_lora_tn(dY, N, T, M, N, r, lora_scale, true, dL2, part, s));
+  return QL_OK;
+}
+
 int qlora_nf4_levels(float* out16) {
   if (!out16) return QL_ERR_NULL;
   std::memcpy(out16, nf4_params().q, 16 * sizeof(float));

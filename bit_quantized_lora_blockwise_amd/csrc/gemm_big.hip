@@ -28,6 +28,8 @@
 //    (three byte selects per four nibbles and plane), so it needs no LDS reads.
 //  * Work groups are dispatched round-robin over the 8 XCDs; the tile order is
 //    remapped so that each XCD (with its own L2) gets a contiguous run of tiles.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace {
@@ -178,10 +180,26 @@ struct HalfCodes {
   float c1v;
 };
 
+// bf16-weight variant, dX: a thread's 64 bytes (32 columns) of one weight row.
+struct RowBytes {
+  u32x4 v[4];
+};
+struct NoStage {};
+
+template <bool kDx, bool kB16>
+using StageT = typename std::conditional<kB16, typename std::conditional<kDx, RowBytes, NoStage>::type,
+                                         HalfCodes>::type;
+
 // ---------------------------------------------------------------------------
 // kTail: dX with N not a multiple of 64 (the last step masks activation
 // columns past N).
-template <bool kDx, bool kTail>
+// kB16: the same kernel with a bf16 weight W [N, K] in place of the packed 4-bit
+// one (LoRA over a bf16 base, and the dequantise-then-GEMM strategy that gives
+// it the dequantised W'): the forward's weight tile is sent from global memory
+// straight into LDS like the activation tile (same layout and swizzle); the dX
+// weight tile [64 rows of W][256 columns] is staged through registers into a
+// padded LDS tile and read with the transposing LDS read.  No dequantisation.
+template <bool kDx, bool kTail, bool kB16 = false>
 __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict__ A, int64_t M, int64_t K,
                                                      int64_t N, const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ c2,
@@ -189,7 +207,8 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ LA,   // T (fwd) / G (dX)
                                                      const uint16_t* __restrict__ LB,   // L2 (fwd) / L1 (dX)
                                                      int r, float scale, uint16_t* __restrict__ C,
-                                                     Nf4Params p, int nseg, int64_t seg) {
+                                                     Nf4Params p, int nseg, int64_t seg,
+                                                     const uint16_t* __restrict__ Wb) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_b[2 * kBufElems];   // weight tiles; LoRA operands first
   __shared__ __attribute__((aligned(16))) uint16_t lds_a0[kBM * kBR];      // activation tiles (two buffers,
   __shared__ __attribute__((aligned(16))) uint16_t lds_a1[kBM * kBR];      //  filled by buffer-to-LDS loads)
@@ -202,6 +221,7 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   const int64_t P = kDx ? K : N;          // output columns
   const int64_t R = kDx ? N : K;          // reduction length
   const int64_t kblocks = K / qk::kBlock;
+  constexpr bool kPerm = kDx && !kB16;    // dX columns in the lookup order (0, 2, 4, 6, 1, 3, 5, 7)
 
   // ---- tile of this work group: XCD x = (linear id) % 8 takes a contiguous
   // run of tiles in row-major tile order.
@@ -273,8 +293,8 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
             const bf16x8 a = qk::frag_rowmajor(la, kPL, 64 * rg + 32 * i, 16 * s);
             // dX: the column of accumulator slot (l % 32) is dx_slot_col(l % 32)
             const bf16x8 b =
-                kDx ? *(const LDS_AS bf16x8*)(lb + (128 * ch + 32 * j + dx_slot_col(l & 31)) * kPL + 16 * s +
-                                              8 * (l >> 5))
+                kDx ? *(const LDS_AS bf16x8*)(lb + (128 * ch + 32 * j + (kPerm ? dx_slot_col(l & 31) : (l & 31))) *
+                                                       kPL + 16 * s + 8 * (l >> 5))
                     : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
             z = qk::mfma32(a, b, z);
           }
@@ -308,11 +328,13 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   // Tile st goes straight from global memory into the LDS buffer: each wave's
   // load j fills rows 64 (w % 4) + 32 (w / 4) + 8 j .. +8 in lane order (lane l:
   // 16 bytes at 16 l), the lane's global offset carrying the chunk swizzle.
-  auto dma_a = [&](int64_t st, LDS_AS uint16_t* abuf) {
+  // The bf16-weight forward sends its weight tile (rows p0 .. p0 + 255 of W,
+  // the same row length R = K) the same way.
+  auto dma_tile = [&](const uint16_t* src, int64_t rows, int64_t r0, int64_t st, LDS_AS uint16_t* abuf) {
     const int64_t left = R - st * kBR;
     const int rem = __builtin_amdgcn_readfirstlane((int)(left < kBR ? left : kBR));   // columns in this step
-    const uint64_t nrec = rem > 0 ? (uint64_t)(M - m0) * R * 2 - (uint64_t)st * kBR * 2 : 0;
-    const uint64_t base = (uint64_t)(uintptr_t)(A + m0 * R + (rem > 0 ? st * kBR : 0));
+    const uint64_t nrec = rem > 0 ? (uint64_t)(rows - r0) * R * 2 - (uint64_t)st * kBR * 2 : 0;
+    const uint64_t base = (uint64_t)(uintptr_t)(src + r0 * R + (rem > 0 ? st * kBR : 0));
     const uint16_t* pa = (const uint16_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
                                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base));
     const __amdgpu_buffer_rsrc_t ra = rsrc(pa, (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)nrec));
@@ -336,6 +358,8 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
           : "memory");
     }
   };
+  auto dma_a = [&](int64_t st, LDS_AS uint16_t* abuf) { dma_tile(A, M, m0, st, abuf); };
+  auto dma_w = [&](int64_t st, LDS_AS uint16_t* bbuf) { dma_tile(Wb, N, p0, st, bbuf); };
   // A fragment of sub-step s, tile i: row 64 (w % 4) + 32 i + l % 32, chunk 2 s + l / 32.
   uint32_t afrag_off[4];
 #pragma unroll
@@ -343,6 +367,30 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     afrag_off[s] = (uint32_t)((64 * rg + (l & 31)) * kBR * 2 + 16 * ((2 * s + (l >> 5)) ^ ((l >> 1) & 7)));
   auto afrag = [&](const LDS_AS uint16_t* abuf, int s, int i) {
     return *(const LDS_AS bf16x8*)((const LDS_AS char*)abuf + afrag_off[s] + 32 * kBR * 2 * i);
+  };
+
+  // ---- bf16 weight tiles (kB16).  Forward: B fragment of column p from the
+  // DMA'd [p][k] tile, addressed like the A fragments.  dX: thread t loads 64
+  // bytes of row 64 step + t / 8 of W (columns p0 + 32 (t % 8) .. +32) two steps
+  // ahead and stores them into the [n][p] tile of pitch kPD.
+  const __amdgpu_buffer_rsrc_t rw = rsrc(Wb, kB16 ? (uint64_t)N * K * 2 : 0);
+  auto wfrag = [&](const LDS_AS uint16_t* bbuf, int s, int j) {
+    return *(const LDS_AS bf16x8*)((const LDS_AS char*)bbuf + afrag_off[s] - (64 * rg) * kBR * 2 +
+                                   (128 * ch + 32 * j) * kBR * 2);
+  };
+  auto load_wrow = [&](int64_t step) {
+    RowBytes rb_;
+    const int64_t wrow = step * kBR + (t >> 3);
+    const int64_t col = p0 + 32 * (t & 7);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = wrow < N && col + 8 * q < K;
+      rb_.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? (uint32_t)((wrow * K + col + 8 * q) * 2) : kOOB, 0, 0);
+    }
+    return rb_;
+  };
+  auto store_wrow = [&](const RowBytes& rb_, LDS_AS uint16_t* buf, int q) {
+    *(LDS_AS u32x4*)(buf + (t >> 3) * kPD + 32 * (t & 7) + 8 * q) = rb_.v[q];
   };
 
   // ---- weight tiles.  The thread pair (2 u, 2 u + 1) owns one block per step,
@@ -397,21 +445,27 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   LDS_AS uint16_t* a0 = (LDS_AS uint16_t*)lds_a0;
   LDS_AS uint16_t* a1 = (LDS_AS uint16_t*)lds_a1;
   const int64_t nsteps = (R + kBR - 1) / kBR;
+  using Stage = StageT<kDx, kB16>;
   auto step = [&](int64_t st, const LDS_AS uint16_t* acur, LDS_AS uint16_t* anext, const LDS_AS uint16_t* bcur,
-                  LDS_AS uint16_t* bnext, const HalfCodes& hc_now, HalfCodes& hc_later) {
+                  LDS_AS uint16_t* bnext, const Stage& hc_now, Stage& hc_later) {
     // Nothing is in flight here but, on the first step, the loads issued before
     // the loop: waiting for them explicitly tells the compiler's wait tracking
     // that the codes of this step have arrived, so that it places no wait after
     // the loads to LDS below (which it cannot count, and would wait for).
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     dma_a(st + 1, anext);
-    hc_later = load_codes(st + 2);
+    if constexpr (kB16 && !kDx) dma_w(st + 1, bnext);
+    else if constexpr (kB16) hc_later = load_wrow(st + 2);
+    else hc_later = load_codes(st + 2);
     __builtin_amdgcn_sched_barrier(0);
-    const BlockLut L = make_lut(qk::e4m3fn_to_f32(hc_now.c2b) * hc_now.c1v, p);
+    BlockLut L;
+    if constexpr (!kB16) L = make_lut(qk::e4m3fn_to_f32(hc_now.c2b) * hc_now.c1v, p);
     // fragments of sub-step s + 1 are read from LDS while sub-step s runs
     auto bfrag = [&](int s, int j) {
-      return kDx ? frag_planes((const LDS_AS uint8_t*)bcur, 16 * s, 128 * ch + 32 * j)
-                 : qk::frag_rowmajor(bcur, kPF, 128 * ch + 32 * j, 16 * s);
+      if constexpr (kB16) return kDx ? qk::frag_kmajor(bcur, kPD, 16 * s, 128 * ch + 32 * j) : wfrag(bcur, s, j);
+      else
+        return kDx ? frag_planes((const LDS_AS uint8_t*)bcur, 16 * s, 128 * ch + 32 * j)
+                   : qk::frag_rowmajor(bcur, kPF, 128 * ch + 32 * j, 16 * s);
     };
     bf16x8 bq[2][4], aq[2][2];
 #pragma unroll
@@ -431,17 +485,26 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
         acc[0][j] = qk::mfma32(aq[s & 1][0], bq[s & 1][j], acc[0][j]);
         acc[1][j] = qk::mfma32(aq[s & 1][1], bq[s & 1][j], acc[1][j]);
       }
-      // one 8-weight group of the next weight tile per sub-step
-      store8(L, hc_now.c[s], bnext, s);
-      // schedule: the next sub-step's fragment reads first, then one MFMA at a
-      // time interleaved with the dequantisation VALU work, then the LDS store
-      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 10 : 6, 0);   // DS read
+      if constexpr (kB16) {
+        // the bf16 weight: a quarter of the thread's row bytes per sub-step (dX);
+        // the forward's tile is already on its way to LDS
+        if constexpr (kDx) store_wrow(hc_now, bnext, s);
+        if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 10 : 6, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                         // MFMA
+        if constexpr (kDx) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // DS write
+      } else {
+        // one 8-weight group of the next weight tile per sub-step
+        store8(L, hc_now.c[s], bnext, s);
+        // schedule: the next sub-step's fragment reads first, then one MFMA at a
+        // time interleaved with the dequantisation VALU work, then the LDS store
+        if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 10 : 6, 0);   // DS read
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                         // VALU
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                         // VALU
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, kDx ? 2 : 1, 0);                 // DS write
       }
-      __builtin_amdgcn_sched_group_barrier(0x200, kDx ? 2 : 1, 0);                 // DS write
     }
     __builtin_amdgcn_sched_barrier(0);
     // activation tile st + 1 has landed and this wave's LDS stores are done; the
@@ -449,12 +512,21 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), seen by the compiler's wait tracking
     __builtin_amdgcn_s_barrier();
   };
-  HalfCodes hA, hB;
+  Stage hA, hB;
   {
     dma_a(0, a0);
-    const HalfCodes h0 = load_codes(0);
-    hA = load_codes(1);
-    dequant_store(h0, b0);
+    if constexpr (kB16 && !kDx) {
+      dma_w(0, b0);
+    } else if constexpr (kB16) {
+      const RowBytes h0 = load_wrow(0);
+      hA = load_wrow(1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) store_wrow(h0, b0, q);
+    } else {
+      const HalfCodes h0 = load_codes(0);
+      hA = load_codes(1);
+      dequant_store(h0, b0);
+    }
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), seen by the compiler's wait tracking
     __builtin_amdgcn_s_barrier();
   }
@@ -471,7 +543,7 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t pc = p0 + 128 * ch + 32 * j + (kDx ? dx_slot_col(qk::acc_col()) : qk::acc_col());
+      const int64_t pc = p0 + 128 * ch + 32 * j + (kPerm ? dx_slot_col(qk::acc_col()) : qk::acc_col());
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + 64 * rg + 32 * i + qk::acc_row(e);
@@ -494,14 +566,41 @@ hipError_t launch_qgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, in
   const int64_t P = dx ? K : N;
   const int64_t seg = N / nseg;   // columns of W per segment (a multiple of 256 when nseg > 1)
   dim3 grid((unsigned)((P + kBP - 1) / kBP), (unsigned)((M + kBM - 1) / kBM));
+  const uint16_t* nw = nullptr;
   if (!dx)
     hipLaunchKernelGGL((k_qgemm_big<false, false>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
-                       scale, C, nf4_params(), nseg, seg);
+                       scale, C, nf4_params(), nseg, seg, nw);
   else if (N % kBR == 0)
     hipLaunchKernelGGL((k_qgemm_big<true, false>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
-                       scale, C, nf4_params(), nseg, seg);
+                       scale, C, nf4_params(), nseg, seg, nw);
   else
     hipLaunchKernelGGL((k_qgemm_big<true, true>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
-                       scale, C, nf4_params(), nseg, seg);
+                       scale, C, nf4_params(), nseg, seg, nw);
+  return hipGetLastError();
+}
+
+bool bgemm_ok(bool dx, int64_t M, int64_t K, int64_t N) {
+  // 32-bit buffer offsets into the activations and the bf16 weight; 16-byte
+  // aligned rows of the activations and of W (K % 8 == 0, N % 8 == 0)
+  (void)dx;
+  return (K % 8) == 0 && (N % 8) == 0 && M * K * 2 < (int64_t(1) << 31) && M * N * 2 < (int64_t(1) << 31) &&
+         N * K * 2 < (int64_t(1) << 31);
+}
+
+hipError_t launch_bgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, int64_t N, const uint16_t* W,
+                            const uint16_t* LA, const uint16_t* LB, int r, float scale, uint16_t* C, hipStream_t s) {
+  const int64_t P = dx ? K : N;
+  dim3 grid((unsigned)((P + kBP - 1) / kBP), (unsigned)((M + kBM - 1) / kBM));
+  const uint8_t* nc = nullptr;
+  const float* nf = nullptr;
+  if (!dx)
+    hipLaunchKernelGGL((k_qgemm_big<false, false, true>), grid, dim3(kT), 0, s, A, M, K, N, nc, nc, nf, LA, LB, r,
+                       scale, C, nf4_params(), 1, N, W);
+  else if (N % kBR == 0)
+    hipLaunchKernelGGL((k_qgemm_big<true, false, true>), grid, dim3(kT), 0, s, A, M, K, N, nc, nc, nf, LA, LB, r,
+                       scale, C, nf4_params(), 1, N, W);
+  else
+    hipLaunchKernelGGL((k_qgemm_big<true, true, true>), grid, dim3(kT), 0, s, A, M, K, N, nc, nc, nf, LA, LB, r,
+                       scale, C, nf4_params(), 1, N, W);
   return hipGetLastError();
 }

@@ -107,6 +107,12 @@ bool qgemm_big_ok(bool dx, int64_t M, int64_t K, int64_t N);
 hipError_t launch_qgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                             const uint8_t* c2, const float* c1, const uint16_t* LA, const uint16_t* LB, int r,
                             float scale, uint16_t* C, hipStream_t s, int nseg = 1);
+// The same two GEMMs with a bf16 weight W [N, K] in place of the packed one
+// (LoRA over a bf16 base): dx = false Y = bf16(X W^T + scale T L2), dx = true
+// dX = bf16(dY W + G L1^T).  bgemm_ok says whether the shapes qualify.
+bool bgemm_ok(bool dx, int64_t M, int64_t K, int64_t N);
+hipError_t launch_bgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, int64_t N, const uint16_t* W,
+                            const uint16_t* LA, const uint16_t* LB, int r, float scale, uint16_t* C, hipStream_t s);
 // dX[M, K] = bf16(dY W' + G L1^T)
 hipError_t launch_qgemm_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                            const uint8_t* c2, const float* c1, const uint16_t* G, const uint16_t* L1, int r,

@@ -293,6 +293,37 @@ int q4_dequantize(const uint8_t* codes, int64_t rows, int64_t cols, int codebook
  * an unknown id).                                                               */
 int q4_levels(int codebook, float* out16);
 
+/* LoRA over a bf16 base: the same layer with a 16-bit frozen weight W [N, K]
+ * (bf16, row-major, out x in) in place of the 4-bit one, computed by the same
+ * GEMM kernels with the dequantisation replaced by plain bf16 tile loads. This
+ * is the baseline the pages compare QLoRA with (examadda page, "The Trade-off:
+ * Speed": QLoRA trains more slowly than LoRA because the 4-bit weights are
+ * dequantised on every pass; inferensys glossary, paragraph on the
+ * dequantising kernel: the overhead is small where the product is
+ * compute-bound), and with W = nf4_dequantize(...) it is the
+ * dequantise-then-multiply strategy.
+ *   lora_linear_fwd:   T = bf16(X L1), Y = bf16(X W^T + lora_scale T L2)
+ *   lora_linear_bwd:   G = bf16(lora_scale dY L2^T), dX = bf16(dY W + G L1^T)
+ *                      (NULL: skipped), dL1 = fp32(X^T G), dL2 = fp32(lora_scale T^T dY);
+ *                      W gets no gradient.
+ *   lora_linear_fwd_t: Y given T (one kernel);  lora_linear_dx: dX given G (one kernel).
+ * Shapes, layouts, alignment and errors as qlora_linear_*, with W replacing
+ * codes/c2/c1; workspaces as qlora_linear_fwd_workspace / _bwd_workspace; also
+ * QL_ERR_SHAPE unless N % 8 == 0 (rows of dY and W are read in 16-byte pieces),
+ * or when W (2 N K bytes) or an activation matrix reaches 2^31 bytes.          */
+int lora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* W,
+                    const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
+                    uint16_t* Y, uint16_t* T_out, void* workspace, size_t ws_bytes, void* stream);
+int lora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K, int64_t N,
+                    const uint16_t* W, const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
+                    const uint16_t* T, uint16_t* dX, float* dL1, float* dL2,
+                    void* workspace, size_t ws_bytes, void* stream);
+int lora_linear_fwd_t(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* W,
+                      const uint16_t* T, const uint16_t* L2, int r, float lora_scale,
+                      uint16_t* Y, void* stream);
+int lora_linear_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint16_t* W,
+                   const uint16_t* G, const uint16_t* L1, int r, uint16_t* dX, void* stream);
+
 /* Host-only helpers (no GPU needed). */
 /* The 16 NF4 levels (fp32, ascending) that the kernels use, copied to out[16].  */
 int qlora_nf4_levels(float* out16);

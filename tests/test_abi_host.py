@@ -348,3 +348,26 @@ def test_noalloc_forward_validation():
     assert L.qlora_linear_fwd_noalloc(A, 64, 512, 256, A, A, A, A, A, 65, 1.0, A, None, None) == -2
     assert L.qlora_linear_fwd_noalloc(A, 64, 512, 256, A, A, A, A, A, 8, 1.0, MIS, None, None) == -4
     assert L.qlora_linear_fwd_noalloc(A, 64, 512, 256, A, A, A, A, A, 8, 1.0, A, MIS, None) == -4
+
+
+def test_bf16_base_layer_validation():
+    _, L = _lib()
+    M, K, N, r = 64, 512, 256, 8
+    ws = L.qlora_linear_fwd_workspace(M, K, N, r)
+    fwd = lambda X=A, W=A, K=K, r=r, Y=A, ws_b=ws: L.lora_linear_fwd(X, M, K, N, W, A, A, r, 1.0, Y, None, A, ws_b,
+                                                                     None)
+    assert fwd(W=None) == -1
+    assert fwd(K=500) == -2
+    assert fwd(r=0) == -2
+    assert fwd(Y=MIS) == -4
+    assert fwd(ws_b=ws - 1) == -5
+    wb = L.qlora_linear_bwd_workspace(M, K, N, r)
+    bwd = lambda W=A, dL2=A, ws_b=wb: L.lora_linear_bwd(A, A, M, K, N, W, A, A, r, 1.0, None, None, A, dL2, A, ws_b,
+                                                        None)
+    assert bwd(W=None) == -1
+    assert bwd(dL2=MIS) == -4
+    assert bwd(ws_b=wb - 256) == -5
+    assert L.lora_linear_fwd_t(A, M, K, N, None, A, A, r, 1.0, A, None) == -1
+    assert L.lora_linear_fwd_t(A, M, K, N, A, A, A, 65, 1.0, A, None) == -2
+    assert L.lora_linear_dx(A, M, K, N, A, A, MIS, r, A, None) == -4
+    assert L.lora_linear_dx(A, M, K, 1 << 31, A, A, A, r, A, None) == -2     # W beyond 2^31 bytes
