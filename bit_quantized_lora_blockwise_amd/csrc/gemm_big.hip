@@ -5,27 +5,28 @@
 // paragraph; the frozen base is dequantised on the fly (examadda page, "The
 // Core Idea"; inferensys glossary, paragraph on the dequantising kernel).
 //
-// Tile: 256 activation rows x 256 output columns, reduction steps of 64.
-// 512 threads = eight waves, two per SIMD, so that the dequantisation VALU
-// work of one wave fills the gaps between the MFMAs of the other (a single
-// wave barely overlaps its own VALU work with its MFMAs on gfx950).  Wave w
-// owns rows 64 (w % 4) .. +64 and columns 128 (w / 4) .. +128 of the tile:
-// 2 x 4 MFMA 32x32x16 tiles, 128 fp32 accumulators per lane.
-//  * Activation tile of a step (256 x 64 bf16): at the start of the step
-//    before, each wave sends 32 of its rows (eight rows of 128 bytes per
-//    16-byte-per-lane load) from global memory straight into the other buffer
-//    of a double-buffered LDS tile (buffer loads to LDS: no registers, no LDS
-//    store instructions), XOR-swizzled through the lanes' global offsets so that
-//    fragment reads are free of bank conflicts.  The two waves of a row group
-//    both read from it.
-//  * Weight tile (256 x 64): rebuilt from the packed 4-bit stream once per work
-//    group; each pair of threads owns one first-level block (64 weights) and
-//    each thread converts half of it per step into a double-buffered LDS tile.
-//    The forward reads B fragments directly, the dX path (where the reduction
-//    runs across the stored rows of W) through ds_read_b64_tr_b16.
+// Tile: 256 activation rows x 256 output columns, reduction steps of 64, in
+// double-buffered LDS tiles.  768 threads = twelve waves in two roles:
+//  * eight consumer waves (two per SIMD) only read fragments from LDS and
+//    issue MFMA 32x32x16 bf16: wave c owns rows 64 (c % 4) .. +64 and columns
+//    128 (c / 4) .. +128 of the tile, 2 x 4 MFMA tiles, 128 fp32 accumulators
+//    per lane;
+//  * four producer waves (one per SIMD) fill the other buffers for the next
+//    step: the activation tile (256 x 64 bf16) goes from global memory straight
+//    into LDS (buffer loads to LDS, XOR-swizzled through the lanes' global
+//    offsets so that fragment reads are free of bank conflicts), and each
+//    producer lane rebuilds one first-level block (64 weights) of the weight
+//    tile from the packed 4-bit stream, loaded two steps ahead.
+// The roles are split because a wave's own VALU work barely overlaps its own
+// MFMAs on gfx950, while MFMA and VALU instructions of different waves on one
+// SIMD co-issue: separating them measured 6-13% faster than eight waves that
+// each did both.  One barrier per step hands the new buffers over.
 //  * Dequantisation keeps the block's 16 bf16 values W'(v) = bf16(fl32(q[v] s'))
 //    in registers as two byte planes and looks each nibble up with v_perm_b32
 //    (three byte selects per four nibbles and plane), so it needs no LDS reads.
+//    The forward's weight tile is [column][k] bf16 (plain fragment reads); the
+//    dX path (where the reduction runs across the stored rows of W) keeps it as
+//    byte planes read with ds_read_b64_tr_b8, which interleaves the planes.
 //  * Work groups are dispatched round-robin over the 8 XCDs; the tile order is
 //    remapped so that each XCD (with its own L2) gets a contiguous run of tiles.
 #include <type_traits>
@@ -34,7 +35,8 @@
 
 namespace {
 
-constexpr int kT = 512;           // threads per work group
+constexpr int kT = 768;           // threads per work group: 8 consumer + 4 producer waves
+constexpr int kTC = 512;          // consumer threads
 constexpr int kBM = 256;          // activation rows per tile
 constexpr int kBP = 256;          // output columns per tile
 constexpr int kBR = 64;           // reduction per step
@@ -173,32 +175,42 @@ __device__ __forceinline__ bf16x8 frag_planes(const LDS_AS uint8_t* base, int k0
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Half a block's packed codes (32 weights), its scale byte and group scale.
-struct HalfCodes {
-  u32x4 c;
+// What a producer lane loads for one step of the packed weight: a block's 32
+// bytes of codes with its scale byte and group scale (the bf16 weight goes
+// straight to LDS and needs none).
+struct BlockCodes {
+  u32x4 v[2];
   uint32_t c2b;
   float c1v;
 };
+struct NoCodes {};
 
-// bf16-weight variant, dX: a thread's 64 bytes (32 columns) of one weight row.
-struct RowBytes {
-  u32x4 v[4];
-};
-struct NoStage {};
+// bf16 dX weight tile [64 rows of W][256 columns], rows of 512 bytes: 16-byte
+// chunk c of row k is kept in slot c ^ (4 (k % 4)), so that the 4 rows x 64
+// bytes that 32 lanes of a transposed read touch fall on distinct banks.
+__device__ __forceinline__ bf16x8 frag_kmajor_sw(const LDS_AS uint16_t* base, int k0, int col0) {
+  const int l = threadIdx.x & 63;
+  const int G = l >> 4, i = l & 15;
+  const int row = k0 + ((G >> 1) << 3) + (i >> 2);
+  const int col = col0 + ((G & 1) << 4) + ((i & 3) << 2);
+  const int off = row * 512 + 16 * ((col >> 3) ^ (4 * (row & 3))) + 2 * (col & 7);
+  const LDS_AS char* pb = (const LDS_AS char*)base + off;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)pb);
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(pb + 4 * 512));
+  u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  u32x4 v = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
 
-template <bool kDx, bool kB16>
-using StageT = typename std::conditional<kB16, typename std::conditional<kDx, RowBytes, NoStage>::type,
-                                         HalfCodes>::type;
-
-// ---------------------------------------------------------------------------
 // kTail: dX with N not a multiple of 64 (the last step masks activation
 // columns past N).
 // kB16: the same kernel with a bf16 weight W [N, K] in place of the packed 4-bit
 // one (LoRA over a bf16 base, and the dequantise-then-GEMM strategy that gives
-// it the dequantised W'): the forward's weight tile is sent from global memory
-// straight into LDS like the activation tile (same layout and swizzle); the dX
-// weight tile [64 rows of W][256 columns] is staged through registers into a
-// padded LDS tile and read with the transposing LDS read.  No dequantisation.
+// it the dequantised W'): the producers send the forward's weight tile from
+// global memory straight into LDS like the activation tile (same layout and
+// swizzle), or stage the dX weight tile [64 rows of W][256 columns] through
+// registers into a padded LDS tile that the consumers read with the transposing
+// LDS read.  No dequantisation.
 template <bool kDx, bool kTail, bool kB16 = false>
 __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict__ A, int64_t M, int64_t K,
                                                      int64_t N, const uint8_t* __restrict__ codes,
@@ -214,10 +226,8 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) uint16_t lds_a1[kBM * kBR];      //  filled by buffer-to-LDS loads)
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
-  SplitConst kc;
-  asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
-  asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
-  const int rg = w & 3, ch = w >> 2;      // row group (64 rows), column half (128 columns)
+  const bool producer = w >= 8;           // uniform per wave
+  const int rg = w & 3, ch = (w >> 2) & 1;  // consumers: row group (64 rows), column half (128 columns)
   const int64_t P = kDx ? K : N;          // output columns
   const int64_t R = kDx ? N : K;          // reduction length
   const int64_t kblocks = K / qk::kBlock;
@@ -236,73 +246,77 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   }
 
   f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  // ---- LoRA term first: fwd acc = s * (T L2); dX acc = G L1^T (rank zero-padded
-  //      to 64); the base product then accumulates onto it.  With nseg > 1
-  //      segments of seg output columns (fwd) or reduction columns (dX), each
-  //      segment g has its own T_g / G_g [M, r] (at LA + g M r) and L2_g [r, seg]
-  //      (at LB + g r seg) / L1_g [K, r] (at LB + g K r): the forward tile uses
-  //      its own segment's pair (tiles never straddle segments), the dX tile
-  //      sums the products of all segments.
+  // ---- LoRA term first (consumers): fwd acc = s * (T L2); dX acc = G L1^T
+  //      (rank zero-padded to 64); the base product then accumulates onto it.
+  //      With nseg > 1 segments of seg output columns (fwd) or reduction
+  //      columns (dX), each segment g has its own T_g / G_g [M, r] (at LA + g M r)
+  //      and L2_g [r, seg] (at LB + g r seg) / L1_g [K, r] (at LB + g K r): the
+  //      forward tile uses its own segment's pair (tiles never straddle
+  //      segments), the dX tile sums the products of all segments.
   {
     LDS_AS uint16_t* la = (LDS_AS uint16_t*)lds_b;                 // [256][kPL]: T / G rows
     LDS_AS uint16_t* lb = (LDS_AS uint16_t*)lds_b + kBM * kPL;     // fwd: L2 [64][kPD]; dX: L1 [256][kPL]
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     const int ng = kDx ? nseg : 1;
     for (int g = 0; g < ng; ++g) {
       const int64_t gs = kDx ? g : p0 / seg;
-      const uint16_t* la_src = LA + gs * M * r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (m0 + row < M) v = load_row8(la_src + (m0 + row) * r, cc, r);
-        *(LDS_AS u32x4*)(la + row * kPL + cc) = v;
-      }
-      if (!kDx) {
-        const uint16_t* lb_src = LB + gs * r * seg;
-        const int64_t pc = p0 - gs * seg;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = (t >> 5) + 16 * i, pp = (t & 31) * 8;
-          u32x4 v = {0, 0, 0, 0};
-          if (c < r) v = load_row8(lb_src + (int64_t)c * seg, pc + pp, seg);
-          *(LDS_AS u32x4*)(lb + c * kPD + pp) = v;
-        }
-      } else {
-        const uint16_t* lb_src = LB + gs * K * r;
+      if (!producer) {
+        const uint16_t* la_src = LA + gs * M * r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
           u32x4 v = {0, 0, 0, 0};
-          if (p0 + row < K) v = load_row8(lb_src + (p0 + row) * r, cc, r);
-          *(LDS_AS u32x4*)(lb + row * kPL + cc) = v;
+          if (m0 + row < M) v = load_row8(la_src + (m0 + row) * r, cc, r);
+          *(LDS_AS u32x4*)(la + row * kPL + cc) = v;
+        }
+        if (!kDx) {
+          const uint16_t* lb_src = LB + gs * r * seg;
+          const int64_t pc = p0 - gs * seg;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = (t >> 5) + 16 * i, pp = (t & 31) * 8;
+            u32x4 v = {0, 0, 0, 0};
+            if (c < r) v = load_row8(lb_src + (int64_t)c * seg, pc + pp, seg);
+            *(LDS_AS u32x4*)(lb + c * kPD + pp) = v;
+          }
+        } else {
+          const uint16_t* lb_src = LB + gs * K * r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
+            u32x4 v = {0, 0, 0, 0};
+            if (p0 + row < K) v = load_row8(lb_src + (p0 + row) * r, cc, r);
+            *(LDS_AS u32x4*)(lb + row * kPL + cc) = v;
+          }
         }
       }
       __syncthreads();
-      const int ksteps = (r + 15) / 16;
+      if (!producer) {
+        const int ksteps = (r + 15) / 16;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x16 z = acc[i][j];
-          for (int s = 0; s < ksteps; ++s) {
-            const bf16x8 a = qk::frag_rowmajor(la, kPL, 64 * rg + 32 * i, 16 * s);
-            // dX: the column of accumulator slot (l % 32) is dx_slot_col(l % 32)
-            const bf16x8 b =
-                kDx ? *(const LDS_AS bf16x8*)(lb + (128 * ch + 32 * j + (kPerm ? dx_slot_col(l & 31) : (l & 31))) *
-                                                       kPL + 16 * s + 8 * (l >> 5))
-                    : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
-            z = qk::mfma32(a, b, z);
+          for (int j = 0; j < 4; ++j) {
+            f32x16 z = acc[i][j];
+            for (int s = 0; s < ksteps; ++s) {
+              const bf16x8 a = qk::frag_rowmajor(la, kPL, 64 * rg + 32 * i, 16 * s);
+              // dX: the column of accumulator slot (l % 32) is dx_slot_col(l % 32)
+              const bf16x8 b =
+                  kDx ? *(const LDS_AS bf16x8*)(lb + (128 * ch + 32 * j + (kPerm ? dx_slot_col(l & 31) : (l & 31))) *
+                                                         kPL + 16 * s + 8 * (l >> 5))
+                      : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
+              z = qk::mfma32(a, b, z);
+            }
+            acc[i][j] = z;
           }
-          acc[i][j] = z;
-        }
+      }
       __syncthreads();
     }
-    if (!kDx) {
+    if (!kDx && !producer) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -310,57 +324,185 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     }
   }
 
-  // ---- activation tiles.  Wave w loads rows 64 (w % 4) + 32 (w / 4) .. +32 of
-  // the tile, eight rows per 16-byte load (lane l: row + l / 8, slot l % 8).
-  // In LDS, row rho keeps its 16-byte chunk c in slot c ^ ((rho >> 1) & 7): the
-  // lane loads chunk (l % 8) ^ (that swizzle) and stores linearly.
-  uint32_t achunk[2], arow_off[4];
-  achunk[0] = (uint32_t)((l & 7) ^ (l >> 4));     // rows with (rho >> 1) & 7 = l / 16
-  achunk[1] = achunk[0] ^ 4u;                     // rows with (rho >> 1) & 7 = 4 + l / 16
+  LDS_AS uint16_t* b0 = (LDS_AS uint16_t*)lds_b;
+  LDS_AS uint16_t* b1 = (LDS_AS uint16_t*)lds_b + kBufElems;
+  LDS_AS uint16_t* a0 = (LDS_AS uint16_t*)lds_a0;
+  LDS_AS uint16_t* a1 = (LDS_AS uint16_t*)lds_a1;
+  const int64_t nsteps = (R + kBR - 1) / kBR;
+
+  if (producer) {
+    // ================================ producers ================================
+    // At the top of step st the consumers multiply tiles st; the producers send
+    // activation tile st + 1 (and, bf16 forward, weight tile st + 1) into the
+    // other buffers, issue the loads for step st + 2, rebuild weight tile st + 1
+    // from the codes loaded during the step before, and wait for all of it
+    // before the barrier that ends the step.
+    const int pw = w - 8;                 // producer wave 0..3
+    const int tp = t - kTC;               // producer thread 0..255
+    SplitConst kc;
+    asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
+    asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
+
+    // Activation (and bf16 forward weight) tiles: producer wave pw sends rows
+    // 64 pw .. +64, eight rows of 128 bytes per 16-byte-per-lane load (lane l:
+    // row + l / 8, written at LDS base + 16 l).  In LDS, row rho keeps its
+    // 16-byte chunk c in slot c ^ ((rho >> 1) & 7): the lane loads chunk
+    // (l % 8) ^ (that swizzle).
+    uint32_t achunk[2], arow_off[8];
+    achunk[0] = (uint32_t)((l & 7) ^ (l >> 4));     // rows with (rho >> 1) & 7 = l / 16
+    achunk[1] = achunk[0] ^ 4u;                     // rows with (rho >> 1) & 7 = 4 + l / 16
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 64 * rg + 32 * ch + 8 * j + (l >> 3);
-    arow_off[j] = (uint32_t)((int64_t)row * R * 2) + 16u * achunk[j & 1];
-  }
-  // Step st reads through a descriptor based at column 64 st of the tile's first
-  // row whose size ends at the end of A: rows past M read as zeros, and a step
-  // past the reduction has size 0.
-  // Tile st goes straight from global memory into the LDS buffer: each wave's
-  // load j fills rows 64 (w % 4) + 32 (w / 4) + 8 j .. +8 in lane order (lane l:
-  // 16 bytes at 16 l), the lane's global offset carrying the chunk swizzle.
-  // The bf16-weight forward sends its weight tile (rows p0 .. p0 + 255 of W,
-  // the same row length R = K) the same way.
-  auto dma_tile = [&](const uint16_t* src, int64_t rows, int64_t r0, int64_t st, LDS_AS uint16_t* abuf) {
-    const int64_t left = R - st * kBR;
-    const int rem = __builtin_amdgcn_readfirstlane((int)(left < kBR ? left : kBR));   // columns in this step
-    const uint64_t nrec = rem > 0 ? (uint64_t)(rows - r0) * R * 2 - (uint64_t)st * kBR * 2 : 0;
-    const uint64_t base = (uint64_t)(uintptr_t)(src + r0 * R + (rem > 0 ? st * kBR : 0));
-    const uint16_t* pa = (const uint16_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
-                                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base));
-    const __amdgpu_buffer_rsrc_t ra = rsrc(pa, (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)nrec));
-    const bool ok0 = !kTail || 8 * (int)achunk[0] < rem;    // chunks past the reduction read as zeros
-    const bool ok1 = !kTail || 8 * (int)achunk[1] < rem;
-    // Issued from inline assembly, which writes no register: the compiler's
-    // own wait counting only over-waits around it, and it does not make every
-    // LDS read of the step wait for these loads (the builtin does, as it cannot
-    // tell the buffers apart); the barrier at the end of the step waits for them.
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t dst = (uint32_t)(uintptr_t)(abuf + (64 * rg + 32 * ch + 8 * j) * kBR);
-      const uint32_t vo = ((j & 1) ? ok1 : ok0) ? arow_off[j] : kOOB;
-      // M0 (the LDS address, read when the load issues) is saved and restored
-      // here, since the compiler does not track it across inline assembly
-      uint32_t m0_saved;
-      asm volatile(
-          "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-          : "=&s"(m0_saved)
-          : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(vo), "s"(ra)
-          : "memory");
+    for (int j = 0; j < 8; ++j) {
+      const int row = 64 * pw + 8 * j + (l >> 3);
+      arow_off[j] = (uint32_t)((int64_t)row * R * 2) + 16u * achunk[j & 1];
     }
-  };
-  auto dma_a = [&](int64_t st, LDS_AS uint16_t* abuf) { dma_tile(A, M, m0, st, abuf); };
-  auto dma_w = [&](int64_t st, LDS_AS uint16_t* bbuf) { dma_tile(Wb, N, p0, st, bbuf); };
-  // A fragment of sub-step s, tile i: row 64 (w % 4) + 32 i + l % 32, chunk 2 s + l / 32.
+    // Step st of a matrix with `rows` rows from row r0 goes through a descriptor
+    // based at column 64 st of row r0 whose size ends at the end of the matrix:
+    // rows past the end read as zeros, and a step past the reduction has size 0.
+    // The loads are issued from inline assembly, which writes no register: the
+    // compiler's own wait counting only over-waits around it, and it does not
+    // make LDS reads wait for these loads (the builtin does, as it cannot tell
+    // the buffers apart); the wait before each barrier covers them.
+    auto dma_tile = [&](const uint16_t* src, int64_t rows, int64_t r0, int64_t st, LDS_AS uint16_t* buf) {
+      const int64_t left = R - st * kBR;
+      const int rem = __builtin_amdgcn_readfirstlane((int)(left < kBR ? left : kBR));   // columns in this step
+      const uint64_t nrec = rem > 0 ? (uint64_t)(rows - r0) * R * 2 - (uint64_t)st * kBR * 2 : 0;
+      const uint64_t base = (uint64_t)(uintptr_t)(src + r0 * R + (rem > 0 ? st * kBR : 0));
+      const uint16_t* pa = (const uint16_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base));
+      const __amdgpu_buffer_rsrc_t ra = rsrc(pa, (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)nrec));
+      const bool ok0 = !kTail || 8 * (int)achunk[0] < rem;    // chunks past the reduction read as zeros
+      const bool ok1 = !kTail || 8 * (int)achunk[1] < rem;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t dst = (uint32_t)(uintptr_t)(buf + (64 * pw + 8 * j) * kBR);
+        const uint32_t vo = ((j & 1) ? ok1 : ok0) ? arow_off[j] : kOOB;
+        // M0 (the LDS address, read when the load issues) is saved and restored
+        // here, since the compiler does not track it across inline assembly
+        uint32_t m0_saved;
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+            : "=&s"(m0_saved)
+            : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(vo), "s"(ra)
+            : "memory");
+      }
+    };
+
+    // Weight tiles.  Producer thread tp rebuilds one block per step:
+    //  fwd: weight row p0 + tp, block st;                   tile [tp][k]
+    //  dX : weight row 64 st + tp / 4, block p0 / 64 + tp % 4; byte-plane rows 2 (tp / 4) (+1)
+    using Stage = typename std::conditional<kB16, NoCodes, BlockCodes>::type;
+    const __amdgpu_buffer_rsrc_t rc = rsrc(codes, kB16 ? 0 : (uint64_t)N * (K / 2));
+    const __amdgpu_buffer_rsrc_t r2 = rsrc(c2, kB16 ? 0 : (uint64_t)N * kblocks);
+    const __amdgpu_buffer_rsrc_t r1 = rsrc(c1, kB16 ? 0 : 4 * (((uint64_t)N * kblocks + 255) / 256));
+    auto load_stage = [&](int64_t step) {
+      Stage h;
+      if constexpr (!kB16) {
+        int64_t wrow, kb;
+        if (!kDx) { wrow = p0 + tp; kb = step; }
+        else { wrow = step * kBR + (tp >> 2); kb = p0 / 64 + (tp & 3); }
+        // out-of-range blocks get bit 31 set in their offsets: past every buffer end
+        const uint32_t oob = (wrow < N && kb < kblocks) ? 0u : kOOB;
+        const uint32_t b = (uint32_t)(wrow * kblocks + kb);
+        const uint32_t co = (uint32_t)(wrow * (K / 2) + kb * 32) | oob;
+        h.v[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
+        h.v[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, co + 16, 0, 0);
+        h.c2b = __builtin_amdgcn_raw_buffer_load_b8(r2, b | oob, 0, 0);
+        h.c1v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (4 * (b >> 8)) | oob, 0, 0));
+      }
+      return h;
+    };
+    auto store_stage = [&](const Stage& h, LDS_AS uint16_t* buf) {
+      if constexpr (!kB16) {
+        const BlockLut L = make_lut(qk::e4m3fn_to_f32(h.c2b) * h.c1v, p);
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) {
+          const uint32_t c = h.v[q8 >> 2][q8 & 3];
+          if (kDx) {
+            u32x2 lo8, hi8;
+            dequant8_planes(L, c, kc, lo8, hi8);
+            // 8-byte chunk c of each 32-byte column group of weight row k at chunk c ^ (k % 4)
+            const int k = tp >> 2, j = tp & 3;
+            LDS_AS uint8_t* d =
+                (LDS_AS uint8_t*)buf + 2 * k * kPlane + 64 * j + 32 * (q8 >> 2) + 8 * ((q8 & 3) ^ (k & 3));
+            *(LDS_AS u32x2*)d = lo8;
+            *(LDS_AS u32x2*)(d + kPlane) = hi8;
+          } else {
+            *(LDS_AS u32x4*)(buf + tp * kPF + 8 * q8) = dequant8(L, c, kc);
+          }
+        }
+      }
+    };
+    // bf16 dX: weight rows 64 st .. +64, columns p0 .. p0 + 255, sent straight
+    // to LDS: producer wave pw's load j fills rows 16 pw + 2 j (+1), lane l row
+    // (l / 32), slot l % 32, fetching chunk (l % 32) ^ (4 (row % 4)); chunks past
+    // column K and rows past N read as zeros.
+    auto dma_wdx = [&](int64_t st, LDS_AS uint16_t* buf) {
+      const int64_t r0 = st * kBR;
+      const uint64_t nrec = r0 < N ? (uint64_t)(N - r0) * K * 2 - (uint64_t)p0 * 2 : 0;
+      const uint64_t base = (uint64_t)(uintptr_t)(Wb + (r0 < N ? r0 * K + p0 : 0));
+      const uint16_t* pa = (const uint16_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base));
+      const __amdgpu_buffer_rsrc_t ra = rsrc(pa, (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)nrec));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = 16 * pw + 2 * j + (l >> 5);
+        const int chunk = (l & 31) ^ (4 * (row & 3));
+        const bool ok = p0 + 8 * chunk < K;
+        const uint32_t vo = ok ? (uint32_t)(row * K * 2 + 16 * chunk) : kOOB;
+        const uint32_t dst = (uint32_t)(uintptr_t)(buf + (16 * pw + 2 * j) * 256);
+        uint32_t m0_saved;
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+            : "=&s"(m0_saved)
+            : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(vo), "s"(ra)
+            : "memory");
+      }
+    };
+    auto send = [&](int64_t st, LDS_AS uint16_t* abuf, LDS_AS uint16_t* bbuf) {
+      dma_tile(A, M, m0, st, abuf);
+      if constexpr (kB16 && !kDx) dma_tile(Wb, N, p0, st, bbuf);
+      if constexpr (kB16 && kDx) dma_wdx(st, bbuf);
+    };
+    Stage hA, hB;
+    {
+      send(0, a0, b0);
+      const Stage h0 = load_stage(0);
+      hA = load_stage(1);
+      store_stage(h0, b0);
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), seen by the compiler's wait tracking
+      __builtin_amdgcn_s_barrier();
+    }
+    // Steps in pairs with no exit between them, so that the loop body is one
+    // basic block and the early loads stay where they are issued; an odd step
+    // count runs one more step over zeros (codes and activations past the end).
+    // The wait at the top of a step finds everything issued in the step before
+    // arrived (the barrier waited for it) and tells the compiler's wait
+    // tracking so, so that it places no wait after the loads to LDS it cannot
+    // count.
+    for (int64_t st = 0; st < nsteps; st += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      send(st + 1, a1, b1);
+      hB = load_stage(st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      store_stage(hA, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      send(st + 2, a0, b0);
+      hA = load_stage(st + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      store_stage(hB, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      __builtin_amdgcn_s_barrier();
+    }
+    return;
+  }
+
+  // ================================ consumers ================================
+  // A fragment of sub-step s, tile i: row 64 (c % 4) + 32 i + l % 32, chunk 2 s + l / 32.
   uint32_t afrag_off[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -368,115 +510,30 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   auto afrag = [&](const LDS_AS uint16_t* abuf, int s, int i) {
     return *(const LDS_AS bf16x8*)((const LDS_AS char*)abuf + afrag_off[s] + 32 * kBR * 2 * i);
   };
-
-  // ---- bf16 weight tiles (kB16).  Forward: B fragment of column p from the
-  // DMA'd [p][k] tile, addressed like the A fragments.  dX: thread t loads 64
-  // bytes of row 64 step + t / 8 of W (columns p0 + 32 (t % 8) .. +32) two steps
-  // ahead and stores them into the [n][p] tile of pitch kPD.
-  const __amdgpu_buffer_rsrc_t rw = rsrc(Wb, kB16 ? (uint64_t)N * K * 2 : 0);
-  auto wfrag = [&](const LDS_AS uint16_t* bbuf, int s, int j) {
-    return *(const LDS_AS bf16x8*)((const LDS_AS char*)bbuf + afrag_off[s] - (64 * rg) * kBR * 2 +
-                                   (128 * ch + 32 * j) * kBR * 2);
-  };
-  auto load_wrow = [&](int64_t step) {
-    RowBytes rb_;
-    const int64_t wrow = step * kBR + (t >> 3);
-    const int64_t col = p0 + 32 * (t & 7);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool ok = wrow < N && col + 8 * q < K;
-      rb_.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? (uint32_t)((wrow * K + col + 8 * q) * 2) : kOOB, 0, 0);
-    }
-    return rb_;
-  };
-  auto store_wrow = [&](const RowBytes& rb_, LDS_AS uint16_t* buf, int q) {
-    *(LDS_AS u32x4*)(buf + (t >> 3) * kPD + 32 * (t & 7) + 8 * q) = rb_.v[q];
-  };
-
-  // ---- weight tiles.  The thread pair (2 u, 2 u + 1) owns one block per step,
-  // thread 2 u + h converts its half h (32 weights):
-  //  fwd: weight row p0 + t / 2, block = step;                  tile [t / 2][32 h ..)
-  //  dX : weight row 64 step + t / 8, block p0 / 64 + (t / 2) % 4; tile [t / 8][64 ((t / 2) % 4) + 32 h ..)
-  const __amdgpu_buffer_rsrc_t rc = rsrc(codes, (uint64_t)N * (K / 2));
-  const __amdgpu_buffer_rsrc_t r2 = rsrc(c2, (uint64_t)N * kblocks);
-  const __amdgpu_buffer_rsrc_t r1 = rsrc(c1, 4 * (((uint64_t)N * kblocks + 255) / 256));
-  const int half = t & 1;
-  auto load_codes = [&](int64_t step) {
-    int64_t wrow, kb;
-    if (!kDx) { wrow = p0 + (t >> 1); kb = step; }
-    else { wrow = step * kBR + (t >> 3); kb = p0 / 64 + ((t >> 1) & 3); }
-    // out-of-range blocks get bit 31 set in their offsets: past every buffer end
-    const uint32_t oob = (wrow < N && kb < kblocks) ? 0u : kOOB;
-    const uint32_t b = (uint32_t)(wrow * kblocks + kb);
-    HalfCodes hc;
-    hc.c = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)(wrow * (K / 2) + kb * 32 + 16 * half) | oob, 0, 0);
-    hc.c2b = __builtin_amdgcn_raw_buffer_load_b8(r2, b | oob, 0, 0);
-    hc.c1v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (4 * (b >> 8)) | oob, 0, 0));
-    return hc;
-  };
-  // fwd: element offset of the thread's 32 weights; dX: byte offset of their
-  // low-byte plane row (the high bytes follow one plane row later)
-  const int dq_off = kDx ? 2 * (t >> 3) * kPlane + 64 * ((t >> 1) & 3) + 32 * half : (t >> 1) * kPF + 32 * half;
-  auto store8 = [&](const BlockLut& L, uint32_t c, LDS_AS uint16_t* buf, int q) {
-    if (kDx) {
-      u32x2 lo8, hi8;
-      dequant8_planes(L, c, kc, lo8, hi8);
-      LDS_AS uint8_t* d = (LDS_AS uint8_t*)buf + dq_off + 8 * (q ^ ((t >> 3) & 3));   // chunk swizzle, see frag_planes
-      *(LDS_AS u32x2*)d = lo8;
-      *(LDS_AS u32x2*)(d + kPlane) = hi8;
+  // B fragment of sub-step s, column tile j (columns 128 (c / 4) + 32 j ..)
+  auto bfrag = [&](const LDS_AS uint16_t* bcur, int s, int j) {
+    if constexpr (kB16) {
+      if constexpr (kDx) return frag_kmajor_sw(bcur, 16 * s, 128 * ch + 32 * j);
+      else   // the [p][k] tile sent like the activations, addressed like the A fragments
+        return *(const LDS_AS bf16x8*)((const LDS_AS char*)bcur + afrag_off[s] - (64 * rg) * kBR * 2 +
+                                       (128 * ch + 32 * j) * kBR * 2);
     } else {
-      *(LDS_AS u32x4*)(buf + dq_off + 8 * q) = dequant8(L, c, kc);
+      return kDx ? frag_planes((const LDS_AS uint8_t*)bcur, 16 * s, 128 * ch + 32 * j)
+                 : qk::frag_rowmajor(bcur, kPF, 128 * ch + 32 * j, 16 * s);
     }
   };
-  auto dequant_store = [&](const HalfCodes& hc, LDS_AS uint16_t* buf) {
-    const BlockLut L = make_lut(qk::e4m3fn_to_f32(hc.c2b) * hc.c1v, p);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) store8(L, hc.c[q], buf, q);
-  };
-
-  // ---- main loop.  At the top of step st: LDS holds activation tile st and
-  // weight tile st; registers hold codes(st + 1).  Step st sends activation tile
-  // st + 1 into the other activation buffer (free: its last reads ended before
-  // the previous barrier), loads codes(st + 2), multiplies, and converts
-  // codes(st + 1) into the other weight buffer; the barrier at its end waits for
-  // both new tiles.
-  LDS_AS uint16_t* b0 = (LDS_AS uint16_t*)lds_b;
-  LDS_AS uint16_t* b1 = (LDS_AS uint16_t*)lds_b + kBufElems;
-  LDS_AS uint16_t* a0 = (LDS_AS uint16_t*)lds_a0;
-  LDS_AS uint16_t* a1 = (LDS_AS uint16_t*)lds_a1;
-  const int64_t nsteps = (R + kBR - 1) / kBR;
-  using Stage = StageT<kDx, kB16>;
-  auto step = [&](int64_t st, const LDS_AS uint16_t* acur, LDS_AS uint16_t* anext, const LDS_AS uint16_t* bcur,
-                  LDS_AS uint16_t* bnext, const Stage& hc_now, Stage& hc_later) {
-    // Nothing is in flight here but, on the first step, the loads issued before
-    // the loop: waiting for them explicitly tells the compiler's wait tracking
-    // that the codes of this step have arrived, so that it places no wait after
-    // the loads to LDS below (which it cannot count, and would wait for).
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-    dma_a(st + 1, anext);
-    if constexpr (kB16 && !kDx) dma_w(st + 1, bnext);
-    else if constexpr (kB16) hc_later = load_wrow(st + 2);
-    else hc_later = load_codes(st + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    BlockLut L;
-    if constexpr (!kB16) L = make_lut(qk::e4m3fn_to_f32(hc_now.c2b) * hc_now.c1v, p);
-    // fragments of sub-step s + 1 are read from LDS while sub-step s runs
-    auto bfrag = [&](int s, int j) {
-      if constexpr (kB16) return kDx ? qk::frag_kmajor(bcur, kPD, 16 * s, 128 * ch + 32 * j) : wfrag(bcur, s, j);
-      else
-        return kDx ? frag_planes((const LDS_AS uint8_t*)bcur, 16 * s, 128 * ch + 32 * j)
-                   : qk::frag_rowmajor(bcur, kPF, 128 * ch + 32 * j, 16 * s);
-    };
+  // Fragments of sub-step s + 1 are read from LDS while sub-step s multiplies.
+  auto compute = [&](const LDS_AS uint16_t* acur, const LDS_AS uint16_t* bcur) {
     bf16x8 bq[2][4], aq[2][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bq[0][j] = bfrag(0, j);
+    for (int j = 0; j < 4; ++j) bq[0][j] = bfrag(bcur, 0, j);
     aq[0][0] = afrag(acur, 0, 0);
     aq[0][1] = afrag(acur, 0, 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s < 3) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bq[(s + 1) & 1][j] = bfrag(s + 1, j);
+        for (int j = 0; j < 4; ++j) bq[(s + 1) & 1][j] = bfrag(bcur, s + 1, j);
         aq[(s + 1) & 1][0] = afrag(acur, s + 1, 0);
         aq[(s + 1) & 1][1] = afrag(acur, s + 1, 1);
       }
@@ -485,57 +542,16 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
         acc[0][j] = qk::mfma32(aq[s & 1][0], bq[s & 1][j], acc[0][j]);
         acc[1][j] = qk::mfma32(aq[s & 1][1], bq[s & 1][j], acc[1][j]);
       }
-      if constexpr (kB16) {
-        // the bf16 weight: a quarter of the thread's row bytes per sub-step (dX);
-        // the forward's tile is already on its way to LDS
-        if constexpr (kDx) store_wrow(hc_now, bnext, s);
-        if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 10 : 6, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                         // MFMA
-        if constexpr (kDx) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // DS write
-      } else {
-        // one 8-weight group of the next weight tile per sub-step
-        store8(L, hc_now.c[s], bnext, s);
-        // schedule: the next sub-step's fragment reads first, then one MFMA at a
-        // time interleaved with the dequantisation VALU work, then the LDS store
-        if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, kDx ? 10 : 6, 0);   // DS read
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                         // VALU
-        }
-        __builtin_amdgcn_sched_group_barrier(0x200, kDx ? 2 : 1, 0);                 // DS write
-      }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // activation tile st + 1 has landed and this wave's LDS stores are done; the
-    // barrier hands both new tiles to all waves
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), seen by the compiler's wait tracking
-    __builtin_amdgcn_s_barrier();
   };
-  Stage hA, hB;
-  {
-    dma_a(0, a0);
-    if constexpr (kB16 && !kDx) {
-      dma_w(0, b0);
-    } else if constexpr (kB16) {
-      const RowBytes h0 = load_wrow(0);
-      hA = load_wrow(1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) store_wrow(h0, b0, q);
-    } else {
-      const HalfCodes h0 = load_codes(0);
-      hA = load_codes(1);
-      dequant_store(h0, b0);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), seen by the compiler's wait tracking
-    __builtin_amdgcn_s_barrier();
-  }
-  // Steps in pairs with no exit between them, so that the loop body is one
-  // basic block and the early loads stay where they are issued; an odd step
-  // count runs one more step over zeros (codes and activations past the end).
+  __builtin_amdgcn_s_barrier();            // first tiles in LDS
   for (int64_t st = 0; st < nsteps; st += 2) {
-    step(st, a0, a1, b0, b1, hA, hB);
-    step(st + 1, a1, a0, b1, b0, hB, hA);
+    compute(a0, b0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0): this wave's fragment reads are done
+    __builtin_amdgcn_s_barrier();
+    compute(a1, b1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
   }
 
   // ---- store C (bf16), lane layout of the 32x32 accumulators
