@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--step-only", action="store_true",
+                    help="only the timed headline steps (for kernel traces of the step)")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the per-kernel roofline timings (fused GEMMs and the decode forward), printed as "
                          "one JSON line: the run that the committed kernel trace profiles")
@@ -813,6 +815,10 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / args.steps
     flops = sum(L.flops() for L in lins)
     value = flops / (ms_step * 1e-3) / 1e12
+    if args.step_only:
+        print(json.dumps({"step_only": True, "value": round(value, 3), "ms_per_step": round(ms_step, 4),
+                          "steps": args.steps, "warmup": args.warmup}))
+        return
 
     # phases of the step, each timed alone
     phases = {}
