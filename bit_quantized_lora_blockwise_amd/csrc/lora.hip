@@ -144,6 +144,160 @@ __global__ __launch_bounds__(kThreads) void k_lora_skinny(const uint16_t* __rest
   }
 }
 
+// The same partial product for the common case (R, lda, r multiples of 8,
+// 8 <= r <= 64, 16-byte aligned operands), laid out for streaming with about one
+// work group per CU.  A work group owns 64 rows of A and one slice of the
+// reduction and runs 16 waves: wave (g, p) takes rows 16 g .. 16 g + 15 of the
+// tile, all r columns (four 16x16x32 MFMA tiles), and the 64-column steps
+// p, p + 4, p + 8, ... of the slice.  The rows of A go straight from memory into
+// MFMA operand registers (lane l: row l % 16, eight columns at 8 (l / 16)),
+// kSkDepth of the wave's steps ahead; the four B tiles of a group of steps
+// (64 x 64 each, from L2) are held in registers as far ahead and pass through
+// double-buffered LDS, one barrier per group.
+// At the end the four phases' sums are added in LDS in the order p = 0 .. 3.
+// Per CU this keeps well over 100 KB of A in flight with four waves per SIMD,
+// while each slice of B is read once per 64 rows and the slices stay few.
+constexpr int kSkGroups = 4;                       // row groups of 16
+constexpr int kSkPhases = 4;                       // steps taken in turn
+constexpr int kSkThreads = 64 * kSkGroups * kSkPhases;
+constexpr int kSkDepth = 4;                        // groups of A and B in flight
+
+template <bool kBkr>
+__global__ __launch_bounds__(kSkThreads, 1) void k_lora_skinny_stream(const uint16_t* __restrict__ A, int64_t M,
+                                                                     int64_t R, int64_t lda,
+                                                                     const uint16_t* __restrict__ Bm, int r,
+                                                                     int64_t chunk, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kSkPhases][kTile * kPitch];
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int rg = w % kSkGroups, ph = w / kSkGroups;
+  const int64_t m0 = (int64_t)blockIdx.x * kTile;
+  const int split = blockIdx.y;
+  const int64_t k_beg = split * chunk;
+  const int64_t k_end = min(R, k_beg + chunk);
+  const int nsteps = (int)((k_end - k_beg + kTile - 1) / kTile);
+  const int ngroups = (nsteps + kSkPhases - 1) / kSkPhases;   // group gi: steps kSkPhases gi + p
+
+  // A operand: lane l reads row m0 + 16 rg + l % 16, columns k + 8 (l / 16) .. +8
+  const int64_t arow = m0 + 16 * rg + (l & 15);
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A, (uint64_t)M * lda * 2);
+  const uint32_t abase = (uint32_t)(arow * lda * 2);
+  const int64_t akq = 8 * (l >> 4);
+  auto load_a = [&](int gi, u32x4 (&v)[2]) {
+    const int64_t k0 = k_beg + (int64_t)(kSkPhases * gi + ph) * kTile;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t k = k0 + 32 * u + akq;
+      const bool ok = arow < M && k < k_end;             // k_end is a multiple of 8
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? abase + (uint32_t)(k * 2) : kOOB, 0, 0);
+    }
+  };
+  // B tiles of a group: threads 256 q .. 256 q + 255 move the tile of step
+  // kSkPhases gi + q, thread tt row tt / 8 (+32), eight columns at 8 (tt % 8);
+  // kBkr: tile [k][c] from L1 [R, r]; otherwise tile [c][k] from L2 [r, R]
+  const __amdgpu_buffer_rsrc_t rb = rsrc(Bm, (uint64_t)R * r * 2);
+  const int bq = t >> 8, tt = t & 255;
+  auto load_b = [&](int gi, u32x4 (&v)[2]) {
+    const int64_t k0 = k_beg + (int64_t)(kSkPhases * gi + bq) * kTile;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = (tt >> 3) + 32 * i, q = 8 * (tt & 7);
+      bool ok;
+      int64_t off;
+      if (kBkr) {
+        ok = k0 + rr < k_end && q < r;
+        off = (k0 + rr) * r + q;
+      } else {
+        ok = rr < r && k0 + q < k_end;
+        off = (int64_t)rr * R + k0 + q;
+      }
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? (uint32_t)(off * 2) : kOOB, 0, 0);
+    }
+  };
+  auto store_b = [&](const u32x4 (&v)[2], int buf) {
+    LDS_AS uint16_t* dst = (LDS_AS uint16_t*)Bs[buf][bq];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *(LDS_AS u32x4*)(dst + ((tt >> 3) + 32 * i) * kPitch + 8 * (tt & 7)) = v[i];
+  };
+  // B operand of the 16x16x32 MFMA: lane l holds B(k + 8 (l / 16) .. +8, c + l % 16)
+  auto frag_b = [&](const LDS_AS uint16_t* bs, int k, int c) -> bf16x8 {
+    const int G = l >> 4, i = l & 15;
+    if (kBkr) {
+      // [k][c] tile: transposed reads, each 16-lane group a 4 x 16 block
+      const LDS_AS uint16_t* p = bs + (k + 8 * G + (i >> 2)) * kPitch + c + 4 * (i & 3);
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p);
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p + 4 * kPitch));
+      u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+      return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+    }
+    return *(const LDS_AS bf16x8*)(bs + (c + i) * kPitch + k + 8 * G);
+  };
+
+  // this wave's A rows and the work group's B tiles, kSkDepth groups ahead: group
+  // gi's A in a[gi % kSkDepth], its B tiles in breg[gi % kSkDepth] until they are
+  // stored to LDS during group gi - 1
+  u32x4 a[kSkDepth][2], breg[kSkDepth][2];
+  // Loads return in issue order, so the B tiles (small, soon needed) are
+  // requested ahead of the A rows: a wait for a B tile then never waits for A.
+  {
+    u32x4 b0[2];
+    load_b(0, b0);
+#pragma unroll
+    for (int j = 1; j <= kSkDepth; ++j) load_b(j, breg[j % kSkDepth]);
+#pragma unroll
+    for (int j = 0; j < kSkDepth; ++j) load_a(j, a[j]);
+    store_b(b0, 0);
+  }
+  __syncthreads();
+  f32x4 acc[4] = {};
+  const int ntile = (r + 15) / 16;
+  // group gi: MFMAs out of Bs[gi & 1], the tiles of gi + 1 into the other
+  // buffer, then the tiles of gi + 1 + kSkDepth and this wave's A rows of
+  // gi + kSkDepth are requested
+  auto group = [&](int gi, u32x4 (&av)[2], u32x4 (&bn)[2]) {
+    const LDS_AS uint16_t* bs = (const LDS_AS uint16_t*)Bs[gi & 1][ph];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8 x = __builtin_bit_cast(bf16x8, av[u]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < ntile) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, frag_b(bs, 32 * u, 16 * j), acc[j], 0, 0, 0);
+    }
+    store_b(bn, (gi + 1) & 1);
+    load_b(gi + 1 + kSkDepth, bn);
+    load_a(gi + kSkDepth, av);
+    __syncthreads();
+  };
+  for (int g0 = 0; g0 < ngroups; g0 += kSkDepth) {
+#pragma unroll
+    for (int j = 0; j < kSkDepth; ++j)
+      if (g0 + j < ngroups) group(g0 + j, a[j], breg[(j + 1) % kSkDepth]);
+  }
+  // the phases' sums added in order p = 0 .. 3 (the LDS tiles are free: every
+  // wave has passed the barrier after its last fragment reads)
+  float* red = (float*)&Bs[0][0][0];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(w * 16 + 4 * j + v) * 64 + l] = acc[j][v];
+  __syncthreads();
+  if (ph == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 16 * j + (l & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float sum = red[(rg * 16 + 4 * j + v) * 64 + l];
+#pragma unroll
+        for (int p = 1; p < kSkPhases; ++p) sum += red[((p * kSkGroups + rg) * 16 + 4 * j + v) * 64 + l];
+        // lane l holds C[4 (l / 16) + v][16 j + l % 16]
+        const int64_t m = m0 + 16 * rg + 4 * (l >> 4) + v;
+        if (j < ntile && m < M && c < r) part[((int64_t)split * M + m) * r + c] = sum;
+      }
+    }
+  }
+}
+
 // Sum of `splits` fp32 partials, part[k * n + i], added in order k = 0, 1, ...
 // starting from 0 (every path that adds these partials uses this order).
 // Four outputs per thread: 16-byte loads, all splits' loads of a group of
@@ -417,9 +571,35 @@ SplitPlan plan_rowsplit(int64_t tiles, int64_t R) {
   return SplitPlan{(int)splits, chunk};
 }
 
+// Split for the streaming kernel: about one work group per CU (64-row tiles
+// times slices), each slice at least four 64-column steps long.
+static SplitPlan plan_stream(int64_t tiles, int64_t R) {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess || n < 1)
+      n = 256;
+    return n;
+  }();
+  int64_t splits = (cus + tiles / 2) / tiles;
+  const int64_t max_splits = R / 256;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int64_t chunk = (R + splits - 1) / splits;
+  chunk = (chunk + kTile - 1) / kTile * kTile;
+  splits = (R + chunk - 1) / chunk;
+  return SplitPlan{(int)splits, chunk};
+}
+
+static bool skinny_stream_ok(const uint16_t* A, int64_t M, int64_t R, int64_t lda, const uint16_t* B, int r) {
+  return (R % 8) == 0 && (lda % 8) == 0 && (r % 8) == 0 && r >= 8 && r <= 64 && ((uintptr_t)A & 15) == 0 &&
+         ((uintptr_t)B & 15) == 0 && M * lda * 2 < (int64_t(1) << 31) && R * r * 2 < (int64_t(1) << 31);
+}
+
 size_t lora_skinny_ws(int64_t M, int64_t R, int r) {
-  const SplitPlan sp = plan_rowsplit((M + kTile - 1) / kTile, R);
-  const int64_t splits = M <= 16 ? std::max<int64_t>(sp.splits, decode_t_slices(R)) : sp.splits;
+  const int64_t tiles = (M + kTile - 1) / kTile;
+  int64_t splits = std::max<int64_t>(plan_rowsplit(tiles, R).splits, plan_stream(tiles, R).splits);
+  if (M <= 16) splits = std::max<int64_t>(splits, decode_t_slices(R));
   return (size_t)splits * M * r * sizeof(float);
 }
 
@@ -434,6 +614,19 @@ hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t l
     return hipGetLastError();
   }
   const int64_t tiles = (M + kTile - 1) / kTile;
+  if (skinny_stream_ok(A, M, R, lda, B, r)) {
+    const SplitPlan sp = plan_stream(tiles, R);
+    dim3 grid((unsigned)tiles, (unsigned)sp.splits);
+    if (b_is_kr)
+      hipLaunchKernelGGL((k_lora_skinny_stream<true>), grid, dim3(kSkThreads), 0, s, A, M, R, lda, B, r, sp.chunk, ws);
+    else
+      hipLaunchKernelGGL((k_lora_skinny_stream<false>), grid, dim3(kSkThreads), 0, s, A, M, R, lda, B, r, sp.chunk, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_skinny_reduce, dim3(grid_for((M * r + 3) / 4)), dim3(kThreads), 0, s, ws, sp.splits,
+                       M * (int64_t)r, scale, out);
+    return hipGetLastError();
+  }
   const SplitPlan sp = plan_rowsplit(tiles, R);
   dim3 grid((unsigned)tiles, (unsigned)sp.splits);
   const bool avec = (R % 8) == 0 && (lda % 8) == 0 && ((uintptr_t)A & 15) == 0;
