@@ -14,7 +14,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora.so")
+# QLORA_LIBRARY selects another build of the same library (the host-sanitized
+# one that the sanitizer test runs the ABI checks against); default: in-tree.
+_LIB_PATH = os.environ.get("QLORA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora.so")
 _lib = None
 
 QL_F32, QL_BF16 = 0, 1
