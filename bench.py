@@ -278,6 +278,59 @@ def comparators(lins, reps):
     return out
 
 
+def decode_stacked_bench(dev, reps=200):
+    """Stacked linears at decode size (M = 1): LLaMA-7B q|k|v (3 x 4096->4096) and
+    gate|up (2 x 4096->11008) as one qlora_group_fwd call (one T-slice launch for
+    every adapter, one decode launch over the stacked rows) against the same
+    segments as separate qlora_linear_fwd calls; graph-replayed over rotated
+    weight copies like decode_bench."""
+    import torch
+    import bit_quantized_lora_blockwise_amd as q
+    import workloads as WL
+    res = {}
+    K, r, M = 4096, 64, 1
+    for name, G, N in (("qkv", 3, 4096), ("gate_up", 2, 11008)):
+        W = WL.normal((G * N, K), 0.02, 9100 + G, device=dev).to(torch.bfloat16)
+        codes, absmax = q.nf4_quantize(W)
+        c2, c1 = q.nf4_double_quant(absmax)
+        del W, absmax
+        packed = codes.numel() + c2.numel() + c1.numel() * 4
+        copies = max(8, (600 << 20) // packed + 1)
+        layers = [(codes.clone(), c2.clone(), c1.clone()) for _ in range(copies)]
+        L1 = WL.normal((G, K, r), 1.0 / K, 9200 + G, device=dev).to(torch.bfloat16)
+        L2 = WL.normal((G, r, N), 0.01, 9300 + G, device=dev).to(torch.bfloat16)
+        X = WL.normal((M, K), 1.0, 9400 + G, device=dev).to(torch.bfloat16)
+        Y = torch.empty((M, G * N), dtype=torch.bfloat16, device=dev)
+        T = torch.empty((G, M, r), dtype=torch.bfloat16, device=dev)
+        wsg = torch.empty((int(q.lib().qlora_group_fwd_workspace(M, K, N, G, r)),), dtype=torch.uint8, device=dev)
+        wss = torch.empty((q.qlora_linear_fwd_workspace(M, K, N, r),), dtype=torch.uint8, device=dev)
+        Ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(G)]
+        nb = N * K // 64
+        it = [0]
+
+        def stacked():
+            cd, cc2, cc1 = layers[it[0] % copies]
+            it[0] += 1
+            q.qlora_group_fwd(X, cd, cc2, cc1, N, G, L1, L2, 1.0, Y=Y, T_out=T, workspace=wsg)
+
+        def separate():
+            cd, cc2, cc1 = layers[it[0] % copies]
+            it[0] += 1
+            for g in range(G):
+                q.qlora_linear_fwd(X, cd.view(-1)[g * N * K // 2:(g + 1) * N * K // 2], cc2.view(-1)[g * nb:(g + 1) * nb],
+                                   cc1.view(-1)[g * nb // 256:(g + 1) * nb // 256], N, L1[g], L2[g], 1.0, Y=Ys[g],
+                                   T_out=T[g], workspace=wss)
+
+        sms = time_graph_launches(stacked, copies * 2, max(4, reps // (copies * 2)))
+        pms = time_graph_launches(separate, copies * 2, max(4, reps // (copies * 2)))
+        res[name] = {"G": G, "N": N, "K": K, "M": M, "packed_bytes": packed, "stacked_us": sms * 1e3,
+                     "stacked_packed_gbps": packed / (sms * 1e-3) / 1e9, "separate_us": pms * 1e3,
+                     "separate_packed_gbps": packed / (pms * 1e-3) / 1e9}
+        del layers
+        torch.cuda.empty_cache()
+    return res
+
+
 def decode_bench(dev, reps=200):
     import torch
     import bit_quantized_lora_blockwise_amd as q
@@ -839,6 +892,7 @@ def main():
 
     dec = decode_bench(dev)
     dec_roof = decode_roofline(dec)
+    dec["stacked_m1"] = decode_stacked_bench(dev)
     enc = encode_bench(dev)
     enc["model_80_layers"] = encode_model_bench(dev)
     mrg = merge_bench(dev)

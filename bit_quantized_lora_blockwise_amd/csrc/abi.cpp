@@ -90,6 +90,18 @@ bool group_ok(int64_t M, int64_t K, int64_t N, int G, int r) {
   return N % 256 == 0 && M > 16 && qgemm_big_ok(false, M, K, N * G) && qgemm_big_ok(true, M, K, N * G);
 }
 
+// Stacked forward at decode size (M <= 16, G > 1): one T-slice launch for all
+// adapters and one decode launch over the stacked rows; X must fit the decode
+// kernel's LDS (M K <= 16384) and r be a multiple of 4.
+bool group_decode_ok(int64_t M, int64_t K, int64_t N, int G, int r) {
+  return G > 1 && G <= 16 && M >= 1 && M <= 16 && N > 0 && N % 256 == 0 && N <= (int64_t(1) << 31) / G &&
+         shapes_ok(M, K, N * G, r) && (r % 4) == 0 && qgemv_group_ok(M, K, N, G);
+}
+
+bool group_fwd_ok(int64_t M, int64_t K, int64_t N, int G, int r) {
+  return group_ok(M, K, N, G, r) || group_decode_ok(M, K, N, G, r);
+}
+
 struct GroupWs {
   size_t t_bytes, g_bytes, part_bytes, total;
 };
@@ -215,17 +227,23 @@ int q4_levels(int codebook, float* out16) {
 }
 
 
-size_t qlora_group_fwd_workspace(int64_t M, int64_t K, int64_t N, int G, int r) {
-  if (!group_ok(M, K, N, G, r)) return 0;
+size_t group_fwd_ws(int64_t M, int64_t K, int64_t N, int G, int r) {
   const GroupWs w = group_ws(M, K, N, G, r);
-  return w.t_bytes + w.part_bytes;
+  size_t part = w.part_bytes;
+  if (group_decode_ok(M, K, N, G, r)) part = std::max(part, round_up((size_t)G * kDecodeTSlices * M * r * 4));
+  return w.t_bytes + part;
+}
+
+size_t qlora_group_fwd_workspace(int64_t M, int64_t K, int64_t N, int G, int r) {
+  if (!group_fwd_ok(M, K, N, G, r)) return 0;
+  return group_fwd_ws(M, K, N, G, r);
 }
 
 int qlora_group_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, int G, const uint8_t* codes,
                     const uint8_t* c2, const float* c1, const uint16_t* L1, const uint16_t* L2, int r,
                     float lora_scale, uint16_t* Y, uint16_t* T_out, void* workspace, size_t ws_bytes, void* stream) {
   if (!X || !codes || !c2 || !c1 || !L1 || !L2 || !Y) return QL_ERR_NULL;
-  if (!group_ok(M, K, N, G, r)) return QL_ERR_SHAPE;
+  if (!group_fwd_ok(M, K, N, G, r)) return QL_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(codes) || !aligned16(c2) || !aligned16(c1) || !aligned16(L1) ||
       !aligned16(L2) || !aligned16(Y) || (T_out && !aligned16(T_out)))
     return QL_ERR_ALIGN;
@@ -233,12 +251,20 @@ int qlora_group_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, int G, c
     return qlora_linear_fwd(X, M, K, N, codes, c2, c1, L1, L2, r, lora_scale, Y, T_out, workspace, ws_bytes,
                             stream);
   const GroupWs w = group_ws(M, K, N, G, r);
-  if (!workspace || ws_bytes < w.t_bytes + w.part_bytes) return QL_ERR_WORKSPACE;
+  if (!workspace || ws_bytes < group_fwd_ws(M, K, N, G, r)) return QL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return QL_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   uint16_t* T = T_out ? T_out : (uint16_t*)ws;
   float* part = (float*)(ws + w.t_bytes);
+  if (M <= 16) {
+    // decode size: the slices of every T_g in one launch, added and rounded in the decode kernel
+    if (!decode_t_ok(M, K, X, L1)) return QL_ERR_ALIGN;
+    QL_TRY(launch_lora_part(X, M, K, L1, r, part, s, G));
+    QL_TRY(launch_qgemv_group_tpart(X, M, K, N, G, codes, c2, c1, part, decode_t_slices(K), T_out, L2, r,
+                                    lora_scale, Y, s));
+    return QL_OK;
+  }
   for (int g = 0; g < G; ++g)
     QL_TRY(launch_lora_skinny(X, M, K, K, L1 + (int64_t)g * K * r, true, r, 1.0f, T + (int64_t)g * M * r, part, s));
   QL_TRY(launch_qgemm_big(false, X, M, K, N * G, codes, c2, c1, T, L2, r, lora_scale, Y, s, G));

@@ -24,9 +24,12 @@
 // stages it in LDS once per CU and walks 16-row tiles in turn; larger X is staged
 // slice by slice when there is at most one tile per CU, and otherwise read from
 // global memory together with the step's codes.
+#include "dequant.h"
 #include "kernels.h"
 
 namespace {
+
+using namespace nf4;
 
 constexpr int kRows = 16;                 // weight rows (output columns) per work group
 constexpr int kXBytes = 32768;            // LDS budget for X: M * K <= 16384
@@ -43,91 +46,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint64_t b
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, 0x00020000);
 }
 
-// (a & m) | o in one instruction; m and o are kept in VGPRs (a VOP3 encoding
-// takes no literal and at most one SGPR).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
-}
-
-// ---------------------------------------------------------------------------
-// One block's dequantisation table held in registers.
-struct BlockLut {
-  uint32_t lo[4], hi[4];   // byte planes: lo[j] byte i = low byte of W'(4 j + i), hi likewise
-};
-
-__device__ __forceinline__ BlockLut make_lut(float s, const Nf4Params& p) {
-  uint32_t pk[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) pk[i] = qk::pack_bf16x2(p.q[2 * i] * s, p.q[2 * i + 1] * s);
-  BlockLut L;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    L.lo[j] = __builtin_amdgcn_perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
-    L.hi[j] = __builtin_amdgcn_perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
-  }
-  return L;
-}
-
-// Constants of the nibble split, held in VGPRs for v_and_or_b32.
-struct SplitConst {
-  uint32_t m4, b0;   // 0x04040404, 0x03020100
-};
-
-// 16-entry byte lookup of four 4-bit indices: x7 holds their low three bits,
-// sel = 0x03020100 + 4 * (bit 3 of each index) picks the entry 8..15 candidate.
-__device__ __forceinline__ uint32_t lut16(const uint32_t (&T)[4], uint32_t x7, uint32_t sel) {
-  const uint32_t a = __builtin_amdgcn_perm(T[1], T[0], x7);   // entries 0..7
-  const uint32_t b = __builtin_amdgcn_perm(T[3], T[2], x7);   // entries 8..15
-  return __builtin_amdgcn_perm(b, a, sel);
-}
-
-// Eight nibbles of one 32-bit word (element j in bits 4j..4j+3) -> byte-plane
-// lookups of the even elements (le, he) and odd elements (lo, ho).
-struct Planes {
-  uint32_t le, he, lo, ho;
-};
-
-__device__ __forceinline__ Planes lookup8(const BlockLut& L, uint32_t c, const SplitConst& k) {
-  const uint32_t xe = c & 0x07070707u;               // elements 0, 2, 4, 6: low 3 bits
-  const uint32_t se = and_or(c >> 1, k.m4, k.b0);    //   and their bit 3 as a selector
-  const uint32_t xo = (c >> 4) & 0x07070707u;        // elements 1, 3, 5, 7
-  const uint32_t so = and_or(c >> 5, k.m4, k.b0);
-  Planes P;
-  P.le = lut16(L.lo, xe, se);
-  P.he = lut16(L.hi, xe, se);
-  P.lo = lut16(L.lo, xo, so);
-  P.ho = lut16(L.hi, xo, so);
-  return P;
-}
-
-// Weights in element order (bf16 pairs e0 e1, e2 e3, e4 e5, e6 e7).
-__device__ __forceinline__ u32x4 dequant8(const BlockLut& L, uint32_t c, const SplitConst& k) {
-  const Planes P = lookup8(L, c, k);
-  const uint32_t e02 = __builtin_amdgcn_perm(P.he, P.le, 0x05010400u);   // [W'(e0), W'(e2)]
-  const uint32_t e46 = __builtin_amdgcn_perm(P.he, P.le, 0x07030602u);   // [W'(e4), W'(e6)]
-  const uint32_t o13 = __builtin_amdgcn_perm(P.ho, P.lo, 0x05010400u);   // [W'(e1), W'(e3)]
-  const uint32_t o57 = __builtin_amdgcn_perm(P.ho, P.lo, 0x07030602u);   // [W'(e5), W'(e7)]
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(o13, e02, 0x05040100u);
-  r[1] = __builtin_amdgcn_perm(o13, e02, 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(o57, e46, 0x05040100u);
-  r[3] = __builtin_amdgcn_perm(o57, e46, 0x07060302u);
-  return r;
-}
-
-// Weights in the order (0, 2, 4, 6, 1, 3, 5, 7) of the word.
-__device__ __forceinline__ u32x4 dequant8_eo(const BlockLut& L, uint32_t c, const SplitConst& k) {
-  const Planes P = lookup8(L, c, k);
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(P.he, P.le, 0x05010400u);   // W'(e0), W'(e2)
-  r[1] = __builtin_amdgcn_perm(P.he, P.le, 0x07030602u);   // W'(e4), W'(e6)
-  r[2] = __builtin_amdgcn_perm(P.ho, P.lo, 0x05010400u);   // W'(e1), W'(e3)
-  r[3] = __builtin_amdgcn_perm(P.ho, P.lo, 0x07030602u);   // W'(e5), W'(e7)
-  return r;
-}
-
 // Operands of one step of a lane: its block's codes and scales, and (when X is
 // not staged in LDS) the 64 matching columns of its row of X.
 template <bool kXLds>
@@ -141,6 +59,12 @@ struct Step {
 // kTPart: T is not given but formed here from the S fp32 slices Tp[s][m][c]
 // (added in order s = 0 .. S-1, rounded once), and written to T (if not null)
 // by work group 0.
+// Stacked linears (G segments of seg_tiles 16-row tiles each, sharing X): the
+// work group's segment sg has its own T_sg (at T + sg M r; slices at
+// Tp + sg S M r) and L2_sg [r, l2ld] at L2 + sg r l2ld, whose column is the row
+// within the segment; Y [M, ld] spans all segments.  The first work group of
+// each segment writes that segment's T.  One linear: seg_tiles >= the grid,
+// l2ld = ld.
 // Eight-wave work groups are held to six waves per SIMD (three work groups per
 // CU, at most 80 VGPRs): given the registers, the compiler would otherwise keep
 // more values live and fit only two.
@@ -151,7 +75,8 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
                                                         const float* __restrict__ c1,
                                                         uint16_t* __restrict__ T, const float* __restrict__ Tp, int S,
                                                         const uint16_t* __restrict__ L2, int r, float scale,
-                                                        uint16_t* __restrict__ Y, Nf4Params p) {
+                                                        uint16_t* __restrict__ Y, Nf4Params p, int seg_tiles,
+                                                        int64_t l2ld) {
   constexpr int kThr = 64 * kWv;
   __shared__ __attribute__((aligned(16))) uint8_t lds[(kXLds ? kXBytes + kZeroBytes : 0) + kWv * 64 * 16];
   const int t = threadIdx.x;
@@ -159,12 +84,16 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
   const int g = l >> 4, col = l & 15;
   const int64_t n0 = (int64_t)blockIdx.x * kRows;
   const int64_t nrow = n0 + col;
+  const uint32_t sg = blockIdx.x / (uint32_t)seg_tiles;          // segment of this work group
+  const int64_t nloc = nrow - (int64_t)sg * seg_tiles * kRows;  // its row within the segment
+  const bool seg_first = blockIdx.x == sg * (uint32_t)seg_tiles;
+  if (T) T += (int64_t)sg * M * r;                  // a null T (no T to write) stays null
+  if (kTPart) Tp += (int64_t)sg * S * M * r;
+  L2 += (int64_t)sg * r * l2ld;
   const bool row_ok = nrow < N;
   const bool m_ok = col < M;                       // A-operand row of this lane is X[col]
   const uint32_t kblocks = (uint32_t)(K / qk::kBlock);
-  SplitConst kc;
-  asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
-  asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
+  const SplitConst kc = split_const();
 
   // K is walked in steps of four blocks (256 columns); the waves take the steps
   // in turn, and in step s lane group g takes block 4 s + g, so the four lanes
@@ -217,12 +146,12 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
   // the end, so that no wait for them covers the code stream.
   uint16_t vl[4], vt16[4];
   {
-    const __amdgpu_buffer_rsrc_t rl = rsrc(L2, 2 * ((uint64_t)(r - 1) * ld + N));
+    const __amdgpu_buffer_rsrc_t rl = rsrc(L2, 2 * (uint64_t)r * l2ld);
     const __amdgpu_buffer_rsrc_t rt = rsrc(T, 2 * (uint64_t)M * r);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool rk = rb + j < r;
-      const uint32_t ol = (rk && row_ok) ? (uint32_t)(2 * ((int64_t)(rb + j) * ld + nrow)) : kOOB;
+      const uint32_t ol = (rk && row_ok) ? (uint32_t)(2 * ((int64_t)(rb + j) * l2ld + nloc)) : kOOB;
       vl[j] = __builtin_amdgcn_raw_buffer_load_b16(rl, ol, 0, 0);
       if (!kTPart) {
         const uint32_t ot = (rk && m_ok) ? (uint32_t)(2 * (col * r + rb + j)) : kOOB;
@@ -266,7 +195,7 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
         if (s < S) sum += ps[s];
 #pragma unroll
       for (int j = 0; j < 4; ++j) vt[j] = qk::f32_to_bf16(sum[j]);
-      if (T && blockIdx.x == 0 && t_ok) {
+      if (T && seg_first && t_ok) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) T[col * r + rb + j] = (uint16_t)vt[j];
       }
@@ -399,9 +328,7 @@ __global__ __launch_bounds__(512) void k_qgemv_persist(const uint16_t* __restric
   const uint32_t kblocks = (uint32_t)(K / qk::kBlock);
   const int64_t ntiles = (N + kRows - 1) / kRows;
   const int64_t my_tiles = ntiles > blockIdx.x ? (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
-  SplitConst kc;
-  asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
-  asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
+  const SplitConst kc = split_const();
   const uint32_t nsteps = (kblocks + 3) / 4;
   const uint32_t nst = nsteps > (uint32_t)w ? (nsteps - (uint32_t)w + kWv - 1) / kWv : 0u;   // steps per tile, uniform
   const uint32_t kb0 = 4u * (uint32_t)w + (uint32_t)g;
@@ -623,9 +550,7 @@ __global__ __launch_bounds__(512) void k_qgemv_slices(const uint16_t* __restrict
   const uint32_t my_tiles = kT == 1 ? 1u : (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const uint32_t nrow0 = blockIdx.x * kRows + (uint32_t)col;          // this lane's row in its first tile
   const uint32_t trows = gridDim.x * kRows;                           // rows from one of its tiles to the next
-  SplitConst kc;
-  asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
-  asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
+  const SplitConst kc = split_const();
   const uint32_t nsteps = (kblocks + 3) / 4;
   const uint32_t nst = nsteps > (uint32_t)w ? (nsteps - (uint32_t)w + kWv - 1) / kWv : 0u;   // uniform
   const uint32_t kb0 = 4u * (uint32_t)w + (uint32_t)g;
@@ -831,6 +756,8 @@ struct QgemvArgs {
   int r;
   float scale;
   uint16_t* Y;
+  int seg_tiles = 0x7fffffff;   // 16-row tiles per stacked segment (one linear: more than any grid)
+  int64_t l2ld = 0;             // row stride of each segment's L2 (0: ld)
 };
 
 template <bool kTPart>
@@ -853,7 +780,8 @@ hipError_t launch_slices(int kt, unsigned grid, int64_t ksl, hipStream_t s, cons
 template <bool kXLds, int kWv, int kXPer, bool kTPart>
 hipError_t launch_one(dim3 grid, hipStream_t s, const QgemvArgs& a) {
   hipLaunchKernelGGL((k_qgemv_fwd<kXLds, kWv, kXPer, kTPart>), grid, dim3(64 * kWv), 0, s, a.X, a.M, a.K, a.rows,
-                     a.ld, a.codes, a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params());
+                     a.ld, a.codes, a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params(), a.seg_tiles,
+                     a.l2ld ? a.l2ld : a.ld);
   return hipGetLastError();
 }
 
@@ -935,6 +863,21 @@ hipError_t launch_qgemv_fwd_tpart(const uint16_t* X, int64_t M, int64_t K, int64
   if (S < 1 || S > kDecodeTSlices || (r % 4) != 0 || ((uintptr_t)Tpart & 15) != 0) return hipErrorInvalidValue;
   const QgemvArgs a{X, M, K, 0, N, codes, c2, c1, T_out, Tpart, S, L2, r, scale, Y};
   return launch_shape<true>(a, N, s);
+}
+
+bool qgemv_group_ok(int64_t M, int64_t K, int64_t N, int G) {
+  return M >= 1 && M * K * 2 <= kXBytes && N % kRows == 0 && G >= 1 && (int64_t)G * N * (K / 2) < (int64_t(1) << 31);
+}
+
+hipError_t launch_qgemv_group_tpart(const uint16_t* X, int64_t M, int64_t K, int64_t N, int G, const uint8_t* codes,
+                                    const uint8_t* c2, const float* c1, const float* Tpart, int S, uint16_t* T_out,
+                                    const uint16_t* L2, int r, float scale, uint16_t* Y, hipStream_t s) {
+  if (!qgemv_group_ok(M, K, N, G) || S < 1 || S > kDecodeTSlices || (r % 4) != 0 || ((uintptr_t)Tpart & 15) != 0)
+    return hipErrorInvalidValue;
+  QgemvArgs a{X, M, K, (int64_t)G * N, (int64_t)G * N, codes, c2, c1, T_out, Tpart, S, L2, r, scale, Y};
+  a.seg_tiles = (int)(N / kRows);
+  a.l2ld = N;
+  return launch_lds<8, true>(dim3((unsigned)(G * (N / kRows))), s, a);
 }
 
 hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,

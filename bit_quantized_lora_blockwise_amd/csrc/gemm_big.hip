@@ -31,9 +31,12 @@
 //    remapped so that each XCD (with its own L2) gets a contiguous run of tiles.
 #include <type_traits>
 
+#include "dequant.h"
 #include "kernels.h"
 
 namespace {
+
+using namespace nf4;
 
 constexpr int kT = 768;           // threads per work group: 8 consumer + 4 producer waves
 constexpr int kTC = 512;          // consumer threads
@@ -66,87 +69,6 @@ __device__ __forceinline__ u32x4 load_row8(const uint16_t* __restrict__ row, int
     v[j >> 1] |= h << (16 * (j & 1));
   }
   return v;
-}
-
-// ---------------------------------------------------------------------------
-// Dequantisation of one block held in registers.
-struct BlockLut {
-  uint32_t lo[4], hi[4];   // byte planes: lo[j] byte i = low byte of W'(4 j + i), hi likewise
-};
-
-__device__ __forceinline__ BlockLut make_lut(float s, const Nf4Params& p) {
-  uint32_t pk[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) pk[i] = qk::pack_bf16x2(p.q[2 * i] * s, p.q[2 * i + 1] * s);
-  BlockLut L;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    L.lo[j] = __builtin_amdgcn_perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
-    L.hi[j] = __builtin_amdgcn_perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
-  }
-  return L;
-}
-
-// (a & m) | o in one instruction; m and o are kept in VGPRs (a VOP3 encoding
-// takes no literal and at most one SGPR).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
-}
-
-// Constants of the nibble split, held in VGPRs for v_and_or_b32.
-struct SplitConst {
-  uint32_t m4, b0;   // 0x04040404, 0x03020100
-};
-
-// 16-entry byte lookup of four 4-bit indices: x7 holds their low three bits,
-// sel = 0x03020100 + 4 * (bit 3 of each index) picks the entry 8..15 candidate.
-__device__ __forceinline__ uint32_t lut16(const uint32_t (&T)[4], uint32_t x7, uint32_t sel) {
-  const uint32_t a = __builtin_amdgcn_perm(T[1], T[0], x7);   // entries 0..7
-  const uint32_t b = __builtin_amdgcn_perm(T[3], T[2], x7);   // entries 8..15
-  return __builtin_amdgcn_perm(b, a, sel);
-}
-
-// Eight nibbles of one 32-bit word (element j in bits 4j..4j+3): index bytes of
-// the even elements (xe, se) and the odd elements (xo, so).
-struct Split {
-  uint32_t xe, se, xo, so;
-};
-
-__device__ __forceinline__ Split split8(uint32_t c, const SplitConst& k) {
-  Split sp;
-  sp.xe = c & 0x07070707u;               // elements 0, 2, 4, 6: low 3 bits
-  sp.se = and_or(c >> 1, k.m4, k.b0);    //   and their bit 3 as a selector
-  sp.xo = (c >> 4) & 0x07070707u;        // elements 1, 3, 5, 7
-  sp.so = and_or(c >> 5, k.m4, k.b0);
-  return sp;
-}
-
-// Eight nibbles -> four packed bf16 pairs in element order.
-__device__ __forceinline__ u32x4 dequant8(const BlockLut& L, uint32_t c, const SplitConst& k) {
-  const Split sp = split8(c, k);
-  const uint32_t le = lut16(L.lo, sp.xe, sp.se), he = lut16(L.hi, sp.xe, sp.se);
-  const uint32_t lo_ = lut16(L.lo, sp.xo, sp.so), ho = lut16(L.hi, sp.xo, sp.so);
-  const uint32_t e02 = __builtin_amdgcn_perm(he, le, 0x05010400u);   // [W'(e0), W'(e2)]
-  const uint32_t e46 = __builtin_amdgcn_perm(he, le, 0x07030602u);   // [W'(e4), W'(e6)]
-  const uint32_t o13 = __builtin_amdgcn_perm(ho, lo_, 0x05010400u);  // [W'(e1), W'(e3)]
-  const uint32_t o57 = __builtin_amdgcn_perm(ho, lo_, 0x07030602u);  // [W'(e5), W'(e7)]
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(o13, e02, 0x05040100u);   // e0, e1
-  r[1] = __builtin_amdgcn_perm(o13, e02, 0x07060302u);   // e2, e3
-  r[2] = __builtin_amdgcn_perm(o57, e46, 0x05040100u);   // e4, e5
-  r[3] = __builtin_amdgcn_perm(o57, e46, 0x07060302u);   // e6, e7
-  return r;
-}
-
-// Eight nibbles -> the low and high bytes of their bf16 values, each as eight
-// bytes in the element order (0, 2, 4, 6, 1, 3, 5, 7).
-__device__ __forceinline__ void dequant8_planes(const BlockLut& L, uint32_t c, const SplitConst& k, u32x2& lo8,
-                                                u32x2& hi8) {
-  const Split sp = split8(c, k);
-  lo8 = u32x2{lut16(L.lo, sp.xe, sp.se), lut16(L.lo, sp.xo, sp.so)};
-  hi8 = u32x2{lut16(L.hi, sp.xe, sp.se), lut16(L.hi, sp.xo, sp.so)};
 }
 
 // Column held in slot `s` of a dX weight tile: within each group of eight the
@@ -339,9 +261,7 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     // before the barrier that ends the step.
     const int pw = w - 8;                 // producer wave 0..3
     const int tp = t - kTC;               // producer thread 0..255
-    SplitConst kc;
-    asm volatile("v_mov_b32 %0, 0x04040404" : "=v"(kc.m4));
-    asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kc.b0));
+    const SplitConst kc = split_const();
 
     // Activation (and bf16 forward weight) tiles: producer wave pw sends rows
     // 64 pw .. +64, eight rows of 128 bytes per 16-byte-per-lane load (lane l:

@@ -56,11 +56,13 @@ size_t lora_skinny_ws(int64_t M, int64_t R, int r);
 // partial sums part[s][m][c] over S = decode_t_slices(K) <= kDecodeTSlices
 // slices of the reduction.  launch_lora_skinny adds them in order s = 0..S-1 for
 // such shapes, and so does the decode kernel, so T is the same on every path.
+// G > 1: stacked adapters L1_g [K, r] at L1 + g K r, slices of segment g at
+// part + g S M r (one launch for all).
 constexpr int kDecodeTSlices = 8;
 int decode_t_slices(int64_t K);
 bool decode_t_ok(int64_t M, int64_t K, const void* X, const void* L1);
 hipError_t launch_lora_part(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float* part,
-                            hipStream_t s);
+                            hipStream_t s, int G = 1);
 hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t lda, const uint16_t* B, bool b_is_kr,
                               int r, float scale, uint16_t* out, float* ws, hipStream_t s);
 
@@ -94,6 +96,14 @@ hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, 
 // Same, with T = bf16(sum over s of Tpart[s]) formed by the kernel from the S
 // fp32 slices of launch_lora_part (r % 4 == 0, Tpart 16-byte aligned); T_out
 // (optional) receives that T.
+// Stacked linears at decode size: G segments of N rows of one packed matrix
+// [G N, K] sharing X, each with its own T (formed from the slices of
+// launch_lora_part(..., G)) and L2_g [r, N] (at L2 + g r N); Y [M, G N].  Only
+// for X that fits the kernel's LDS (M K <= 16384) and N % 16 == 0.
+bool qgemv_group_ok(int64_t M, int64_t K, int64_t N, int G);
+hipError_t launch_qgemv_group_tpart(const uint16_t* X, int64_t M, int64_t K, int64_t N, int G, const uint8_t* codes,
+                                    const uint8_t* c2, const float* c1, const float* Tpart, int S, uint16_t* T_out,
+                                    const uint16_t* L2, int r, float scale, uint16_t* Y, hipStream_t s);
 hipError_t launch_qgemv_fwd_tpart(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                                   const uint8_t* c2, const float* c1, const float* Tpart, int S, uint16_t* T_out,
                                   const uint16_t* L2, int r, float scale, uint16_t* Y, hipStream_t s);

@@ -462,6 +462,9 @@ int grid_for(int64_t items) {
 // 8 g .. 8 g + 7 of the step) and add their results in LDS in a fixed order.
 // The slices are summed in order s = 0 .. S-1 by whoever needs T (the reduce
 // kernel below, or the decode kernel's prologue), so every path gets the same T.
+// Stacked linears: G adapters L1_g [K, r] at L1 + g K r, all in one launch (the
+// column tiles of segment g follow those of g - 1), slices of segment g at
+// part + g S M r.
 constexpr int kPartWaves = 16;
 constexpr int kPartCh = 4;
 
@@ -472,7 +475,11 @@ __global__ __launch_bounds__(64 * kPartWaves) void k_lora_part(const uint16_t* _
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
   const int g = l >> 4, col = l & 15;
-  const int c = blockIdx.x * 16 + col;
+  const int ctiles = (r + 15) / 16;
+  const int seg = blockIdx.x / ctiles;                    // stacked adapter of this work group
+  L1 += (int64_t)seg * K * r;
+  part += (int64_t)seg * gridDim.y * M * r;
+  const int c = (blockIdx.x - seg * ctiles) * 16 + col;
   const bool c_ok = c < r;
   const bool m_ok = col < M;
   const int64_t k_beg = (int64_t)blockIdx.y * rows;
@@ -549,10 +556,10 @@ bool decode_t_ok(int64_t M, int64_t K, const void* X, const void* L1) {
 }
 
 hipError_t launch_lora_part(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float* part,
-                            hipStream_t s) {
+                            hipStream_t s, int G) {
   const int S = decode_t_slices(K);
   const int64_t rows = ((K + S - 1) / S + 31) / 32 * 32;
-  dim3 grid((unsigned)((r + 15) / 16), (unsigned)S);
+  dim3 grid((unsigned)(G * ((r + 15) / 16)), (unsigned)S);
   hipLaunchKernelGGL(k_lora_part, grid, dim3(64 * kPartWaves), 0, s, X, M, K, L1, r, rows, part);
   return hipGetLastError();
 }

@@ -223,7 +223,11 @@ int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_
  *     exactly as qlora_linear_bwd of segment g (dL1, dL2: G consecutive blocks);
  *     dX = bf16(sum_g (dY_g W'_g + G_g L1_g^T)), one rounding (NULL: skipped).
  * Requirements beyond qlora_linear_*: 1 <= G <= 16; for G > 1, N % 256 == 0 and
- * M > 16 (QL_ERR_SHAPE otherwise). Workspace from the _workspace queries.      */
+ * M > 16, except that qlora_group_fwd also takes decode sizes, 1 <= M <= 16,
+ * when X fits the decode kernel's LDS (M K <= 16384) and r % 4 == 0: then every
+ * segment's T and the whole stacked output come from two launches (Y_g and T
+ * bit-identical to qlora_linear_fwd of segment g). QL_ERR_SHAPE otherwise.
+ * Workspace from the _workspace queries.                                        */
 size_t qlora_group_fwd_workspace(int64_t M, int64_t K, int64_t N, int G, int r);
 int qlora_group_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, int G,
                     const uint8_t* codes, const uint8_t* c2, const float* c1,

@@ -195,7 +195,10 @@ def test_group_and_adamw_validation():
     assert L.qlora_group_fwd_workspace(M, K, N, 3, r) > 0
     assert L.qlora_group_fwd_workspace(M, K, 200, 3, r) == 0        # segments must be multiples of 256
     assert L.qlora_group_fwd_workspace(M, K, 200, 1, r) > 0         # a single segment is the plain layer
-    assert L.qlora_group_fwd_workspace(16, K, N, 3, r) == 0         # decode-sized M is not stacked
+    assert L.qlora_group_fwd_workspace(16, K, N, 3, r) > 0          # decode size: X fits the decode kernel's LDS
+    assert L.qlora_group_fwd_workspace(16, 2048, N, 3, r) == 0      # decode size with X above 32 KB
+    assert L.qlora_group_fwd_workspace(4, K, N, 3, 6) == 0          # decode size needs r % 4 == 0
+    assert L.qlora_group_bwd_workspace(16, K, N, 3, r) == 0         # the stacked backward needs M > 16
     assert L.qlora_group_fwd_workspace(M, K, N, 0, r) == 0
     assert L.qlora_group_fwd_workspace(M, K, N, 17, r) == 0
     assert L.qlora_group_bwd_workspace(M, K, N, 3, 65) == 0

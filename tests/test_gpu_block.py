@@ -84,6 +84,45 @@ def test_stacked_equals_separate_and_oracle(M, K, N, G, r):
         assert_close(f32np(dL2[g]), rdL2[g], f"stacked dL2[{g}]")
 
 
+@pytest.mark.parametrize("M,K,N,G,r", [(1, 4096, 256, 3, 64), (4, 512, 512, 2, 16), (3, 1024, 768, 3, 8),
+                                        (16, 1024, 256, 2, 64), (2, 8192, 256, 2, 4)])
+def test_stacked_decode_equals_separate_and_oracle(M, K, N, G, r):
+    """Decode-sized stacked forward (one T-slice launch for every adapter, one
+    decode launch over the stacked rows): Y and T equal the separate layers'
+    decode-path results bit for bit, and the oracle within the tolerance."""
+    q = qlib()
+    s = 1.5
+    seed = 31 * M + K + N + 7 * G + r
+    print(f"[group decode] M={M} K={K} N={N} G={G} r={r}", flush=True)
+    Ws, L1, L2 = _segments(G, N, K, r, seed)
+    X = WL.normal((M, K), 1.0, seed + 100).to(DEV)
+    L1d, L2d = L1.to(DEV), L2.to(DEV)
+    codes, absmax = q.nf4_quantize(torch.cat(Ws).to(DEV))
+    c2, c1 = q.nf4_double_quant(absmax)
+    Y, T = q.qlora_group_fwd(X, codes, c2, c1, N, G, L1d, L2d, s, T_out=True)
+    Y2, _ = q.qlora_group_fwd(X, codes, c2, c1, N, G, L1d, L2d, s)          # no T to write
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
+    nb = N * K // 64
+    for g in range(G):
+        cg = codes.view(-1)[g * N * K // 2:(g + 1) * N * K // 2]
+        c2g = c2.view(-1)[g * nb:(g + 1) * nb]
+        c1g = c1.view(-1)[g * nb // 256:(g + 1) * nb // 256]
+        Yg, Tg = q.qlora_linear_fwd(X, cg, c2g, c1g, N, L1d[g], L2d[g], s, T_out=True)
+        torch.cuda.synchronize()
+        assert torch.equal(Y[:, g * N:(g + 1) * N].view(torch.int16), Yg.view(torch.int16)), g
+        assert torch.equal(T[g].view(torch.int16), Tg.view(torch.int16)), g
+    Wq = []
+    for g in range(G):
+        rc, ra = O.nf4_quantize(Ws[g].float().numpy())
+        rc2, rc1 = O.nf4_double_quant(ra)
+        Wq.append(O.nf4_dequantize(rc, rc2, rc1, N, K))
+    rY, rT = B.qlora_group_forward(bits(X), Wq, [bits(L1[g]) for g in range(G)], [bits(L2[g]) for g in range(G)], s)
+    assert_close(bits(Y), rY, "stacked decode Y")
+    for g in range(G):
+        assert_close(bits(T[g]), rT[g], f"stacked decode T[{g}]")
+
+
 @pytest.mark.parametrize("names", [("q", "k", "v"), ("gate", "up")])
 def test_stacked_llama65b_full(names):
     """The stacked q|k|v and gate|up of a LLaMA-65B block at M = 2048 tokens
