@@ -59,8 +59,7 @@ BwdWs bwd_ws(int64_t M, int64_t K, int64_t N, int r) {
   w.g_bytes = round_up((size_t)M * r * 2);
   size_t p = lora_skinny_ws(M, K, r);
   p = std::max(p, lora_skinny_ws(M, N, r));
-  p = std::max(p, lora_tn_ws(M, K, r));
-  p = std::max(p, lora_tn_ws(M, N, r));
+  p = std::max(p, lora_tn_pair_ws(M, K, N, r));
   w.part_bytes = round_up(p);
   w.total = w.t_bytes + w.g_bytes + w.part_bytes;
   return w;
@@ -111,8 +110,7 @@ GroupWs group_ws(int64_t M, int64_t K, int64_t N, int G, int r) {
   w.g_bytes = round_up((size_t)G * M * r * 2);
   size_t p = lora_skinny_ws(M, K, r);
   p = std::max(p, lora_skinny_ws(M, N, r));
-  p = std::max(p, lora_tn_ws(M, K, r));
-  p = std::max(p, lora_tn_ws(M, N, r));
+  p = std::max(p, lora_tn_pair_ws(M, K, N, r));
   w.part_bytes = round_up(p);
   w.total = w.t_bytes + w.g_bytes + w.part_bytes;
   return w;
@@ -308,9 +306,8 @@ int qlora_group_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K,
   if (dX) QL_TRY(launch_qgemm_big(true, dY, M, K, N * G, codes, c2, c1, Gm, L1, r, 1.0f, dX, s, G));
   for (int g = 0; g < G; ++g) {
     const int64_t mr = (int64_t)g * M * r;
-    QL_TRY(launch_lora_tn(X, K, Gm + mr, M, K, r, 1.0f, false, dL1 + (int64_t)g * K * r, part, s));
-    QL_TRY(launch_lora_tn(dY + (int64_t)g * N, ldy, Tg + mr, M, N, r, lora_scale, true, dL2 + (int64_t)g * r * N,
-                          part, s));
+    QL_TRY(launch_lora_tn_pair(X, K, Gm + mr, K, 1.0f, dL1 + (int64_t)g * K * r, dY + (int64_t)g * N, ldy, Tg + mr,
+                               N, lora_scale, dL2 + (int64_t)g * r * N, M, r, part, s));
   }
   return QL_OK;
 }
@@ -395,8 +392,7 @@ int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K
   }
   QL_TRY(launch_lora_skinny(dY, M, N, N, L2, false, r, lora_scale, G, part, s));
   if (dX) QL_TRY(run_dx_gemm(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s));
-  QL_TRY(launch_lora_tn(X, K, G, M, K, r, 1.0f, false, dL1, part, s));
-  QL_TRY(launch_lora_tn(dY, N, T, M, N, r, lora_scale, true, dL2, part, s));
+  QL_TRY(launch_lora_tn_pair(X, K, G, K, 1.0f, dL1, dY, N, T, N, lora_scale, dL2, M, r, part, s));
   return QL_OK;
 }
 
@@ -520,8 +516,7 @@ int lora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K,
   }
   QL_TRY(launch_lora_skinny(dY, M, N, N, L2, false, r, lora_scale, G, part, s));
   if (dX) QL_TRY(launch_bgemm_big(true, dY, M, K, N, W, G, L1, r, 1.0f, dX, s));
-  QL_TRY(launch_lora_tn(X, K, G, M, K, r, 1.0f, false, dL1, part, s));
-  QL_TRY(launch_lora_tn(dY, N, T, M, N, r, lora_scale, true, dL2, part, s));
+  QL_TRY(launch_lora_tn_pair(X, K, G, K, 1.0f, dL1, dY, N, T, N, lora_scale, dL2, M, r, part, s));
   return QL_OK;
 }
 

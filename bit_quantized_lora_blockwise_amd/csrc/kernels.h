@@ -69,6 +69,13 @@ hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t l
 // C[p, c] = scale * sum_m A[m][p] * B[m][c] with A [M, P] (row stride lda),
 // B [M, r]; stored as out[P, r] (transpose_out = false) or out[r, P] (true), fp32.
 size_t lora_tn_ws(int64_t M, int64_t P, int r);
+// Two such products in one launch (and their sums in one more): the first
+// stored out0[P0, r], the second transposed out1_t[r, P1]; the workspace holds
+// both products' partials (lora_tn_pair_ws).
+size_t lora_tn_pair_ws(int64_t M, int64_t P0, int64_t P1, int r);
+hipError_t launch_lora_tn_pair(const uint16_t* A0, int64_t lda0, const uint16_t* B0, int64_t P0, float scale0,
+                               float* out0, const uint16_t* A1, int64_t lda1, const uint16_t* B1, int64_t P1,
+                               float scale1, float* out1_t, int64_t M, int r, float* ws, hipStream_t s);
 hipError_t launch_lora_tn(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t M, int64_t P, int r,
                           float scale, bool transpose_out, float* out, float* ws, hipStream_t s);
 

@@ -337,17 +337,17 @@ __global__ __launch_bounds__(kThreads) void k_skinny_reduce(const float* __restr
   }
 }
 
-// C[p, c] partial over one slice of m: sum_m A[m][p] * B[m][c], A [M, P], B [M, r].
+// C[p, c] partial over one slice of m: sum_m A[m][p] * B[m][c], A [M, P], B [M, r];
+// this work group's tile of 64 p is `tile`, its slice of m is `split`.
 template <bool kVecA, bool kVecB>
-__global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict__ A, int64_t lda,
-                                                      const uint16_t* __restrict__ B, int64_t M, int64_t P, int r,
-                                                      int64_t chunk, float* __restrict__ part) {
+__device__ __forceinline__ void tn_tile(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
+                                        int64_t M, int64_t P, int r, int64_t chunk, float* __restrict__ part,
+                                        int tile, int split) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * kPitch];
   const int w = threadIdx.x >> 6;
   const int wp = w & 1, wc = w >> 1;
-  const int64_t p0 = (int64_t)blockIdx.x * kTile;
-  const int split = blockIdx.y;
+  const int64_t p0 = (int64_t)tile * kTile;
   const int64_t m_beg = split * chunk;
   const int64_t m_end = min(M, m_beg + chunk);
   const int64_t nsteps = (m_end - m_beg + kTile - 1) / kTile;
@@ -395,11 +395,39 @@ __global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_tn_reduce(const float* __restrict__ part, int splits, int64_t P, int r,
-                                                        float scale, float* __restrict__ out) {
+template <bool kVecA, bool kVecB>
+__global__ __launch_bounds__(kThreads) void k_lora_tn(const uint16_t* __restrict__ A, int64_t lda,
+                                                      const uint16_t* __restrict__ B, int64_t M, int64_t P, int r,
+                                                      int64_t chunk, float* __restrict__ part) {
+  tn_tile<kVecA, kVecB>(A, lda, B, M, P, r, chunk, part, blockIdx.x, blockIdx.y);
+}
+
+// Two independent products of this kind in one launch (the backward's dL1 and
+// dL2): work groups 0 .. n0 - 1 take the first, the rest the second.
+struct TnJob {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t P, chunk;
+  float* part;
+  int tiles, splits;
+};
+
+template <bool kVecA, bool kVecB>
+__global__ __launch_bounds__(kThreads) void k_lora_tn_pair(TnJob j0, TnJob j1, int64_t M, int r) {
+  const int n0 = j0.tiles * j0.splits;
+  const bool second = (int)blockIdx.x >= n0;         // uniform over the work group
+  const TnJob j = second ? j1 : j0;
+  const int b = second ? (int)blockIdx.x - n0 : (int)blockIdx.x;
+  tn_tile<kVecA, kVecB>(j.A, j.lda, j.B, M, j.P, r, j.chunk, j.part, b % j.tiles, b / j.tiles);
+}
+
+// out[i] = scale * (sum of the slices), i over P * r, by work groups blk of nblk.
+__device__ __forceinline__ void tn_reduce_span(const float* __restrict__ part, int splits, int64_t P, int r,
+                                               float scale, float* __restrict__ out, int blk, int nblk) {
   const int64_t n = P * r;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t stride = (int64_t)nblk * kThreads;
+  const int64_t t0 = (int64_t)blk * kThreads + threadIdx.x;
   if ((n & 3) == 0) {
     const int64_t n4 = n >> 2;
     for (int64_t i4 = t0; i4 < n4; i4 += stride) ((f32x4*)out)[i4] = scale * sum_splits4((const f32x4*)part, splits, n4, i4);
@@ -412,17 +440,22 @@ __global__ __launch_bounds__(kThreads) void k_tn_reduce(const float* __restrict_
   }
 }
 
+__global__ __launch_bounds__(kThreads) void k_tn_reduce(const float* __restrict__ part, int splits, int64_t P, int r,
+                                                        float scale, float* __restrict__ out) {
+  tn_reduce_span(part, splits, P, r, scale, out, blockIdx.x, gridDim.x);
+}
+
 // Same sum written transposed, out[c * P + p] for the partial element p * r + c:
 // a work group takes 16 consecutive p, adds its 16 x r partials (each thread
 // four adjacent c of one p when r % 4 == 0, all loads of a group issued
 // together) into LDS and writes r rows of 16 contiguous outputs.
 constexpr int kTrP = 16;
 
-__global__ __launch_bounds__(kThreads) void k_tn_reduce_t(const float* __restrict__ part, int splits, int64_t P, int r,
-                                                          float scale, float* __restrict__ out) {
+__device__ __forceinline__ void tn_reduce_t_block(const float* __restrict__ part, int splits, int64_t P, int r,
+                                                  float scale, float* __restrict__ out, int blk) {
   __shared__ float tile[kTrP][65];
   const int64_t n = P * r;
-  const int64_t p0 = (int64_t)blockIdx.x * kTrP;
+  const int64_t p0 = (int64_t)blk * kTrP;
   const int np = (int)min((int64_t)kTrP, P - p0);
   if ((r & 3) == 0) {
     const int r4 = r >> 2;
@@ -446,6 +479,22 @@ __global__ __launch_bounds__(kThreads) void k_tn_reduce_t(const float* __restric
     const int c = e / kTrP, pl = e - c * kTrP;
     if (pl < np) out[(int64_t)c * P + p0 + pl] = tile[pl][c];
   }
+}
+
+__global__ __launch_bounds__(kThreads) void k_tn_reduce_t(const float* __restrict__ part, int splits, int64_t P, int r,
+                                                          float scale, float* __restrict__ out) {
+  tn_reduce_t_block(part, splits, P, r, scale, out, blockIdx.x);
+}
+
+// The two sums of a k_lora_tn_pair launch in one launch: work groups 0 .. nb0 - 1
+// write the first product as out0[P0, r], the rest the second transposed as
+// out1[r, P1].
+__global__ __launch_bounds__(kThreads) void k_tn_reduce_pair(const float* __restrict__ part0, int splits0, int64_t P0,
+                                                             float scale0, float* __restrict__ out0, int nb0,
+                                                             const float* __restrict__ part1, int splits1, int64_t P1,
+                                                             float scale1, float* __restrict__ out1, int r) {
+  if ((int)blockIdx.x < nb0) tn_reduce_span(part0, splits0, P0, r, scale0, out0, blockIdx.x, nb0);
+  else tn_reduce_t_block(part1, splits1, P1, r, scale1, out1, (int)blockIdx.x - nb0);
 }
 
 int grid_for(int64_t items) {
@@ -662,6 +711,37 @@ hipError_t launch_lora_skinny(const uint16_t* A, int64_t M, int64_t R, int64_t l
 size_t lora_tn_ws(int64_t M, int64_t P, int r) {
   const SplitPlan sp = plan_rowsplit((P + kTile - 1) / kTile, M);
   return (size_t)sp.splits * P * r * sizeof(float);
+}
+
+size_t lora_tn_pair_ws(int64_t M, int64_t P0, int64_t P1, int r) {
+  return (lora_tn_ws(M, P0, r) + 255) / 256 * 256 + lora_tn_ws(M, P1, r);
+}
+
+hipError_t launch_lora_tn_pair(const uint16_t* A0, int64_t lda0, const uint16_t* B0, int64_t P0, float scale0,
+                               float* out0, const uint16_t* A1, int64_t lda1, const uint16_t* B1, int64_t P1,
+                               float scale1, float* out1_t, int64_t M, int r, float* ws, hipStream_t s) {
+  const bool vec = (P0 % 8) == 0 && (lda0 % 8) == 0 && ((uintptr_t)A0 & 15) == 0 && (P1 % 8) == 0 &&
+                   (lda1 % 8) == 0 && ((uintptr_t)A1 & 15) == 0 && (r % 8) == 0 && ((uintptr_t)B0 & 15) == 0 &&
+                   ((uintptr_t)B1 & 15) == 0;
+  float* part1 = ws + (lora_tn_ws(M, P0, r) + 255) / 256 * 256 / sizeof(float);
+  if (!vec) {
+    hipError_t e = launch_lora_tn(A0, lda0, B0, M, P0, r, scale0, false, out0, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_lora_tn(A1, lda1, B1, M, P1, r, scale1, true, out1_t, part1, s);
+  }
+  const SplitPlan sp0 = plan_rowsplit((P0 + kTile - 1) / kTile, M);
+  const SplitPlan sp1 = plan_rowsplit((P1 + kTile - 1) / kTile, M);
+  const TnJob j0{A0, lda0, B0, P0, sp0.chunk, ws, (int)((P0 + kTile - 1) / kTile), sp0.splits};
+  const TnJob j1{A1, lda1, B1, P1, sp1.chunk, part1, (int)((P1 + kTile - 1) / kTile), sp1.splits};
+  const unsigned nwg = (unsigned)(j0.tiles * j0.splits + j1.tiles * j1.splits);
+  hipLaunchKernelGGL((k_lora_tn_pair<true, true>), dim3(nwg), dim3(kThreads), 0, s, j0, j1, M, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nb0 = grid_for((P0 * r + 3) / 4);
+  const unsigned nb1 = (unsigned)((P1 + kTrP - 1) / kTrP);
+  hipLaunchKernelGGL(k_tn_reduce_pair, dim3((unsigned)nb0 + nb1), dim3(kThreads), 0, s, ws, sp0.splits, P0, scale0,
+                     out0, nb0, part1, sp1.splits, P1, scale1, out1_t, r);
+  return hipGetLastError();
 }
 
 hipError_t launch_lora_tn(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t M, int64_t P, int r,
