@@ -288,6 +288,15 @@ def test_llama65b_block_linear_full(name):
     _big_case(WL.config4_linear(name), f"llama65b {name} M=2048")
 
 
+@pytest.mark.parametrize("M,K,N,r", [(300, 4160, 1000, 24), (1000, 640, 2048, 64), (130, 8192, 512, 8)])
+def test_streaming_lora_products_partial_steps(M, K, N, r):
+    """Shapes that take the streaming skinny kernel (reduction, row stride and r
+    multiples of 8) with a partial last 64-column step, a partial last group of
+    four steps, ragged 64-row tiles and a rank that leaves an MFMA column tile
+    partly empty; every output of the layer against the oracle."""
+    full_case(WL.layer_inputs(N, K, M, r, seed_base=777 + M + r, l2_std=0.1), 0.75, "streaming lora")
+
+
 @pytest.mark.parametrize("M", [8, 96])
 def test_stage_entry_points_match_fused_calls(M):
     """lora_down + fwd_t == fwd; grad_in + dx == the dX of bwd (same kernels, bitwise)."""
