@@ -31,9 +31,13 @@ int hip_status(hipError_t e) {
     if (e_ != hipSuccess) return hip_status(e_); \
   } while (0)
 
+// The kernels address activations and packed codes with 32-bit buffer offsets:
+// X and dX (M K bf16), Y and dY (M N bf16) and W's codes (N K / 2 bytes) must
+// each stay below 2^31 bytes; larger batches are split by the caller.
 bool shapes_ok(int64_t M, int64_t K, int64_t N, int r) {
-  return M > 0 && K > 0 && N > 0 && (K % 64) == 0 && r >= 1 && r <= 64 &&
-         M <= (int64_t(1) << 31) && K <= (int64_t(1) << 31) && N <= (int64_t(1) << 31);
+  constexpr int64_t kLim = int64_t(1) << 31;
+  return M > 0 && K > 0 && N > 0 && (K % 64) == 0 && r >= 1 && r <= 64 && M < kLim && K < kLim && N < kLim &&
+         M * K * 2 < kLim && M * N * 2 < kLim && N * (K / 2) < kLim;
 }
 
 // Workspace layout of the forward: [T (M x r bf16) when the caller gives no T_out][fp32 partials].
@@ -65,13 +69,13 @@ BwdWs bwd_ws(int64_t M, int64_t K, int64_t N, int r) {
   return w;
 }
 
-// Forward product for M > 16: the large-tile kernel when the shapes qualify.
+// Forward product for M > 16: the large-tile kernel, which takes every shape
+// shapes_ok accepts (K % 64 == 0 makes its rows 16-byte aligned).
 hipError_t run_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes, const uint8_t* c2,
                         const float* c1, const uint16_t* T, const uint16_t* L2, int r, float scale, uint16_t* Y,
                         hipStream_t s) {
-  if (qgemm_big_ok(false, M, K, N))
-    return launch_qgemm_big(false, X, M, K, N, codes, c2, c1, T, L2, r, scale, Y, s);
-  return launch_qgemm_fwd(X, M, K, N, codes, c2, c1, T, L2, r, scale, Y, s);
+  if (!qgemm_big_ok(false, M, K, N)) return hipErrorInvalidValue;
+  return launch_qgemm_big(false, X, M, K, N, codes, c2, c1, T, L2, r, scale, Y, s);
 }
 
 hipError_t run_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint8_t* codes, const uint8_t* c2,
@@ -429,7 +433,9 @@ int qlora_linear_fwd_t(const uint16_t* X, int64_t M, int64_t K, int64_t N, const
 }
 
 size_t qlora_lora_grad_in_workspace(int64_t M, int64_t N, int r) {
-  if (!(M > 0 && N > 0 && r >= 1 && r <= 64 && M <= (int64_t(1) << 31) && N <= (int64_t(1) << 31))) return 0;
+  if (!(M > 0 && N > 0 && r >= 1 && r <= 64 && M < (int64_t(1) << 31) && N < (int64_t(1) << 31) &&
+        M * N * 2 < (int64_t(1) << 31)))
+    return 0;
   return round_up(lora_skinny_ws(M, N, r));
 }
 
@@ -530,7 +536,9 @@ const char* ql_status_string(int status) {
   switch (status) {
     case QL_OK: return "ok";
     case QL_ERR_NULL: return "a required pointer is NULL";
-    case QL_ERR_SHAPE: return "invalid shape (sizes must be > 0, K and cols multiples of 64, 1 <= r <= 64)";
+    case QL_ERR_SHAPE:
+      return "invalid shape (sizes must be > 0, K and cols multiples of 64, 1 <= r <= 64, each activation "
+             "matrix and the packed codes below 2^31 bytes)";
     case QL_ERR_DTYPE: return "unsupported dtype, code book or scale code";
     case QL_ERR_VALUE: return "hyper-parameter out of range";
     case QL_ERR_ALIGN: return "device pointers must be 16-byte aligned";

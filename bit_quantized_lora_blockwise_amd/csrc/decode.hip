@@ -797,15 +797,13 @@ hipError_t launch_lds(dim3 grid, hipStream_t s, const QgemvArgs& a) {
 
 template <bool kTPart>
 hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
-  // Buffer offsets are 32-bit: split the rows into chunks whose packed codes stay
-  // below 2^31 bytes; chunks start on multiples of 256 rows, so every chunk's
-  // blocks start a new double-quantisation group.
-  const int64_t K = a0.K, M = a0.M;
-  const int64_t kblocks = K / qk::kBlock;
-  if (M * K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  int64_t chunk = ((int64_t(1) << 31) - (int64_t(1) << 20)) / (K / 2);
-  chunk = chunk / 256 * 256;
-  if (chunk < 256) return hipErrorInvalidValue;
+  // Buffer offsets are 32-bit: X and the packed codes must each stay below 2^31
+  // bytes (the library's shape check guarantees both).
+  QgemvArgs a = a0;
+  a.rows = N;
+  a.ld = N;
+  const int64_t K = a.K, M = a.M;
+  if (M * K * 2 >= (int64_t(1) << 31) || N * (K / 2) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const bool xlds = M * K * 2 <= kXBytes;
   const bool xpersist = !xlds && M * K * 2 <= kXPersistBytes;
   int cus = 0;
@@ -815,44 +813,29 @@ hipError_t launch_shape(const QgemvArgs& a0, int64_t N, hipStream_t s) {
                                                 hipSuccess || cus < 1)
       cus = 256;
   }
-  for (int64_t r0 = 0; r0 < N; r0 += chunk) {
-    QgemvArgs a = a0;
-    a.rows = N - r0 < chunk ? N - r0 : chunk;
-    a.ld = N;
-    a.codes = a0.codes + r0 * (K / 2);
-    a.c2 = a0.c2 + r0 * kblocks;
-    a.c1 = a0.c1 + r0 * kblocks / 256;
-    a.L2 = a0.L2 + r0;
-    a.Y = a0.Y + r0;
-    if (kTPart && r0 > 0) a.T = nullptr;           // the formed T is written by the first chunk's work group 0
-    const int64_t wgs = (a.rows + kRows - 1) / kRows;
-    dim3 grid((unsigned)wgs);
-    // X read from global memory: 16 waves per work group when the grid alone
-    // would leave SIMDs with fewer than two waves, else 4
-    const bool wide = wgs <= 384;
-    hipError_t e;
-    // X above 128 KB: the slice kernel, one work group per CU (cus >= 1 here)
-    // with at most tpw tiles each, slices a multiple of 4096 columns wide.
-    // Several tiles per work group are measured ahead of X read from global
-    // memory from M = 6 (8192 <-> 22016), behind it at M = 4.
-    const bool big = !xlds && !xpersist;
-    const int64_t ksl = big ? (kXPersistBytes / (2 * M)) / 4096 * 4096 : 0;
-    const int64_t sg = big ? (wgs < cus ? wgs : cus) : 1;
-    const int64_t tpw = (wgs + sg - 1) / sg;
-    if (big && ksl >= 4096 && (tpw == 1 || (tpw <= 8 && M >= 6))) {
-      e = launch_slices<kTPart>((int)tpw, (unsigned)sg, ksl, s, a);
-    } else if (xpersist) {
-      const unsigned pg = (unsigned)(wgs < cus ? wgs : cus);
-      hipLaunchKernelGGL((k_qgemv_persist<kTPart>), dim3(pg), dim3(512), 0, s, a.X, a.M, a.K, a.rows, a.ld, a.codes,
-                         a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params());
-      e = hipGetLastError();
-    } else if (xlds)
-      e = launch_lds<8, kTPart>(grid, s, a);     // 8 waves: measured ahead of 16 on small grids too
-    else   // X read with each step (127 VGPRs): four waves keep four work groups per CU resident
-      e = wide ? launch_one<false, 16, 1, kTPart>(grid, s, a) : launch_one<false, 4, 1, kTPart>(grid, s, a);
-    if (e != hipSuccess) return e;
+  const int64_t wgs = (a.rows + kRows - 1) / kRows;
+  dim3 grid((unsigned)wgs);
+  // X read from global memory: 16 waves per work group when the grid alone
+  // would leave SIMDs with fewer than two waves, else 4
+  const bool wide = wgs <= 384;
+  // X above 128 KB: the slice kernel, one work group per CU (cus >= 1 here)
+  // with at most tpw tiles each, slices a multiple of 4096 columns wide.
+  // Several tiles per work group are measured ahead of X read from global
+  // memory from M = 6 (8192 <-> 22016), behind it at M = 4.
+  const bool big = !xlds && !xpersist;
+  const int64_t ksl = big ? (kXPersistBytes / (2 * M)) / 4096 * 4096 : 0;
+  const int64_t sg = big ? (wgs < cus ? wgs : cus) : 1;
+  const int64_t tpw = (wgs + sg - 1) / sg;
+  if (big && ksl >= 4096 && (tpw == 1 || (tpw <= 8 && M >= 6))) return launch_slices<kTPart>((int)tpw, (unsigned)sg, ksl, s, a);
+  if (xpersist) {
+    const unsigned pg = (unsigned)(wgs < cus ? wgs : cus);
+    hipLaunchKernelGGL((k_qgemv_persist<kTPart>), dim3(pg), dim3(512), 0, s, a.X, a.M, a.K, a.rows, a.ld, a.codes,
+                       a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params());
+    return hipGetLastError();
   }
-  return hipSuccess;
+  if (xlds) return launch_lds<8, kTPart>(grid, s, a);     // 8 waves: measured ahead of 16 on small grids too
+  // X read with each step (127 VGPRs): four waves keep four work groups per CU resident
+  return wide ? launch_one<false, 16, 1, kTPart>(grid, s, a) : launch_one<false, 4, 1, kTPart>(grid, s, a);
 }
 
 }  // namespace

@@ -1,6 +1,6 @@
-// Quantised GEMMs of the layer for training-sized M:
-//   forward  Y  = bf16(X W'^T + s T L2)
-//   backward dX = bf16(dY W' + G L1^T)       (transposed-weight path)
+// Backward GEMM of the layer for the shapes the large-tile kernel does not
+// take (N % 8 != 0, whose dY rows are not 16-byte aligned, and M <= 16):
+//   dX = bf16(dY W' + G L1^T)       (transposed-weight path)
 // W' = doubleDequant(c1, c2, W_NF4) is rebuilt tile by tile from the packed
 // 4-bit stream into bf16 in LDS and fed to bf16 MFMA; it never reaches HBM.
 // Layer formula: nlp-lineage milestone page on QLoRA, "The idea", notation
@@ -64,105 +64,6 @@ __device__ __forceinline__ void stage_rows128(LDS_AS uint16_t* dst, const uint16
     if (r0 + row < rows) v = load_row8(src + (r0 + row) * ld, c0 + cc, cols);
     *(LDS_AS u32x4*)(dst + row * kPA + cc) = v;
   }
-}
-
-// ---------------------------------------------------------------------------
-// Forward: tile of 128 rows (m) x 128 columns (n); 4 waves in 2 x 2, each wave
-// 64 x 64 = 2 x 2 MFMA 32x32 tiles.
-__global__ __launch_bounds__(kThreads) void k_qgemm_fwd(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                        int64_t N, const uint8_t* __restrict__ codes,
-                                                        const uint8_t* __restrict__ c2,
-                                                        const float* __restrict__ c1,
-                                                        const uint16_t* __restrict__ T,
-                                                        const uint16_t* __restrict__ L2, int r, float scale,
-                                                        uint16_t* __restrict__ Y, Nf4Params p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kPA];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kPA];  // also holds the [64][kPB] L2 tile in the prologue
-  __shared__ __attribute__((aligned(16))) float qs[16];
-  const int t = threadIdx.x;
-  const int w = t >> 6;
-  const int wm = w & 1, wn = w >> 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int64_t n0 = (int64_t)blockIdx.x * kBN;
-  if (t < 16) qs[t] = p.q[t];
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  // LoRA term first: acc = s * (T L2) over the rank (zero-padded to 64).
-  {
-    stage_rows128((LDS_AS uint16_t*)As, T, r, M, r, m0, 0);  // As[m][c] = T[m0+m][c]
-    // Bs[c][n] = L2[c][n0 + n], 64 x 128, pitch kPB
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = (t >> 4) + 16 * i;
-      const int nn = (t & 15) * 8;
-      u32x4 v = {0, 0, 0, 0};
-      if (c < r) v = load_row8(L2 + (int64_t)c * N, n0 + nn, N);
-      *(LDS_AS u32x4*)((LDS_AS uint16_t*)Bs + c * kPB + nn) = v;
-    }
-    __syncthreads();
-    const int ksteps = (r + 15) / 16;
-    for (int s = 0; s < ksteps; ++s) {
-      bf16x8 a0 = qk::frag_rowmajor((const LDS_AS uint16_t*)As, kPA, 64 * wm, 16 * s);
-      bf16x8 a1 = qk::frag_rowmajor((const LDS_AS uint16_t*)As, kPA, 64 * wm + 32, 16 * s);
-      bf16x8 b0 = qk::frag_kmajor((const LDS_AS uint16_t*)Bs, kPB, 16 * s, 64 * wn);
-      bf16x8 b1 = qk::frag_kmajor((const LDS_AS uint16_t*)Bs, kPB, 16 * s, 64 * wn + 32);
-      acc[0][0] = qk::mfma32(a0, b0, acc[0][0]);
-      acc[0][1] = qk::mfma32(a0, b1, acc[0][1]);
-      acc[1][0] = qk::mfma32(a1, b0, acc[1][0]);
-      acc[1][1] = qk::mfma32(a1, b1, acc[1][1]);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] *= scale;
-    __syncthreads();
-  }
-
-  const int64_t kblocks = K / kBK;
-  const int drow = t >> 1, dhalf = t & 1;           // dequant: one row, 32 weights per thread
-  const int64_t wrow = n0 + drow;
-  for (int64_t kt = 0; kt < kblocks; ++kt) {
-    stage_rows128((LDS_AS uint16_t*)As, X, K, M, K, m0, kt * kBK);
-    LDS_AS uint16_t* bdst = (LDS_AS uint16_t*)Bs + drow * kPA + 32 * dhalf;
-    if (wrow < N) {
-      const int64_t b = wrow * kblocks + kt;
-      const u32x4 cw = *(const u32x4*)(codes + wrow * (K / 2) + kt * 32 + 16 * dhalf);
-      dequant32_to_lds(bdst, cw, block_scale(c2, c1, b), (const LDS_AS float*)qs);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *(LDS_AS u32x4*)(bdst + 8 * i) = u32x4{0, 0, 0, 0};
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 a0 = qk::frag_rowmajor((const LDS_AS uint16_t*)As, kPA, 64 * wm, 16 * s);
-      bf16x8 a1 = qk::frag_rowmajor((const LDS_AS uint16_t*)As, kPA, 64 * wm + 32, 16 * s);
-      bf16x8 b0 = qk::frag_rowmajor((const LDS_AS uint16_t*)Bs, kPA, 64 * wn, 16 * s);
-      bf16x8 b1 = qk::frag_rowmajor((const LDS_AS uint16_t*)Bs, kPA, 64 * wn + 32, 16 * s);
-      acc[0][0] = qk::mfma32(a0, b0, acc[0][0]);
-      acc[0][1] = qk::mfma32(a0, b1, acc[0][1]);
-      acc[1][0] = qk::mfma32(a1, b0, acc[1][0]);
-      acc[1][1] = qk::mfma32(a1, b1, acc[1][1]);
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + 64 * wn + 32 * j + qk::acc_col();
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + 64 * wm + 32 * i + qk::acc_row(e);
-        if (m < M && n < N) Y[m * N + n] = qk::f32_to_bf16(acc[i][j][e]);
-      }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -259,15 +160,6 @@ __global__ __launch_bounds__(kThreads) void k_qgemm_dx(const uint16_t* __restric
 }
 
 }  // namespace
-
-hipError_t launch_qgemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
-                            const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
-                            float scale, uint16_t* Y, hipStream_t s) {
-  dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL(k_qgemm_fwd, grid, dim3(kThreads), 0, s, X, M, K, N, codes, c2, c1, T, L2, r, scale, Y,
-                     nf4_params());
-  return hipGetLastError();
-}
 
 hipError_t launch_qgemm_dx(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                            const uint8_t* c2, const float* c1, const uint16_t* G, const uint16_t* L1, int r,

@@ -91,12 +91,9 @@ hipError_t launch_adamw(float* param, float* exp_avg, float* exp_avg_sq, const f
                         int64_t n, float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step,
                         hipStream_t s);
 
-// --- quantised GEMMs (gemm.hip, decode.hip) ----------------------------------
-// Y[M, N] = bf16(X W'^T + scale * T L2)
-hipError_t launch_qgemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
-                            const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
-                            float scale, uint16_t* Y, hipStream_t s);
-// Same result for small M (M <= 16), streaming the packed weight once.
+// --- quantised GEMMs (gemm_big.hip, gemm.hip, decode.hip) ----------------------
+// Y[M, N] = bf16(X W'^T + scale * T L2) for small M (M <= 16), streaming the
+// packed weight once (training-sized M: launch_qgemm_big below).
 hipError_t launch_qgemv_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                             const uint8_t* c2, const float* c1, const uint16_t* T, const uint16_t* L2, int r,
                             float scale, uint16_t* Y, hipStream_t s);

@@ -55,7 +55,8 @@ extern "C" {
 typedef enum {
   QL_OK = 0,
   QL_ERR_NULL = -1,      /* a required pointer is NULL                            */
-  QL_ERR_SHAPE = -2,     /* a size is <= 0, K % 64 != 0, r outside [1, 64], ...   */
+  QL_ERR_SHAPE = -2,     /* a size <= 0, K % 64 != 0, r outside [1, 64], a matrix
+                            of the layer calls at 2^31 bytes or more, ...       */
   QL_ERR_DTYPE = -3,     /* unsupported dtype, code book or scale code            */
   QL_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned               */
   QL_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the query returns      */
@@ -112,7 +113,9 @@ size_t qlora_linear_fwd_workspace(int64_t M, int64_t K, int64_t N, int r);
  *   T = bf16(X L1),  Y = bf16(X W'^T + lora_scale * (T L2)),
  * fp32 accumulation, W' as in nf4_dequantize (never materialised).
  * X [M, K] bf16; codes/c2/c1 describe W [N, K]; L1 [K, r] bf16; L2 [r, N] bf16;
- * 1 <= r <= 64. Outputs: Y [M, N] bf16; T_out [M, r] bf16 when non-NULL (keep it
+ * 1 <= r <= 64, K % 64 == 0; X (2 M K bytes), Y (2 M N bytes) and the codes
+ * (N K / 2 bytes) must each stay below 2^31 bytes (split larger batches).
+ * Outputs: Y [M, N] bf16; T_out [M, r] bf16 when non-NULL (keep it
  * for the backward). workspace: ws_bytes >= qlora_linear_fwd_workspace(...),
  * contents need no initialisation and are clobbered.                          */
 int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
@@ -164,8 +167,8 @@ int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K
 
 /* Stage entry points: the single fused kernels of the layer, for callers that
  * keep the LoRA intermediates themselves (activation checkpointing, graph
- * capture of individual stages, per-kernel timing). Same formulas, layouts
- * and rounding points as the calls above.
+ * capture of individual stages, per-kernel timing). Same formulas, layouts,
+ * rounding points and size limits as the calls above.
  *
  * qlora_lora_down: T = bf16(X L1) [M, r] (nlp-lineage page, notation paragraph,
  * the X L1 factor of the adapter path). ws_bytes >= qlora_lora_down_workspace().  */

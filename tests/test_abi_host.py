@@ -339,6 +339,28 @@ def test_binding_rejects_wrong_sized_inputs():
         q.qlora_linear_fwd(X, codes, c2, c1, 64, L1, L2)
 
 
+def test_layer_calls_reject_matrices_of_2_gib():
+    """The layer's kernels address X/dX, Y/dY and the packed codes with 32-bit
+    offsets: a shape that makes any of them 2^31 bytes or more is refused on the
+    host (the size queries return 0, the calls QL_ERR_SHAPE), one size below is
+    accepted."""
+    _, L = _lib()
+    r = 16
+    for M, K, N in [(262144, 4096, 256),        # X: 2 M K = 2^31 bytes
+                    (262144, 256, 4096),        # Y / dY: 2 M N = 2^31 bytes
+                    (64, 4096, 1 << 20)]:       # codes: N K / 2 = 2^31 bytes
+        assert L.qlora_linear_fwd_workspace(M, K, N, r) == 0
+        assert L.qlora_linear_bwd_workspace(M, K, N, r) == 0
+        assert L.qlora_linear_fwd(A, M, K, N, A, A, A, A, A, r, 1.0, A, None, A, 1 << 40, None) == -2
+        assert L.qlora_linear_bwd(A, A, M, K, N, A, A, A, A, A, r, 1.0, None, None, A, A, A, 1 << 40, None) == -2
+        assert L.qlora_linear_fwd_t(A, M, K, N, A, A, A, A, A, r, 1.0, A, None) == -2
+        assert L.qlora_linear_dx(A, M, K, N, A, A, A, A, A, r, A, None) == -2
+    assert L.qlora_linear_fwd_workspace(262143, 4096, 256, r) > 0
+    assert L.qlora_linear_fwd_workspace(64, 4096, (1 << 20) - 64, r) > 0
+    assert L.qlora_lora_down_workspace(262144, 4096, r) == 0
+    assert L.qlora_lora_grad_in_workspace(262144, 4096, r) == 0
+
+
 def test_noalloc_forward_validation():
     """The forward that allocates nothing refuses sizes whose scratch exceeds its
     static array, and bad arguments, on the host (before any HIP call)."""
