@@ -28,13 +28,14 @@ struct Nf4Params {
 
 // Encoder lookup over 34 buckets of width 1/16 in n (index floor(16 n) + 17,
 // n in [-1, 1]); each bucket holds at most one threshold.  For bucket i:
-// t16[i] = 16 * (its threshold), or +inf when it has none; mb[i] = bits of a
-// power-of-two margin m (|16 n' - t16| <= m marks an approximate n' as too
-// close to decide), whose low 4 bits hold the number of thresholds at or below
-// the bucket's lower end.  Built on the host (see nf4_table.cpp).
+// t16[i] = 16 * (its threshold), or +inf when it has none; cnt[i] = the number
+// of thresholds at or below the bucket's lower end.  An approximate 16 n' with
+// |16 n' - t16| <= 2^-18 |t16| is too close to decide (the margin is formed in
+// the kernel; +inf makes it NaN, which never counts as close).  Built on the
+// host (see nf4_table.cpp).
 struct Nf4Buckets {
   float t16[34];
-  uint32_t mb[34];
+  uint32_t cnt[34];
   int ok;   // 1 when the construction's assumptions held
 };
 

@@ -17,15 +17,16 @@ constexpr int kThreads = 256;
 // The code of n = fl32(w / a) is #{k : n >= thr[k]}.  Instead of dividing and
 // comparing with all 15 thresholds, each weight takes n' = w * (16 / a) from
 // one reciprocal per block (within a few ulp of 16 n), finds its 1/16-wide
-// bucket in a 34-entry LDS table (one 8-byte read: the bucket's threshold, a
-// margin and the count of thresholds below the bucket), and compares once.
-// Weights whose n' lies within the margin of the bucket's threshold -- and
+// bucket in a 34-entry LDS table (one 8-byte read: the bucket's threshold t16
+// and the count of thresholds below the bucket), and compares once.  Weights
+// whose n' lies within the margin 2^-18 |t16| of the bucket's threshold -- and
 // all weights of blocks with a nonzero finite absmax outside [2^-123, 2^125),
 // where 16 / absmax would not be a finite normal number -- are redone with the
 // correctly rounded division, so the codes are exactly those of the definition.
 // The eight weights of a thread -> eight packed codes; `a` returns the block's
 // absmax (shared by the 8 lanes of an aligned group through DPP, so all eight
-// lanes of a block must be active together).  tab: the bucket table in LDS.
+// lanes of a block must be active together).  tab: the bucket table in LDS,
+// tab_base its LDS byte address.
 // floor(x) as int32 in one instruction (the compiler emits a floor and a
 // conversion); non-finite x gives an out-of-range index that the caller clamps.
 __device__ __forceinline__ int cvt_floor_i32(float x) {
@@ -48,24 +49,24 @@ __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t*
   const bool a_fast = (m >= 0x02000000u && m < 0x7E000000u) || m >= 0x7F800000u;
   const float y16 = a_fast ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
   uint32_t packed = 0;
-  // a weight is near its bucket's threshold when |n16 - t16| <= margin, i.e. when
-  // fl(|n16 - t16| - margin) <= 0 (exact: the difference of two floats is
-  // non-positive exactly when the first is not larger); the octet is redone when
-  // the smallest of the eight is.  A NaN difference never counts as near, as
-  // before, since the minimum passes over it.
+  // With d = n' - t16: n' >= t16 exactly when d >= 0 (the difference of two
+  // floats is non-negative exactly when the first is not smaller); a weight is
+  // near its threshold when |d| <= 2^-18 |t16|, i.e. when
+  // fl(|d| - 2^-18 |t16|) <= 0 (one fma; the product is exact).  The octet is
+  // redone when the smallest of the eight is; a NaN (bucket without threshold:
+  // |t16| = +inf) never counts as near, since the minimum passes over it.
   float emin = __builtin_inff();
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float n16 = w[j] * y16;
-    // bucket floor(n16) + 17 in [1, 33] for finite weights; the unsigned min keeps
-    // a non-finite input inside the table
-    const uint32_t bi = min((uint32_t)(cvt_floor_i32(n16) + 17), 33u);
-    const uint32_t addr = tab_base + 8u * bi;
+    // bucket floor(n16) + 17 in [0, 33]: the +17 is folded into the address
+    const int bi = min(max(cvt_floor_i32(n16), -17), 16);
+    const uint32_t addr = tab_base + 8u * 17u + 8u * (uint32_t)bi;
     const float t16 = __uint_as_float(*(const LDS_AS uint32_t*)(uintptr_t)addr);
-    const uint32_t mb = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
-    const uint32_t c = (mb & 15u) + (n16 >= t16 ? 1u : 0u);
-    emin = __builtin_fminf(emin, __builtin_fabsf(n16 - t16) - __uint_as_float(mb));
-    packed |= c << (4 * j);
+    const uint32_t cnt = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
+    const float d = n16 - t16;
+    emin = __builtin_fminf(emin, __builtin_fmaf(__builtin_fabsf(t16), -0x1p-18f, __builtin_fabsf(d)));
+    packed |= (cnt + (d >= 0.0f ? 1u : 0u)) << (4 * j);
   }
   const bool redo = (m != 0 && !a_fast) || emin <= 0.0f;
   if (redo) {
@@ -78,7 +79,7 @@ __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t*
       const float n16 = 16.0f * n;                            // exact
       const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);
       const float t16 = __uint_as_float(tab[2 * bi]);
-      const uint32_t c = (tab[2 * bi + 1] & 15u) + (n16 >= t16 ? 1u : 0u);
+      const uint32_t c = tab[2 * bi + 1] + (n16 >= t16 ? 1u : 0u);
       packed |= c << (4 * j);
     }
   }
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict_
   __shared__ __attribute__((aligned(8))) uint32_t tab[34 * 2];
   if (threadIdx.x < 34) {
     tab[2 * threadIdx.x] = __float_as_uint(bk.t16[threadIdx.x]);
-    tab[2 * threadIdx.x + 1] = bk.mb[threadIdx.x];
+    tab[2 * threadIdx.x + 1] = bk.cnt[threadIdx.x];
   }
   __syncthreads();
   const uint32_t tab_base = (uint32_t)(uintptr_t)(LDS_AS uint32_t*)tab;
@@ -143,23 +144,30 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict_
 
 // Encoder and double quantization in one pass: a work group owns whole groups
 // of 256 blocks (2048 octets, eight per thread, all requested up front); the
-// group's max is reduced across the work group and every block's scale code
-// follows at once.  Results equal those of k_nf4_encode then k_double_quant.
+// group's max is reduced across the work group, the blocks' absmax values are
+// parked in LDS, and each thread then forms one block's scale code.  Results
+// equal those of k_nf4_encode then k_double_quant.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restrict__ W, int64_t n_oct,
                                                             uint32_t* __restrict__ codes,
                                                             float* __restrict__ absmax, uint8_t* __restrict__ c2,
                                                             float* __restrict__ c1, int64_t ngroups,
                                                             Nf4Buckets bk) {
-  __shared__ __attribute__((aligned(8))) uint32_t tab[34 * 2];
-  __shared__ uint32_t red[kThreads / 64];
+  // one LDS array with the bucket table first, at LDS address 0 (its addresses
+  // are then 8 bi plus a constant offset), then the wave maxima and the group's
+  // block absmax values
+  __shared__ __attribute__((aligned(16))) uint32_t lds[34 * 2 + kThreads / 64 + qk::kGroup];
+  uint32_t* tab = lds;
+  uint32_t* red = lds + 34 * 2;
+  float* absm = (float*)(lds + 34 * 2 + kThreads / 64);
   if (threadIdx.x < 34) {
     tab[2 * threadIdx.x] = __float_as_uint(bk.t16[threadIdx.x]);
-    tab[2 * threadIdx.x + 1] = bk.mb[threadIdx.x];
+    tab[2 * threadIdx.x + 1] = bk.cnt[threadIdx.x];
   }
   __syncthreads();
   const uint32_t tab_base = (uint32_t)(uintptr_t)(LDS_AS uint32_t*)tab;
   const int t = threadIdx.x;
+  const int64_t nblocks = n_oct / 8;
   constexpr int kIt = qk::kGroup * 8 / kThreads;    // octets per thread per group (8)
   for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
     const int64_t o0 = g * qk::kGroup * 8 + t;
@@ -169,18 +177,18 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restri
       const int64_t o = o0 + (int64_t)it * kThreads;
       raw[it] = load_oct<kBf16>(W, o < n_oct ? o : 0);
     }
-    float a[kIt];
     uint32_t m = 0;
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int64_t o = o0 + (int64_t)it * kThreads;
-      a[it] = 0.0f;
+      float a = 0.0f;
       if (o < n_oct) {                                // whole blocks (8 lanes) are in or out together
         float w[8];
         unpack_oct<kBf16>(raw[it], w);
-        codes[o] = encode8(w, tab, tab_base, a[it]);
+        codes[o] = encode8(w, tab, tab_base, a);
       }
-      m = max(m, __float_as_uint(a[it]));
+      if ((t & 7) == 0) absm[(t >> 3) + 32 * it] = a; // block (o - 2048 g) / 8 of the group
+      m = max(m, __float_as_uint(a));
     }
     m = qk::wave_max_u32(m);
     if ((t & 63) == 0) red[t >> 6] = m;
@@ -188,20 +196,15 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restri
     uint32_t gm = red[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) gm = max(gm, red[i]);
-    __syncthreads();                                  // red is reused by the next group
     const float cmax = __uint_as_float(gm);
-    if ((t & 7) == 0) {
-#pragma unroll
-      for (int it = 0; it < kIt; ++it) {
-        const int64_t o = o0 + (int64_t)it * kThreads;
-        if (o < n_oct) {
-          const int64_t b = o >> 3;
-          c2[b] = (uint8_t)qk::e4m3fn_encode(gm == 0 ? 0.0f : a[it] / cmax);
-          if (absmax) absmax[b] = a[it];
-        }
-      }
+    const int64_t b = g * qk::kGroup + t;             // one block per thread
+    if (b < nblocks) {
+      const float a = absm[t];
+      c2[b] = (uint8_t)qk::e4m3fn_encode(gm == 0 ? 0.0f : a / cmax);
+      if (absmax) absmax[b] = a;
     }
     if (t == 0) c1[g] = cmax;
+    __syncthreads();                                  // red and absm are reused by the next group
   }
 }
 

@@ -86,10 +86,10 @@ Nf4Params build_int4() {
 
 // Bucket table of the encoder.  The approximate quotient n' it is used with
 // is within 2 ulp of the correctly rounded n = w / a (one reciprocal of at most
-// 1 ulp error and one rounded product); the margin is 2^-18 |t16| rounded up to
-// a power of two, far above that, and every threshold must lie farther than
-// the margin from its bucket's ends, so that a quotient placed in a
-// neighbouring bucket still gets the right count.
+// 1 ulp error and one rounded product), i.e. 16 n' within 2^-21 |16 n| of 16 n;
+// the kernel's margin 2^-18 |t16| is far above that near a threshold t16, and
+// every threshold must lie farther than four margins from its bucket's ends,
+// so that a quotient placed in a neighbouring bucket still gets the right count.
 Nf4Buckets build_buckets(const Nf4Params& p) {
   Nf4Buckets b;
   b.ok = 1;
@@ -103,17 +103,12 @@ Nf4Buckets build_buckets(const Nf4Params& p) {
       else if (t16 < hi) { ++inside; t = (float)t16; }
     }
     if (inside > 1) b.ok = 0;
-    float m = 1.0f / 65536.0f;                   // margin for buckets without a threshold
     if (inside == 1) {
-      int e;
-      std::frexp(std::fabs((double)t), &e);      // |t| < 2^e
-      m = std::ldexp(1.0f, e - 18);
+      const double m = std::ldexp(std::fabs((double)t), -18);
       if ((double)t - lo <= 4.0 * m || hi - (double)t <= 4.0 * m) b.ok = 0;
     }
-    uint32_t mbits;
-    std::memcpy(&mbits, &m, 4);
     b.t16[i] = t;
-    b.mb[i] = mbits | (uint32_t)base;            // margin's low mantissa bits are zero
+    b.cnt[i] = (uint32_t)base;
   }
   return b;
 }
