@@ -25,6 +25,7 @@ Also reported (not part of `value`):
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -113,17 +114,26 @@ GEMM_SOURCE = os.path.join(ROOT, "bit_quantized_lora_blockwise_amd", "csrc", "ge
 DECODE_SOURCE = os.path.join(ROOT, "bit_quantized_lora_blockwise_amd", "csrc", "decode.hip")
 
 
+def code_digest(path):
+    """sha256 of a source file with its comments and white space taken out: the
+    digest changes with the code, not with its comments or layout."""
+    import hashlib
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def recorded_traffic(kernel, source=GEMM_SOURCE):
     """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
-    summary, or None when the kernel's source file has changed since those
-    counters were taken (the summary records each source's sha256)."""
-    import hashlib
+    summary, or None when the kernel's source code has changed since those
+    counters were taken (the summary records each source's code digest)."""
     try:
         text = open(TRAFFIC_PROFILE).read()
-        sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
+        digest = code_digest(source)
     except OSError:
         return None
-    if f"{os.path.basename(source)} sha256 {sha}" not in text:
+    if f"{os.path.basename(source)} code sha256 {digest}" not in text:
         return None
     for line in text.splitlines():
         parts = line.split()

@@ -85,14 +85,18 @@ __device__ __forceinline__ bf16x8 frag_planes(const LDS_AS uint8_t* base, int k0
   const int l = threadIdx.x & 63;
   const int g = l >> 4, i = l & 15;
   const int row = 2 * (k0 + 8 * (g >> 1)) + (i >> 1);
-  // 8-byte chunk c of each 32-byte column group of weight row k is stored at
-  // chunk c ^ (k % 4) (k % 4 = (i / 4) % 4 here), which keeps the writes of the
-  // dequantisation free of bank conflicts
+  // 8-byte chunk c of each 32-byte column group G of weight row k is stored at
+  // chunk c ^ (k % 4) of group G ^ ((k / 4) % 2): with 64 four-byte banks and
+  // 32 lanes of 8-byte accesses served together, neither the dequantisation's
+  // writes nor these reads then put two addresses on one bank.  Here
+  // k % 4 = (i / 4) % 4; the first read covers rows with (k / 4) % 2 = 0 (k0 is
+  // a multiple of 16), the second, eight plane rows on, those with 1: it takes
+  // the other 32-byte group of the pair (col0 is a multiple of 32).
   const int chunk = (2 * (g & 1) + (i & 1)) ^ ((i >> 2) & 3);
-  const LDS_AS uint8_t* p = base + row * kPlane + col0 + 8 * chunk;
+  const LDS_AS uint8_t* p = base + row * kPlane + 8 * chunk;
   typedef int v2i __attribute__((ext_vector_type(2)));
-  const v2i a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)p);
-  const v2i b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 8 * kPlane));
+  const v2i a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + col0));
+  const v2i b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 8 * kPlane + (col0 ^ 32)));
   const u32x4 v = {(uint32_t)a[0], (uint32_t)a[1], (uint32_t)b[0], (uint32_t)b[1]};
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -341,10 +345,12 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
           if (kDx) {
             u32x2 lo8, hi8;
             dequant8_planes(L, c, kc, lo8, hi8);
-            // 8-byte chunk c of each 32-byte column group of weight row k at chunk c ^ (k % 4)
+            // 8-byte chunk c of 32-byte column group G of weight row k at chunk
+            // c ^ (k % 4) of group G ^ ((k / 4) % 2): rows k and k + 4 of a wave's
+            // writes then fall on different banks
             const int k = tp >> 2, j = tp & 3;
-            LDS_AS uint8_t* d =
-                (LDS_AS uint8_t*)buf + 2 * k * kPlane + 64 * j + 32 * (q8 >> 2) + 8 * ((q8 & 3) ^ (k & 3));
+            LDS_AS uint8_t* d = (LDS_AS uint8_t*)buf + 2 * k * kPlane + 32 * ((2 * j + (q8 >> 2)) ^ ((k >> 2) & 1)) +
+                                8 * ((q8 & 3) ^ (k & 3));
             *(LDS_AS u32x2*)d = lo8;
             *(LDS_AS u32x2*)(d + kPlane) = hi8;
           } else {
