@@ -29,6 +29,13 @@
 //    byte planes read with ds_read_b64_tr_b8, which interleaves the planes.
 //  * Work groups are dispatched round-robin over the 8 XCDs; the tile order is
 //    remapped so that each XCD (with its own L2) gets a contiguous run of tiles.
+//  * When the tiles outnumber the CUs, the grid is persistent (one work group
+//    per CU, tiles v, v + grid, ...).  Each tile starts with its LoRA term:
+//    the producers stage the LoRA operands in LDS, the consumers multiply them.
+//    The consumers issue no global loads and wait only for their LDS reads,
+//    and their output stores go through a buffer descriptor, so a tile's
+//    stores drain while the next tile's LoRA term and first steps run (the
+//    memory counter a wait would block on counts stores too).
 #include <type_traits>
 
 #include "dequant.h"
@@ -159,96 +166,24 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
   const int64_t kblocks = K / qk::kBlock;
   constexpr bool kPerm = kDx && !kB16;    // dX columns in the lookup order (0, 2, 4, 6, 1, 3, 5, 7)
 
-  // ---- tile of this work group: XCD x = (linear id) % 8 takes a contiguous
-  // run of tiles in row-major tile order.
-  int64_t m0, p0;
-  {
-    const int nwg = gridDim.x * gridDim.y;
-    const int b = blockIdx.x + gridDim.x * blockIdx.y;
-    const int per = nwg / 8, extra = nwg % 8, xcd = b % 8, q = b / 8;
+  // ---- tiles: virtual work group v of the ntiles (one per tile) sits on XCD
+  // v % 8, and XCD x takes a contiguous run of tiles in row-major tile order.
+  // The launch has ntiles work groups (one tile each) or a multiple of 8 that
+  // take tiles v, v + G, ... in turn (persistent).
+  const int tiles_x = (int)((P + kBP - 1) / kBP);
+  const int ntiles = tiles_x * (int)((M + kBM - 1) / kBM);
+  const int vfirst = blockIdx.x + gridDim.x * blockIdx.y;
+  const int vstride = gridDim.x * gridDim.y;
+  int m0 = 0, p0 = 0;   // wave-uniform
+  auto set_tile = [&](int v) {
+    const int per = ntiles / 8, extra = ntiles % 8, xcd = v % 8, q = v / 8;
     const int tile = xcd < extra ? xcd * (per + 1) + q : extra * (per + 1) + (xcd - extra) * per + q;
-    m0 = (int64_t)(tile / gridDim.x) * kBM;
-    p0 = (int64_t)(tile % gridDim.x) * kBP;
-  }
-
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  // ---- LoRA term first (consumers): fwd acc = s * (T L2); dX acc = G L1^T
-  //      (rank zero-padded to 64); the base product then accumulates onto it.
-  //      With nseg > 1 segments of seg output columns (fwd) or reduction
-  //      columns (dX), each segment g has its own T_g / G_g [M, r] (at LA + g M r)
-  //      and L2_g [r, seg] (at LB + g r seg) / L1_g [K, r] (at LB + g K r): the
-  //      forward tile uses its own segment's pair (tiles never straddle
-  //      segments), the dX tile sums the products of all segments.
-  {
-    LDS_AS uint16_t* la = (LDS_AS uint16_t*)lds_b;                 // [256][kPL]: T / G rows
-    LDS_AS uint16_t* lb = (LDS_AS uint16_t*)lds_b + kBM * kPL;     // fwd: L2 [64][kPD]; dX: L1 [256][kPL]
-    const int ng = kDx ? nseg : 1;
-    for (int g = 0; g < ng; ++g) {
-      const int64_t gs = kDx ? g : p0 / seg;
-      if (!producer) {
-        const uint16_t* la_src = LA + gs * M * r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
-          u32x4 v = {0, 0, 0, 0};
-          if (m0 + row < M) v = load_row8(la_src + (m0 + row) * r, cc, r);
-          *(LDS_AS u32x4*)(la + row * kPL + cc) = v;
-        }
-        if (!kDx) {
-          const uint16_t* lb_src = LB + gs * r * seg;
-          const int64_t pc = p0 - gs * seg;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = (t >> 5) + 16 * i, pp = (t & 31) * 8;
-            u32x4 v = {0, 0, 0, 0};
-            if (c < r) v = load_row8(lb_src + (int64_t)c * seg, pc + pp, seg);
-            *(LDS_AS u32x4*)(lb + c * kPD + pp) = v;
-          }
-        } else {
-          const uint16_t* lb_src = LB + gs * K * r;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = (t >> 3) + 64 * i, cc = (t & 7) * 8;
-            u32x4 v = {0, 0, 0, 0};
-            if (p0 + row < K) v = load_row8(lb_src + (p0 + row) * r, cc, r);
-            *(LDS_AS u32x4*)(lb + row * kPL + cc) = v;
-          }
-        }
-      }
-      __syncthreads();
-      if (!producer) {
-        const int ksteps = (r + 15) / 16;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            f32x16 z = acc[i][j];
-            for (int s = 0; s < ksteps; ++s) {
-              const bf16x8 a = qk::frag_rowmajor(la, kPL, 64 * rg + 32 * i, 16 * s);
-              // dX: the column of accumulator slot (l % 32) is dx_slot_col(l % 32)
-              const bf16x8 b =
-                  kDx ? *(const LDS_AS bf16x8*)(lb + (128 * ch + 32 * j + (kPerm ? dx_slot_col(l & 31) : (l & 31))) *
-                                                         kPL + 16 * s + 8 * (l >> 5))
-                      : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
-              z = qk::mfma32(a, b, z);
-            }
-            acc[i][j] = z;
-          }
-      }
-      __syncthreads();
-    }
-    if (!kDx && !producer) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = scale * acc[i][j];
-    }
-  }
+    m0 = __builtin_amdgcn_readfirstlane((tile / tiles_x) * kBM);
+    p0 = __builtin_amdgcn_readfirstlane((tile % tiles_x) * kBP);
+  };
+  const int ng = kDx ? nseg : 1;
+  LDS_AS uint16_t* la = (LDS_AS uint16_t*)lds_b;                 // [256][kPL]: T / G rows
+  LDS_AS uint16_t* lb = (LDS_AS uint16_t*)lds_b + kBM * kPL;     // fwd: L2 [64][kPD]; dX: L1 [256][kPL]
 
   LDS_AS uint16_t* b0 = (LDS_AS uint16_t*)lds_b;
   LDS_AS uint16_t* b1 = (LDS_AS uint16_t*)lds_b + kBufElems;
@@ -390,10 +325,100 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
       if constexpr (kB16 && !kDx) dma_tile(Wb, N, p0, st, bbuf);
       if constexpr (kB16 && kDx) dma_wdx(st, bbuf);
     };
-    Stage hA, hB;
+    // LoRA operands of the tile into the B buffers (free: the consumers passed
+    // the barrier after their last fragment reads of the previous tile), one
+    // segment at a time; the consumers multiply them between the two barriers
+    // that follow.  With 16-byte-aligned rows (r % 8 == 0, and in the forward
+    // seg % 8 == 0) each thread moves its sixteen 16-byte chunks by buffer
+    // loads, chunks past the matrices reading as zeros, all issued before the
+    // first is written to LDS.
+    const bool lora_vec = (r % 8) == 0 && (kDx || (seg % 8) == 0) && M * r * 2 < (int64_t(1) << 31) &&
+                          (kDx ? K * r * 2 : r * seg * 2) < (int64_t(1) << 31);
+    for (int v = vfirst; v < ntiles; v += vstride) {
+    set_tile(v);
+    Stage hA, hB, h0;
+    for (int g = 0; g < ng; ++g) {
+      const int64_t gs = kDx ? g : p0 / seg;
+      const uint16_t* la_src = LA + gs * M * r;
+      if (lora_vec) {
+        u32x4 va[8], vb[8];
+        const __amdgpu_buffer_rsrc_t rla = rsrc(la_src, (uint64_t)M * r * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = tp + 256 * i, row = idx >> 3, cc = (idx & 7) * 8;
+          const bool ok = m0 + row < M && cc < r;
+          va[i] = __builtin_amdgcn_raw_buffer_load_b128(rla, ok ? (uint32_t)(((m0 + row) * r + cc) * 2) : kOOB, 0, 0);
+        }
+        if constexpr (!kDx) {
+          const uint16_t* lb_src = LB + gs * r * seg;
+          const int pc = p0 - (int)(gs * seg);
+          const __amdgpu_buffer_rsrc_t rlb = rsrc(lb_src, (uint64_t)r * seg * 2);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int idx = tp + 256 * i, c = idx >> 5, pp = (idx & 31) * 8;
+            const bool ok = c < r && pc + pp < seg;
+            vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rlb, ok ? (uint32_t)(((int64_t)c * seg + pc + pp) * 2) : kOOB,
+                                                          0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int idx = tp + 256 * i;
+            *(LDS_AS u32x4*)(la + (idx >> 3) * kPL + (idx & 7) * 8) = va[i];
+            *(LDS_AS u32x4*)(lb + (idx >> 5) * kPD + (idx & 31) * 8) = vb[i];
+          }
+        } else {
+          const uint16_t* lb_src = LB + gs * K * r;
+          const __amdgpu_buffer_rsrc_t rlb = rsrc(lb_src, (uint64_t)K * r * 2);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int idx = tp + 256 * i, row = idx >> 3, cc = (idx & 7) * 8;
+            const bool ok = p0 + row < K && cc < r;
+            vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rlb, ok ? (uint32_t)(((int64_t)(p0 + row) * r + cc) * 2) : kOOB,
+                                                          0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int idx = tp + 256 * i;
+            *(LDS_AS u32x4*)(la + (idx >> 3) * kPL + (idx & 7) * 8) = va[i];
+            *(LDS_AS u32x4*)(lb + (idx >> 3) * kPL + (idx & 7) * 8) = vb[i];
+          }
+        }
+      } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = tp + 256 * i, row = idx >> 3, cc = (idx & 7) * 8;
+        u32x4 v8 = {0, 0, 0, 0};
+        if (m0 + row < M) v8 = load_row8(la_src + (m0 + row) * r, cc, r);
+        *(LDS_AS u32x4*)(la + row * kPL + cc) = v8;
+      }
+      if constexpr (!kDx) {
+        const uint16_t* lb_src = LB + gs * r * seg;
+        const int64_t pc = p0 - gs * seg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = tp + 256 * i, c = idx >> 5, pp = (idx & 31) * 8;
+          u32x4 v8 = {0, 0, 0, 0};
+          if (c < r) v8 = load_row8(lb_src + (int64_t)c * seg, pc + pp, seg);
+          *(LDS_AS u32x4*)(lb + c * kPD + pp) = v8;
+        }
+      } else {
+        const uint16_t* lb_src = LB + gs * K * r;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = tp + 256 * i, row = idx >> 3, cc = (idx & 7) * 8;
+          u32x4 v8 = {0, 0, 0, 0};
+          if (p0 + row < K) v8 = load_row8(lb_src + (p0 + row) * r, cc, r);
+          *(LDS_AS u32x4*)(lb + row * kPL + cc) = v8;
+        }
+      }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): this wave's loads and LDS writes
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();         // the consumers have read them
+    }
     {
       send(0, a0, b0);
-      const Stage h0 = load_stage(0);
+      h0 = load_stage(0);
       hA = load_stage(1);
       store_stage(h0, b0);
       __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), seen by the compiler's wait tracking
@@ -424,10 +449,15 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
       __builtin_amdgcn_s_waitcnt(0x0070);
       __builtin_amdgcn_s_barrier();
     }
+    }   // tiles
     return;
   }
 
   // ================================ consumers ================================
+  // They issue no loads: between barriers they only read LDS and store their
+  // outputs, and they wait only for their LDS reads, so one tile's output
+  // stores drain while the next tile's LoRA term and first steps run.
+  f32x16 acc[2][4];
   // A fragment of sub-step s, tile i: row 64 (c % 4) + 32 i + l % 32, chunk 2 s + l / 32.
   uint32_t afrag_off[4];
 #pragma unroll
@@ -470,6 +500,46 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
       }
     }
   };
+  for (int v = vfirst; v < ntiles; v += vstride) {
+  set_tile(v);
+  // ---- LoRA term first: fwd acc = s * (T L2); dX acc = G L1^T (rank
+  //      zero-padded to 64); the base product then accumulates onto it.  With
+  //      nseg > 1 segments (stacked linears) the forward tile uses its own
+  //      segment's pair (tiles never straddle segments), the dX tile sums the
+  //      products of all segments.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  for (int g = 0; g < ng; ++g) {
+    __builtin_amdgcn_s_barrier();          // the producers' LoRA operands are in LDS
+    const int ksteps = (r + 15) / 16;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < ksteps) {
+        const bf16x8 a0f = qk::frag_rowmajor(la, kPL, 64 * rg, 16 * s);
+        const bf16x8 a1f = qk::frag_rowmajor(la, kPL, 64 * rg + 32, 16 * s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // dX: the column of accumulator slot (l % 32) is dx_slot_col(l % 32)
+          const bf16x8 b =
+              kDx ? *(const LDS_AS bf16x8*)(lb + (128 * ch + 32 * j + (kPerm ? dx_slot_col(l & 31) : (l & 31))) *
+                                                     kPL + 16 * s + 8 * (l >> 5))
+                  : qk::frag_kmajor(lb, kPD, 16 * s, 128 * ch + 32 * j);
+          acc[0][j] = qk::mfma32(a0f, b, acc[0][j]);
+          acc[1][j] = qk::mfma32(a1f, b, acc[1][j]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0): this wave's reads of the LoRA operands are done
+    __builtin_amdgcn_s_barrier();
+  }
+  if constexpr (!kDx) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = scale * acc[i][j];
+  }
   __builtin_amdgcn_s_barrier();            // first tiles in LDS
   for (int64_t st = 0; st < nsteps; st += 2) {
     compute(a0, b0);
@@ -480,18 +550,33 @@ __global__ __launch_bounds__(kT, 1) void k_qgemm_big(const uint16_t* __restrict_
     __builtin_amdgcn_s_barrier();
   }
 
-  // ---- store C (bf16), lane layout of the 32x32 accumulators
+  // ---- store C (bf16), lane layout of the 32x32 accumulators, through a
+  // buffer descriptor based at this wave's first output element whose size
+  // ends with the last row of C (rows past M are dropped by the hardware);
+  // lane offsets are 32-bit (M P < 2^30), the (i, j) part a scalar offset.
+  {
+    const int Pi = (int)P;
+    const int rows_left = (int)M - (m0 + 64 * rg);
+    const int cbase = p0 + 128 * ch;
+    const uint32_t nbytes = rows_left > 0 ? (uint32_t)(rows_left * Pi - cbase) * 2u : 0u;
+    const __amdgpu_buffer_rsrc_t rc_out = rsrc(C + (int64_t)(m0 + 64 * rg) * P + cbase, nbytes);
+    const int col = kPerm ? dx_slot_col(l & 31) : (l & 31);
+    const int prem = Pi - (cbase + col);           // columns of this lane still inside C
+    const uint32_t lane_b = (uint32_t)((4 * (l >> 5)) * Pi + col) * 2u;   // acc_row(e) = 8 (e / 4) + 4 (l / 32) + e % 4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t pc = p0 + 128 * ch + 32 * j + (kPerm ? dx_slot_col(qk::acc_col()) : qk::acc_col());
+      for (int j = 0; j < 4; ++j) {
+        if (32 * j < prem) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + 64 * rg + 32 * i + qk::acc_row(e);
-        if (m < M && pc < P) C[m * P + pc] = qk::f32_to_bf16(acc[i][j][e]);
+          for (int e = 0; e < 16; ++e) {
+            const int so = ((32 * i + 8 * (e >> 2) + (e & 3)) * Pi + 32 * j) * 2;
+            __builtin_amdgcn_raw_buffer_store_b16(qk::f32_to_bf16(acc[i][j][e]), rc_out, lane_b, so, 0);
+          }
+        }
       }
-    }
+  }
+  }   // tiles
 }
 
 }  // namespace
@@ -502,12 +587,30 @@ bool qgemm_big_ok(bool dx, int64_t M, int64_t K, int64_t N) {
   return (R % 8) == 0 && M * R * 2 < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31) && M > 16;
 }
 
+// Launch grid: one work group per tile, or, when the tiles outnumber the CUs,
+// a persistent grid of the CU count rounded down to a multiple of 8 (each
+// work group then takes tiles v, v + grid, ... on one XCD), so that a work
+// group's output stores drain while its next tile starts.
+static dim3 tile_grid(int64_t M, int64_t P) {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess || n < 8)
+      n = 256;
+    return n;
+  }();
+  const int64_t tx = (P + kBP - 1) / kBP, ty = (M + kBM - 1) / kBM;
+  const int64_t pers = cus / 8 * 8;
+  if (tx * ty > pers) return dim3((unsigned)pers, 1);
+  return dim3((unsigned)tx, (unsigned)ty);
+}
+
 hipError_t launch_qgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                             const uint8_t* c2, const float* c1, const uint16_t* LA, const uint16_t* LB, int r,
                             float scale, uint16_t* C, hipStream_t s, int nseg) {
   const int64_t P = dx ? K : N;
   const int64_t seg = N / nseg;   // columns of W per segment (a multiple of 256 when nseg > 1)
-  dim3 grid((unsigned)((P + kBP - 1) / kBP), (unsigned)((M + kBM - 1) / kBM));
+  const dim3 grid = tile_grid(M, P);
   const uint16_t* nw = nullptr;
   if (!dx)
     hipLaunchKernelGGL((k_qgemm_big<false, false>), grid, dim3(kT), 0, s, A, M, K, N, codes, c2, c1, LA, LB, r,
@@ -532,7 +635,7 @@ bool bgemm_ok(bool dx, int64_t M, int64_t K, int64_t N) {
 hipError_t launch_bgemm_big(bool dx, const uint16_t* A, int64_t M, int64_t K, int64_t N, const uint16_t* W,
                             const uint16_t* LA, const uint16_t* LB, int r, float scale, uint16_t* C, hipStream_t s) {
   const int64_t P = dx ? K : N;
-  dim3 grid((unsigned)((P + kBP - 1) / kBP), (unsigned)((M + kBM - 1) / kBM));
+  const dim3 grid = tile_grid(M, P);
   const uint8_t* nc = nullptr;
   const float* nf = nullptr;
   if (!dx)
