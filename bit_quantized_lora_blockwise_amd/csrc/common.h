@@ -30,14 +30,19 @@ struct Nf4Params {
 // n in [-1, 1]); each bucket holds at most one threshold.  For bucket i:
 // t16[i] = 16 * (its threshold), or +inf when it has none; cnt[i] = the number
 // of thresholds at or below the bucket's lower end.  An approximate 16 n' with
-// |16 n' - t16| <= 2^-18 |t16| is too close to decide (the margin is formed in
-// the kernel; +inf makes it NaN, which never counts as close).  Built on the
-// host (see nf4_table.cpp).
+// |16 n' - t16| <= kNf4Near is too close to decide (+inf is never close).
+// Built on the host (see nf4_table.cpp).
 struct Nf4Buckets {
   float t16[34];
   uint32_t cnt[34];
   int ok;   // 1 when the construction's assumptions held
 };
+
+// The encoder's approximate quotient n' = w * (16 / a) (one reciprocal of at
+// most 1 ulp and one rounded product) is within 2^-22 |16 n| of 16 n, n = fl(w / a),
+// i.e. within 2^-18.2 of it wherever |16 n| <= 13.8 (the largest |t16|).  The
+// margin below is 2.3 times that.
+static constexpr float kNf4Near = 0x1p-17f;
 
 namespace qk {
 

@@ -19,7 +19,7 @@ constexpr int kThreads = 256;
 // one reciprocal per block (within a few ulp of 16 n), finds its 1/16-wide
 // bucket in a 34-entry LDS table (one 8-byte read: the bucket's threshold t16
 // and the count of thresholds below the bucket), and compares once.  Weights
-// whose n' lies within the margin 2^-18 |t16| of the bucket's threshold -- and
+// whose 16 n' lies within kNf4Near of the bucket's threshold -- and
 // all weights of blocks with a nonzero finite absmax outside [2^-123, 2^125),
 // where 16 / absmax would not be a finite normal number -- are redone with the
 // correctly rounded division, so the codes are exactly those of the definition.
@@ -49,12 +49,11 @@ __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t*
   const bool a_fast = (m >= 0x02000000u && m < 0x7E000000u) || m >= 0x7F800000u;
   const float y16 = a_fast ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
   uint32_t packed = 0;
-  // With d = n' - t16: n' >= t16 exactly when d >= 0 (the difference of two
-  // floats is non-negative exactly when the first is not smaller); a weight is
-  // near its threshold when |d| <= 2^-18 |t16|, i.e. when
-  // fl(|d| - 2^-18 |t16|) <= 0 (one fma; the product is exact).  The octet is
-  // redone when the smallest of the eight is; a NaN (bucket without threshold:
-  // |t16| = +inf) never counts as near, since the minimum passes over it.
+  // With d = 16 n' - t16: 16 n' >= t16 exactly when d >= 0 (the difference of
+  // two floats is non-negative exactly when the first is not smaller); the
+  // octet is redone when the smallest |d| of its eight weights is at most
+  // kNf4Near (a bucket without threshold gives |d| = +inf, never near; a NaN d
+  // from a NaN weight is passed over by the minimum).
   float emin = __builtin_inff();
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -65,10 +64,10 @@ __device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t*
     const float t16 = __uint_as_float(*(const LDS_AS uint32_t*)(uintptr_t)addr);
     const uint32_t cnt = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
     const float d = n16 - t16;
-    emin = __builtin_fminf(emin, __builtin_fmaf(__builtin_fabsf(t16), -0x1p-18f, __builtin_fabsf(d)));
+    emin = __builtin_fminf(emin, __builtin_fabsf(d));
     packed |= (cnt + (d >= 0.0f ? 1u : 0u)) << (4 * j);
   }
-  const bool redo = (m != 0 && !a_fast) || emin <= 0.0f;
+  const bool redo = (m != 0 && !a_fast) || emin <= kNf4Near;
   if (redo) {
     // correctly rounded quotients for the whole octet (the same codes wherever
     // the approximate one was decided)
@@ -181,12 +180,14 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restri
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int64_t o = o0 + (int64_t)it * kThreads;
-      float a = 0.0f;
-      if (o < n_oct) {                                // whole blocks (8 lanes) are in or out together
-        float w[8];
-        unpack_oct<kBf16>(raw[it], w);
-        codes[o] = encode8(w, tab, tab_base, a);
-      }
+      // every octet is encoded (past the end: octet 0 again, results dropped),
+      // so that no load is moved into a branch and waited for there
+      float w[8], a;
+      unpack_oct<kBf16>(raw[it], w);
+      const uint32_t packed = encode8(w, tab, tab_base, a);
+      const bool in = o < n_oct;                      // whole blocks (8 lanes) are in or out together
+      if (in) codes[o] = packed;
+      a = in ? a : 0.0f;
       if ((t & 7) == 0) absm[(t >> 3) + 32 * it] = a; // block (o - 2048 g) / 8 of the group
       m = max(m, __float_as_uint(a));
     }

@@ -84,12 +84,11 @@ Nf4Params build_int4() {
   return from_levels(q);
 }
 
-// Bucket table of the encoder.  The approximate quotient n' it is used with
-// is within 2 ulp of the correctly rounded n = w / a (one reciprocal of at most
-// 1 ulp error and one rounded product), i.e. 16 n' within 2^-21 |16 n| of 16 n;
-// the kernel's margin 2^-18 |t16| is far above that near a threshold t16, and
-// every threshold must lie farther than four margins from its bucket's ends,
-// so that a quotient placed in a neighbouring bucket still gets the right count.
+// Bucket table of the encoder.  Its approximate 16 n' is within 2^-22 |16 n|
+// of 16 n (common.h); the table is accepted when that error stays below half
+// the margin kNf4Near at every threshold (|t16| <= 16) and every threshold lies
+// farther than four margins from its bucket's ends, so that a quotient placed
+// in a neighbouring bucket still gets the right count.
 Nf4Buckets build_buckets(const Nf4Params& p) {
   Nf4Buckets b;
   b.ok = 1;
@@ -104,7 +103,8 @@ Nf4Buckets build_buckets(const Nf4Params& p) {
     }
     if (inside > 1) b.ok = 0;
     if (inside == 1) {
-      const double m = std::ldexp(std::fabs((double)t), -18);
+      const double m = (double)kNf4Near;
+      if (2.0 * std::ldexp(std::fabs((double)t), -22) > m) b.ok = 0;
       if ((double)t - lo <= 4.0 * m || hi - (double)t <= 4.0 * m) b.ok = 0;
     }
     b.t16[i] = t;
