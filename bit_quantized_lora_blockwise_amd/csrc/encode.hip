@@ -10,80 +10,16 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One thread encodes 8 consecutive weights; the 8 lanes of an aligned group
-// cover one block of 64 and share its absmax through DPP.  Codes of the 8
-// weights form one 32-bit word (element j in bits 4j..4j+3).
-//
-// The code of n = fl32(w / a) is #{k : n >= thr[k]}.  Instead of dividing and
-// comparing with all 15 thresholds, each weight takes n' = w * (16 / a) from
-// one reciprocal per block (within a few ulp of 16 n), finds its 1/16-wide
-// bucket in a 34-entry LDS table (one 8-byte read: the bucket's threshold t16
-// and the count of thresholds below the bucket), and compares once.  Weights
-// whose 16 n' lies within kNf4Near of the bucket's threshold -- and
-// all weights of blocks with a nonzero finite absmax outside [2^-123, 2^125),
-// where 16 / absmax would not be a finite normal number -- are redone with the
-// correctly rounded division, so the codes are exactly those of the definition.
-// The eight weights of a thread -> eight packed codes; `a` returns the block's
-// absmax (shared by the 8 lanes of an aligned group through DPP, so all eight
-// lanes of a block must be active together).  tab: the bucket table in LDS,
-// tab_base its LDS byte address.
-// floor(x) as int32 in one instruction (the compiler emits a floor and a
-// conversion); non-finite x gives an out-of-range index that the caller clamps.
-__device__ __forceinline__ int cvt_floor_i32(float x) {
+// 8 * floor(x) as int32 for the bucket address: one conversion (which
+// saturates NaN and +-inf to INT_MAX / INT_MIN) and one 24-bit signed multiply
+// (which reads the low 24 bits of its input).  Every finite x of the encoder has
+// |x| <= 16 (1 + 2^-22), so floor(x) is in [-17, 16] and the result 8 floor(x)
+// exactly; INT_MAX and INT_MIN give -8 and 0, still inside the table, so no
+// clamp is needed.
+__device__ __forceinline__ int bucket_offset(float x) {
   int r;
-  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  asm("v_cvt_flr_i32_f32 %0, %1\n\tv_mul_i32_i24 %0, 8, %0" : "=v"(r) : "v"(x));
   return r;
-}
-
-__device__ __forceinline__ uint32_t encode8(const float (&w)[8], const uint32_t* tab, uint32_t tab_base,
-                                            float& a_out) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(w[j]) & 0x7FFFFFFFu);
-  m = qk::dpp_max8(m);
-  const float a = __uint_as_float(m);
-  // 16 / a when it is a finite normal number, i.e. a in [2^-123, 2^125) (and, as
-  // for any other input, for an infinite or NaN absmax); every other nonzero
-  // absmax -- subnormal, or at either end of the normal range -- takes the exact
-  // division below.  An all-zero block gives n' = 0 (codes 7).
-  const bool a_fast = (m >= 0x02000000u && m < 0x7E000000u) || m >= 0x7F800000u;
-  const float y16 = a_fast ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
-  uint32_t packed = 0;
-  // With d = 16 n' - t16: 16 n' >= t16 exactly when d >= 0 (the difference of
-  // two floats is non-negative exactly when the first is not smaller); the
-  // octet is redone when the smallest |d| of its eight weights is at most
-  // kNf4Near (a bucket without threshold gives |d| = +inf, never near; a NaN d
-  // from a NaN weight is passed over by the minimum).
-  float emin = __builtin_inff();
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float n16 = w[j] * y16;
-    // bucket floor(n16) + 17 in [0, 33]: the +17 is folded into the address
-    const int bi = min(max(cvt_floor_i32(n16), -17), 16);
-    const uint32_t addr = tab_base + 8u * 17u + 8u * (uint32_t)bi;
-    const float t16 = __uint_as_float(*(const LDS_AS uint32_t*)(uintptr_t)addr);
-    const uint32_t cnt = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
-    const float d = n16 - t16;
-    emin = __builtin_fminf(emin, __builtin_fabsf(d));
-    packed |= (cnt + (d >= 0.0f ? 1u : 0u)) << (4 * j);
-  }
-  const bool redo = (m != 0 && !a_fast) || emin <= kNf4Near;
-  if (redo) {
-    // correctly rounded quotients for the whole octet (the same codes wherever
-    // the approximate one was decided)
-    packed = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float n = (m == 0) ? 0.0f : w[j] / a;
-      const float n16 = 16.0f * n;                            // exact
-      const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);
-      const float t16 = __uint_as_float(tab[2 * bi]);
-      const uint32_t c = tab[2 * bi + 1] + (n16 >= t16 ? 1u : 0u);
-      packed |= c << (4 * j);
-    }
-  }
-  a_out = a;
-  return packed;
 }
 
 struct RawOct {
@@ -120,6 +56,93 @@ __device__ __forceinline__ void unpack_oct(const RawOct& r, float (&w)[8]) {
   }
 }
 
+// The largest |w| of the octet as fp32 bits (NaN above +inf).  For bf16 the
+// 16-bit magnitudes of each word's two weights are compared in pairs (one
+// packed max per word) and the larger half is moved to the top.
+template <bool kBf16>
+__device__ __forceinline__ uint32_t oct_absmax_bits(const RawOct& r) {
+  if (kBf16) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 h = __builtin_bit_cast(u16x2, r.v0[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int j = 1; j < 4; ++j) h = __builtin_elementwise_max(h, __builtin_bit_cast(u16x2, r.v0[j] & 0x7FFF7FFFu));
+    return (uint32_t)max(h.x, h.y) << 16;
+  } else {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(r.v0[j] & 0x7FFFFFFFu, r.v1[j] & 0x7FFFFFFFu));
+    return m;
+  }
+}
+
+// One thread encodes 8 consecutive weights; the 8 lanes of an aligned group
+// cover one block of 64 and share its absmax through DPP.  Codes of the 8
+// weights form one 32-bit word (element j in bits 4j..4j+3).
+//
+// The code of n = fl32(w / a) is #{k : n >= thr[k]}.  Instead of dividing and
+// comparing with all 15 thresholds, each weight takes n' = w * (16 / a) from
+// one reciprocal per block (within a few ulp of 16 n), finds its 1/16-wide
+// bucket in a 34-entry LDS table (one 8-byte read: the bucket's threshold t16
+// and the count of thresholds below the bucket), and compares once.  Weights
+// whose 16 n' lies within kNf4Near of the bucket's threshold -- and
+// all weights of blocks with a nonzero finite absmax outside [2^-123, 2^125),
+// where 16 / absmax would not be a finite normal number -- are redone with the
+// correctly rounded division, so the codes are exactly those of the definition.
+// The eight weights of a thread -> eight packed codes; `a` returns the block's
+// absmax (shared by the 8 lanes of an aligned group through DPP, so all eight
+// lanes of a block must be active together).  tab: the bucket table in LDS,
+// tab_base its LDS byte address.
+template <bool kBf16>
+__device__ __forceinline__ uint32_t encode8(const RawOct& r, const uint32_t* tab, uint32_t tab_base,
+                                            float& a_out) {
+  float w[8];
+  unpack_oct<kBf16>(r, w);
+  const uint32_t m = qk::dpp_max8(oct_absmax_bits<kBf16>(r));
+  const float a = __uint_as_float(m);
+  // 16 / a when it is a finite normal number, i.e. a in [2^-123, 2^125) (and, as
+  // for any other input, for an infinite or NaN absmax); every other nonzero
+  // absmax -- subnormal, or at either end of the normal range -- takes the exact
+  // division below.  An all-zero block gives n' = 0 (codes 7).
+  const bool a_fast = (m >= 0x02000000u && m < 0x7E000000u) || m >= 0x7F800000u;
+  const float y16 = a_fast ? 16.0f * __builtin_amdgcn_rcpf(a) : 0.0f;
+  // With d = 16 n' - t16: 16 n' >= t16 exactly when d >= 0 (the difference of
+  // two floats is non-negative exactly when the first is not smaller); the
+  // octet is redone when the smallest |d| of its eight weights is at most
+  // kNf4Near (a bucket without threshold gives |d| = +inf, never near; a NaN d
+  // from a NaN weight is passed over by the minimum).  The codes are gathered
+  // from the last weight down, four bits at a time.
+  float emin = __builtin_inff();
+  uint32_t packed = 0;
+#pragma unroll
+  for (int j = 7; j >= 0; --j) {
+    const float n16 = w[j] * y16;
+    // bucket floor(n16) + 17 in [0, 33]: the +17 is folded into the address
+    const uint32_t addr = tab_base + 8u * 17u + (uint32_t)bucket_offset(n16);
+    const float t16 = __uint_as_float(*(const LDS_AS uint32_t*)(uintptr_t)addr);
+    const uint32_t cnt = *(const LDS_AS uint32_t*)(uintptr_t)(addr + 4);
+    const float d = n16 - t16;
+    emin = __builtin_fminf(emin, __builtin_fabsf(d));
+    packed = (packed << 4) + cnt + (d >= 0.0f ? 1u : 0u);
+  }
+  const bool redo = (m != 0 && !a_fast) || emin <= kNf4Near;
+  if (redo) {
+    // correctly rounded quotients for the whole octet (the same codes wherever
+    // the approximate one was decided)
+    packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float n = (m == 0) ? 0.0f : w[j] / a;
+      const float n16 = 16.0f * n;                            // exact
+      const int bi = min(max((int)__builtin_floorf(n16) + 17, 0), 33);
+      const float t16 = __uint_as_float(tab[2 * bi]);
+      const uint32_t c = tab[2 * bi + 1] + (n16 >= t16 ? 1u : 0u);
+      packed |= c << (4 * j);
+    }
+  }
+  a_out = a;
+  return packed;
+}
+
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict__ W, int64_t n_oct,
                                                          uint32_t* __restrict__ codes,
@@ -133,10 +156,8 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict_
   const uint32_t tab_base = (uint32_t)(uintptr_t)(LDS_AS uint32_t*)tab;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t o = (int64_t)blockIdx.x * kThreads + threadIdx.x; o < n_oct; o += stride) {
-    float w[8];
-    unpack_oct<kBf16>(load_oct<kBf16>(W, o), w);
     float a;
-    codes[o] = encode8(w, tab, tab_base, a);
+    codes[o] = encode8<kBf16>(load_oct<kBf16>(W, o), tab, tab_base, a);
     if ((threadIdx.x & 7) == 0) absmax[o >> 3] = a;
   }
 }
@@ -182,9 +203,8 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restri
       const int64_t o = o0 + (int64_t)it * kThreads;
       // every octet is encoded (past the end: octet 0 again, results dropped),
       // so that no load is moved into a branch and waited for there
-      float w[8], a;
-      unpack_oct<kBf16>(raw[it], w);
-      const uint32_t packed = encode8(w, tab, tab_base, a);
+      float a;
+      const uint32_t packed = encode8<kBf16>(raw[it], tab, tab_base, a);
       const bool in = o < n_oct;                      // whole blocks (8 lanes) are in or out together
       if (in) codes[o] = packed;
       a = in ? a : 0.0f;

@@ -366,3 +366,48 @@ def test_fused_encoder_edge_cases(dtype):
     assert_bitexact(codes.cpu().numpy(), rc, f"fused edge codes {dtype}")
     assert_bitexact(c2.cpu().numpy(), rc2, f"fused edge c2 {dtype}")
     assert_bitexact(c1.cpu().numpy().view(np.uint32), rc1.view(np.uint32), f"fused edge c1 {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_encoders_with_non_finite_weights(dtype):
+    """Non-finite weights leave their own block's codes and their group's scales
+    unspecified, but both encoders still complete, and every block without one
+    (and every group of 256 blocks without one) keeps the oracle's codes,
+    absmax, c2 and c1 bit for bit.  The NaN and infinite quotients reach the
+    bucket lookup, whose address stays inside the table for them."""
+    import bit_quantized_lora_blockwise_amd as q
+    rows, cols = 64, 4096                                           # 4096 blocks, 16 groups
+    W = WL.normal((rows, cols), 0.02, 77, torch.float32)
+    flat = W.view(-1)
+    bad_blocks = {}
+    nan_neg = float(np.array([0xFFC00000], np.uint32).view(np.float32)[0])
+    for blk, vals in ((3 * 256 + 5, [float("nan")]), (3 * 256 + 6, [float("inf")]),
+                      (9 * 256 + 0, [float("-inf"), float("inf")]), (9 * 256 + 255, [nan_neg]),
+                      (12 * 256 + 17, [float("nan")] * 64)):
+        for i, v in enumerate(vals):
+            flat[blk * 64 + (i * 13) % 64] = v
+        bad_blocks[blk] = True
+    if dtype == "bf16":
+        W = W.to(torch.bfloat16)
+    Wd = W.to(DEV)
+    print(f"[encoder non-finite] {rows}x{cols} {dtype}", flush=True)
+    codes, c2, c1, absmax = q.nf4_quantize_dq(Wd, absmax=True)
+    codes_s, absmax_s = q.nf4_quantize(Wd)
+    c2_s, c1_s = q.nf4_double_quant(absmax_s)
+    torch.cuda.synchronize()
+    Wf = W.float().numpy().copy().reshape(-1, 64)
+    Wf[list(bad_blocks)] = 0.0                                     # the oracle sees finite blocks only
+    rc, ra = O.nf4_quantize(Wf.reshape(rows, cols))
+    rc2, rc1 = O.nf4_double_quant(ra)
+    good = np.ones(rows * cols // 64, bool)
+    good[list(bad_blocks)] = False
+    good_groups = np.ones(16, bool)
+    good_groups[[b // 256 for b in bad_blocks]] = False
+    in_good_group = np.repeat(good_groups, 256)
+    for tag, cd, am, s2, s1 in (("fused", codes, absmax, c2, c1), ("two calls", codes_s, absmax_s, c2_s, c1_s)):
+        g_codes = cd.cpu().numpy().reshape(-1, 32)
+        assert_bitexact(g_codes[good], rc.reshape(-1, 32)[good], f"{tag} codes of finite blocks")
+        assert_bitexact(am.cpu().numpy().view(np.uint32)[good], ra.view(np.uint32)[good], f"{tag} absmax")
+        assert_bitexact(s2.cpu().numpy()[in_good_group], rc2[in_good_group], f"{tag} c2 of finite groups")
+        assert_bitexact(s1.cpu().numpy().view(np.uint32)[good_groups], rc1.view(np.uint32)[good_groups],
+                        f"{tag} c1 of finite groups")
