@@ -9,6 +9,11 @@
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kNT = 2;   // cache policy of the weight loads: nontemporal (each weight is read once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
 
 // 8 * floor(x) as int32 for the bucket address: one conversion (which
 // saturates NaN and +-inf to INT_MAX / INT_MIN) and one 24-bit signed multiply
@@ -187,27 +192,31 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restri
   __syncthreads();
   const uint32_t tab_base = (uint32_t)(uintptr_t)(LDS_AS uint32_t*)tab;
   const int t = threadIdx.x;
-  const int64_t nblocks = n_oct / 8;
   constexpr int kIt = qk::kGroup * 8 / kThreads;    // octets per thread per group (8)
+  constexpr uint32_t kOctB = kBf16 ? 16u : 32u;     // bytes of weights per octet
   for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
-    const int64_t o0 = g * qk::kGroup * 8 + t;
+    // the group's weights and codes through descriptors based at its first
+    // octet and sized to its octets (fewer in the last group): loads past the
+    // end return zeros (blocks of zeros, absmax 0, codes that are not kept) and
+    // stores past the end are dropped, so no lane needs a branch or a 64-bit
+    // address
+    const int64_t ob = g * qk::kGroup * 8;
+    const uint32_t noct = (uint32_t)min(n_oct - ob, (int64_t)(qk::kGroup * 8));
+    const __amdgpu_buffer_rsrc_t rw = rsrc((const char*)W + ob * kOctB, noct * kOctB);
+    const __amdgpu_buffer_rsrc_t rc = rsrc(codes + ob, 4u * noct);
     RawOct raw[kIt];
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-      const int64_t o = o0 + (int64_t)it * kThreads;
-      raw[it] = load_oct<kBf16>(W, o < n_oct ? o : 0);
+      raw[it].v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, kOctB * t, kOctB * kThreads * it, kNT);
+      raw[it].v1 = kBf16 ? u32x4{0, 0, 0, 0}
+                         : __builtin_amdgcn_raw_buffer_load_b128(rw, kOctB * t + 16, kOctB * kThreads * it, kNT);
     }
     uint32_t m = 0;
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-      const int64_t o = o0 + (int64_t)it * kThreads;
-      // every octet is encoded (past the end: octet 0 again, results dropped),
-      // so that no load is moved into a branch and waited for there
       float a;
       const uint32_t packed = encode8<kBf16>(raw[it], tab, tab_base, a);
-      const bool in = o < n_oct;                      // whole blocks (8 lanes) are in or out together
-      if (in) codes[o] = packed;
-      a = in ? a : 0.0f;
+      __builtin_amdgcn_raw_buffer_store_b32(packed, rc, 4 * t, 4 * kThreads * it, 0);
       if ((t & 7) == 0) absm[(t >> 3) + 32 * it] = a; // block (o - 2048 g) / 8 of the group
       m = max(m, __float_as_uint(a));
     }
@@ -218,12 +227,13 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restri
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) gm = max(gm, red[i]);
     const float cmax = __uint_as_float(gm);
-    const int64_t b = g * qk::kGroup + t;             // one block per thread
-    if (b < nblocks) {
-      const float a = absm[t];
-      c2[b] = (uint8_t)qk::e4m3fn_encode(gm == 0 ? 0.0f : a / cmax);
-      if (absmax) absmax[b] = a;
-    }
+    // one block per thread; blocks past the end are dropped by the descriptors
+    const uint32_t nb = noct / 8;
+    const float a = absm[t];
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)qk::e4m3fn_encode(gm == 0 ? 0.0f : a / cmax),
+                                         rsrc(c2 + g * qk::kGroup, nb), t, 0, 0);
+    if (absmax)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), rsrc(absmax + g * qk::kGroup, 4u * nb), 4 * t, 0, 0);
     if (t == 0) c1[g] = cmax;
     __syncthreads();                                  // red and absm are reused by the next group
   }
