@@ -32,19 +32,6 @@ struct RawOct {
 };
 
 template <bool kBf16>
-__device__ __forceinline__ RawOct load_oct(const void* __restrict__ W, int64_t o) {
-  RawOct r;
-  if (kBf16) {
-    r.v0 = __builtin_nontemporal_load((const u32x4*)W + o);
-    r.v1 = u32x4{0, 0, 0, 0};
-  } else {
-    r.v0 = __builtin_nontemporal_load((const u32x4*)W + 2 * o);
-    r.v1 = __builtin_nontemporal_load((const u32x4*)W + 2 * o + 1);
-  }
-  return r;
-}
-
-template <bool kBf16>
 __device__ __forceinline__ void unpack_oct(const RawOct& r, float (&w)[8]) {
   if (kBf16) {
 #pragma unroll
@@ -148,31 +135,13 @@ __device__ __forceinline__ uint32_t encode8(const RawOct& r, const uint32_t* tab
   return packed;
 }
 
-template <bool kBf16>
-__global__ __launch_bounds__(kThreads) void k_nf4_encode(const void* __restrict__ W, int64_t n_oct,
-                                                         uint32_t* __restrict__ codes,
-                                                         float* __restrict__ absmax, Nf4Buckets bk) {
-  __shared__ __attribute__((aligned(8))) uint32_t tab[34 * 2];
-  if (threadIdx.x < 34) {
-    tab[2 * threadIdx.x] = __float_as_uint(bk.t16[threadIdx.x]);
-    tab[2 * threadIdx.x + 1] = bk.cnt[threadIdx.x];
-  }
-  __syncthreads();
-  const uint32_t tab_base = (uint32_t)(uintptr_t)(LDS_AS uint32_t*)tab;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t o = (int64_t)blockIdx.x * kThreads + threadIdx.x; o < n_oct; o += stride) {
-    float a;
-    codes[o] = encode8<kBf16>(load_oct<kBf16>(W, o), tab, tab_base, a);
-    if ((threadIdx.x & 7) == 0) absmax[o >> 3] = a;
-  }
-}
-
-// Encoder and double quantization in one pass: a work group owns whole groups
-// of 256 blocks (2048 octets, eight per thread, all requested up front); the
-// group's max is reduced across the work group, the blocks' absmax values are
-// parked in LDS, and each thread then forms one block's scale code.  Results
-// equal those of k_nf4_encode then k_double_quant.
-template <bool kBf16>
+// Encoder, with double quantization in the same pass (kDq): a work group owns
+// whole groups of 256 blocks (2048 octets, eight per thread, all requested up
+// front).  With kDq the group's max is reduced across the work group, the
+// blocks' absmax values are parked in LDS, and each thread then forms one
+// block's scale code (the results equal those of the encoder alone followed by
+// k_double_quant); without it each block's absmax is written as it is found.
+template <bool kBf16, bool kDq = true>
 __global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restrict__ W, int64_t n_oct,
                                                             uint32_t* __restrict__ codes,
                                                             float* __restrict__ absmax, uint8_t* __restrict__ c2,
@@ -217,9 +186,17 @@ __global__ __launch_bounds__(kThreads) void k_nf4_encode_dq(const void* __restri
       float a;
       const uint32_t packed = encode8<kBf16>(raw[it], tab, tab_base, a);
       __builtin_amdgcn_raw_buffer_store_b32(packed, rc, 4 * t, 4 * kThreads * it, 0);
-      if ((t & 7) == 0) absm[(t >> 3) + 32 * it] = a; // block (o - 2048 g) / 8 of the group
+      if (!kDq) {
+        // block (t / 8) + 32 it of the group, dropped past the end
+        if ((t & 7) == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), rsrc(absmax + g * qk::kGroup, noct / 2),
+                                                (uint32_t)(t >> 3) * 4u, 128u * it, 0);
+        continue;
+      }
+      if ((t & 7) == 0) absm[(t >> 3) + 32 * it] = a; // block (t / 8) + 32 it of the group
       m = max(m, __float_as_uint(a));
     }
+    if (!kDq) continue;
     m = qk::wave_max_u32(m);
     if ((t & 63) == 0) red[t >> 6] = m;
     __syncthreads();
@@ -309,14 +286,15 @@ int grid_for(int64_t items, int per_block) {
 hipError_t launch_nf4_encode(const void* W, bool bf16, int64_t elems, uint8_t* codes, float* absmax,
                              hipStream_t s) {
   const int64_t n_oct = elems / 8;
-  const int grid = grid_for(n_oct, kThreads);
+  const int64_t ngroups = (elems / qk::kBlock + qk::kGroup - 1) / qk::kGroup;
   if (!nf4_buckets().ok) return hipErrorInvalidValue;   // table assumptions (checked once on the host)
+  const unsigned grid = (unsigned)(ngroups < 65536 ? ngroups : 65536);
   if (bf16)
-    hipLaunchKernelGGL(k_nf4_encode<true>, dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes, absmax,
-                       nf4_buckets());
+    hipLaunchKernelGGL((k_nf4_encode_dq<true, false>), dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes,
+                       absmax, nullptr, nullptr, ngroups, nf4_buckets());
   else
-    hipLaunchKernelGGL(k_nf4_encode<false>, dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes, absmax,
-                       nf4_buckets());
+    hipLaunchKernelGGL((k_nf4_encode_dq<false, false>), dim3(grid), dim3(kThreads), 0, s, W, n_oct, (uint32_t*)codes,
+                       absmax, nullptr, nullptr, ngroups, nf4_buckets());
   return hipGetLastError();
 }
 
