@@ -411,3 +411,39 @@ def test_encoders_with_non_finite_weights(dtype):
         assert_bitexact(s2.cpu().numpy()[in_good_group], rc2[in_good_group], f"{tag} c2 of finite groups")
         assert_bitexact(s1.cpu().numpy().view(np.uint32)[good_groups], rc1.view(np.uint32)[good_groups],
                         f"{tag} c1 of finite groups")
+
+
+def test_encoders_beyond_2_gib():
+    """A 16400 x 262144 bf16 weight (8.6 GB; its codes 2.15 GB): both encoders
+    address the weights, codes, scale codes and group scales past 2^31 bytes.
+    Each row holds 16 whole groups of 256 blocks, so a row's codes, c2 and c1
+    depend on that row alone; the rows holding byte 2^31 of the weights and of
+    the codes, and the first and last rows, are compared with the oracle."""
+    import bit_quantized_lora_blockwise_amd as q
+    rows, cols = 16400, 262144
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2024)
+    W = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
+    for r0 in range(0, rows, 1024):                   # drawn in slabs to bound the fp32 temporary
+        r1 = min(rows, r0 + 1024)
+        W[r0:r1] = (torch.randn((r1 - r0, cols), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    print(f"[encoder 2 GiB+] {rows}x{cols} bf16", flush=True)
+    codes, c2, c1, _ = q.nf4_quantize_dq(W)
+    codes_s, absmax_s = q.nf4_quantize(W)
+    torch.cuda.synchronize()
+    gpr = cols // (64 * 256)                           # groups per row
+    for row in sorted({0, (1 << 30) // cols, (1 << 32) // cols, rows - 1}):
+        Wr = W[row:row + 1].float().cpu().numpy()
+        rc, ra = O.nf4_quantize(Wr)
+        rc2, rc1 = O.nf4_double_quant(ra)
+        nb = cols // 64
+        tag = f"row {row}"
+        assert_bitexact(codes[row].cpu().numpy().reshape(1, -1), rc, f"{tag} fused codes")
+        assert_bitexact(c2[row * nb:(row + 1) * nb].cpu().numpy(), rc2, f"{tag} fused c2")
+        assert_bitexact(c1[row * gpr:(row + 1) * gpr].cpu().numpy().view(np.uint32), rc1.view(np.uint32),
+                        f"{tag} fused c1")
+        assert_bitexact(codes_s[row].cpu().numpy().reshape(1, -1), rc, f"{tag} codes")
+        assert_bitexact(absmax_s[row * nb:(row + 1) * nb].cpu().numpy().view(np.uint32), ra.view(np.uint32),
+                        f"{tag} absmax")
+    del W, codes, c2, c1, codes_s, absmax_s
+    torch.cuda.empty_cache()
