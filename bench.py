@@ -782,9 +782,9 @@ def cpu_model():
 
 def pmc_probe(lins, reps=3):
     """Launches for hardware-counter runs: fused forward and dX GEMMs of both
-    headline linears, the M = 1 decode forward at 4096 -> 11008 (T given), then
-    one copy of 512 MiB (bytes read = bytes written = 2^29), the known-size
-    reference for the traffic counters."""
+    headline linears, the M = 1 decode forward at 4096 -> 11008 (T given), the
+    one-pass encoder of both weights, then one copy of 512 MiB (bytes read =
+    bytes written = 2^29), the known-size reference for the traffic counters."""
     import torch
     q = lins[0].q
     for L in lins:
@@ -800,6 +800,9 @@ def pmc_probe(lins, reps=3):
     Y1 = torch.empty((1, up.N), dtype=torch.bfloat16, device=X1.device)
     for _ in range(reps):
         q.qlora_linear_fwd_t(X1, up.codes, up.c2, up.c1, up.N, T1, up.L2, 1.0, Y=Y1)
+    for _ in range(reps):
+        for L in lins:
+            L.encode()
     torch.cuda.synchronize()
     src = torch.empty((1 << 28,), dtype=torch.int16, device=lins[0].X.device).fill_(1)
     dst = torch.empty_like(src)
@@ -807,7 +810,7 @@ def pmc_probe(lins, reps=3):
     dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_probe": "done", "gemm_launches_per_kind": reps * len(lins), "decode_launches": reps,
-                      "copy_bytes": 1 << 29}))
+                      "encoder_launches": reps * len(lins), "copy_bytes": 1 << 29}))
 
 
 def decode_roofline(dec):
