@@ -85,6 +85,68 @@ hipError_t run_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, cons
   return launch_qgemm_dx(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s);
 }
 
+// ---- dL1 / dL2 beside the dX product -----------------------------------------
+// The dX product's persistent grid takes its tiles in rounds of one work group
+// per CU (the CU count rounded down to a multiple of 8).  When the tiles leave
+// the last round partly empty, the CUs without a tile in it would idle while
+// the others finish; the two TN products (dL1 = X^T G, dL2 = s T^T dY), which
+// read nothing the dX product writes, then run on a second stream and take
+// those CUs.  A dX tile occupies all of a CU's registers, so the TN work
+// groups only start where a work group of the dX product has finished.  With
+// whole rounds there is no idle round to fill and the products stay in order
+// on the caller's stream.  The kernels, their work split and the order of
+// every sum are the same on both paths, so the results are identical.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  int cus = 0;
+  bool failed = false;
+};
+
+constexpr int kMaxDevices = 64;
+
+// The calling thread's second stream on the current device (default priority,
+// created on first use and kept until the process ends), or nullptr when it
+// cannot be had; the caller then keeps everything on its own stream.
+SideStream* side_stream() {
+  thread_local SideStream per_dev[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& d = per_dev[dev];
+  if (d.failed) return nullptr;
+  if (!d.s) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8 ||
+        hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&d.join, hipEventDisableTiming) != hipSuccess ||
+        hipStreamCreateWithFlags(&d.s, hipStreamNonBlocking) != hipSuccess) {
+      d.failed = true;
+      d.s = nullptr;
+      return nullptr;
+    }
+    d.cus = cus;
+  }
+  return &d;
+}
+
+// Joins the second stream back into the caller's stream s, also after a failed
+// launch `e` on it, so that what was enqueued there stays ordered before s's
+// later work; returns the first error.
+hipError_t join_side(SideStream& d, hipStream_t s, hipError_t e) {
+  hipError_t j = hipEventRecord(d.join, d.s);
+  if (j == hipSuccess) j = hipStreamWaitEvent(s, d.join, 0);
+  return e != hipSuccess ? e : j;
+}
+
+// True when the dX product [M, K] runs on the persistent grid and its last
+// round of tiles (256 x 256 each) is partly empty.
+bool dx_last_round_partial(const SideStream& d, int64_t M, int64_t K, int64_t NG) {
+  if (!qgemm_big_ok(true, M, K, NG)) return false;
+  const int64_t tiles = ((M + 255) / 256) * ((K + 255) / 256);
+  const int64_t grid = d.cus / 8 * 8;
+  return tiles > grid && tiles % grid != 0;
+}
+
 // ---- stacked linears -------------------------------------------------------
 bool group_ok(int64_t M, int64_t K, int64_t N, int G, int r) {
   if (G < 1 || G > 16 || N <= 0 || N > (int64_t(1) << 31) / G) return false;
@@ -307,12 +369,23 @@ int qlora_group_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K,
                               part, s));
   }
   const uint16_t* Tg = T ? T : Tw;
+  SideStream* sd = dX ? side_stream() : nullptr;
+  const bool fork = sd && dx_last_round_partial(*sd, M, K, N * G);
+  if (fork) QL_TRY(hipEventRecord(sd->fork, s));
   if (dX) QL_TRY(launch_qgemm_big(true, dY, M, K, N * G, codes, c2, c1, Gm, L1, r, 1.0f, dX, s, G));
-  for (int g = 0; g < G; ++g) {
-    const int64_t mr = (int64_t)g * M * r;
-    QL_TRY(launch_lora_tn_pair(X, K, Gm + mr, K, 1.0f, dL1 + (int64_t)g * K * r, dY + (int64_t)g * N, ldy, Tg + mr,
-                               N, lora_scale, dL2 + (int64_t)g * r * N, M, r, part, s));
+  hipStream_t st = s;
+  if (fork) {
+    QL_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
+    st = sd->s;
   }
+  hipError_t e = hipSuccess;
+  for (int g = 0; g < G && e == hipSuccess; ++g) {
+    const int64_t mr = (int64_t)g * M * r;
+    e = launch_lora_tn_pair(X, K, Gm + mr, K, 1.0f, dL1 + (int64_t)g * K * r, dY + (int64_t)g * N, ldy, Tg + mr, N,
+                            lora_scale, dL2 + (int64_t)g * r * N, M, r, part, st);
+  }
+  if (fork) e = join_side(*sd, s, e);
+  QL_TRY(e);
   return QL_OK;
 }
 
@@ -395,6 +468,15 @@ int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K
     T = Tw;
   }
   QL_TRY(launch_lora_skinny(dY, M, N, N, L2, false, r, lora_scale, G, part, s));
+  SideStream* sd = dX ? side_stream() : nullptr;
+  if (sd && dx_last_round_partial(*sd, M, K, N)) {
+    QL_TRY(hipEventRecord(sd->fork, s));
+    QL_TRY(run_dx_gemm(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s));
+    QL_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
+    const hipError_t e = launch_lora_tn_pair(X, K, G, K, 1.0f, dL1, dY, N, T, N, lora_scale, dL2, M, r, part, sd->s);
+    QL_TRY(join_side(*sd, s, e));
+    return QL_OK;
+  }
   if (dX) QL_TRY(run_dx_gemm(dY, M, K, N, codes, c2, c1, G, L1, r, dX, s));
   QL_TRY(launch_lora_tn_pair(X, K, G, K, 1.0f, dL1, dY, N, T, N, lora_scale, dL2, M, r, part, s));
   return QL_OK;

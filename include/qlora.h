@@ -158,7 +158,16 @@ size_t qlora_linear_bwd_workspace(int64_t M, int64_t K, int64_t N, int r);
  *   dL2 = fp32(lora_scale * T^T dY)           [r, N]
  * T [M, r] bf16 is the forward's T_out; when NULL it is recomputed from X and L1
  * (gradient-checkpointing style). dY [M, N] bf16. Shapes and workspace as in
- * the forward; ws_bytes >= qlora_linear_bwd_workspace(...).                     */
+ * the forward; ws_bytes >= qlora_linear_bwd_workspace(...).
+ * Streams: when the dX product's tiles (256 x 256) leave the last round of its
+ * persistent grid partly empty, dL1 and dL2 are computed on a second stream
+ * that the library creates once per calling thread and device (default
+ * priority, never destroyed), forked from `stream` after G and joined back into
+ * it before the call returns, also when it fails with QL_ERR_HIP. Work the
+ * caller enqueues on `stream` afterwards is ordered after all of the call's
+ * work, as on one stream, and the results are bit-identical to the one-stream
+ * order. Calls from one thread share that second stream, so their dL1 / dL2
+ * products run in call order even when the callers' streams differ.           */
 int qlora_linear_bwd(const uint16_t* X, const uint16_t* dY, int64_t M, int64_t K, int64_t N,
                      const uint8_t* codes, const uint8_t* c2, const float* c1,
                      const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
@@ -225,6 +234,8 @@ int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_
  *   qlora_group_bwd: dY [M, G N]; per segment G_g, dL1_g [K, r], dL2_g [r, N]
  *     exactly as qlora_linear_bwd of segment g (dL1, dL2: G consecutive blocks);
  *     dX = bf16(sum_g (dY_g W'_g + G_g L1_g^T)), one rounding (NULL: skipped).
+ *     The per-segment dL1 / dL2 products may run on the second stream
+ *     described at qlora_linear_bwd, under the same rule and guarantees.
  * Requirements beyond qlora_linear_*: 1 <= G <= 16; for G > 1, N % 256 == 0 and
  * M > 16, except that qlora_group_fwd also takes decode sizes, 1 <= M <= 16,
  * when X fits the decode kernel's LDS (M K <= 16384) and r % 4 == 0: then every

@@ -325,3 +325,65 @@ def test_read_probe_runs(loads):
     P.empty_probe(1024, 256)
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
+
+
+def _partial_round_K(M):
+    """A K whose dX product [M, K] (256 x 256 tiles) leaves the last round of its
+    persistent grid (the CU count rounded down to a multiple of 8) partly empty."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = cus // 8 * 8
+    rows = (M + 255) // 256
+    cols = grid // rows + 1
+    assert rows * cols > grid and (rows * cols) % grid != 0
+    return 256 * cols
+
+
+def test_backward_second_stream_matches_one_stream():
+    """The dL1 / dL2 products run on the library's second stream when the dX
+    product leaves a partial last round: same bits as the one-stream order
+    (dX = None keeps them on the caller's stream) and as the dX stage entry
+    point, and work the caller enqueues on its stream after the call sees the
+    finished gradients."""
+    q = qlib()
+    M, N, r = 512, 256, 16
+    K = _partial_round_K(M)
+    inp = WL.layer_inputs(N, K, M, r, seed_base=9100, l2_std=0.1)
+    gq, _ = quantize_both(inp["W"])
+    X, L1, L2, dY = (inp[k].to(DEV) for k in ("X", "L1", "L2", "dY"))
+    T = q.qlora_lora_down(X, L1)
+    ref_dX = q.qlora_linear_dx(dY, *gq, K, q.qlora_lora_grad_in(dY, L2, 0.5), L1)
+    _, ref_dL1, ref_dL2 = q.qlora_linear_bwd(X, dY, *gq, L1, L2, 0.5, T=T, dX=None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(2):
+        with torch.cuda.stream(side):
+            dX, dL1, dL2 = q.qlora_linear_bwd(X, dY, *gq, L1, L2, 0.5, T=T)
+            copies = (dX.clone(), dL1.clone(), dL2.clone())
+        side.synchronize()
+        assert torch.equal(copies[0], ref_dX)
+        assert torch.equal(copies[1], ref_dL1) and torch.equal(copies[2], ref_dL2)
+
+
+def test_group_backward_second_stream_matches_segments():
+    """Stacked backward (G = 2) with a partial last dX round: every segment's
+    dL1 / dL2 equal qlora_linear_bwd of that segment bit for bit."""
+    q = qlib()
+    M, N, r, G = 512, 256, 16, 2
+    K = _partial_round_K(M)
+    segs = [WL.layer_inputs(N, K, M, r, seed_base=9200 + 10 * g, l2_std=0.1) for g in range(G)]
+    X = segs[0]["X"].to(DEV)
+    W = torch.cat([s["W"] for s in segs], 0).to(DEV)
+    codes, c2, c1, _ = q.nf4_quantize_dq(W)
+    L1 = torch.stack([s["L1"] for s in segs], 0).to(DEV)
+    L2 = torch.stack([s["L2"] for s in segs], 0).to(DEV)
+    dY = torch.cat([s["dY"] for s in segs], 1).to(DEV)
+    _, gdL1, gdL2 = q.qlora_group_bwd(X, dY, codes, c2, c1, G, L1, L2, 0.5)
+    torch.cuda.synchronize()
+    cg = codes.view(G, N, K // 2)
+    nb = N * K // 64
+    for g in range(G):
+        sg = (cg[g], c2.view(-1)[g * nb:(g + 1) * nb], c1.view(-1)[g * nb // 256:(g + 1) * nb // 256])
+        _, dL1, dL2 = q.qlora_linear_bwd(X, dY[:, g * N:(g + 1) * N].contiguous(), *sg, L1[g], L2[g], 0.5, dX=None)
+        torch.cuda.synchronize()
+        assert torch.equal(gdL1.view(G, K, r)[g], dL1) and torch.equal(gdL2.view(G, r, N)[g], dL2)
