@@ -1,6 +1,11 @@
 // C ABI of libqlora.so: argument checks, workspace sizing and kernel dispatch.
 // Declarations and the contract of each entry point are in include/qlora.h.
+#include <unistd.h>
+
 #include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cstdlib>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -42,15 +47,39 @@ bool shapes_ok(int64_t M, int64_t K, int64_t N, int r) {
 
 // Workspace layout of the forward: [T (M x r bf16) when the caller gives no T_out][fp32 partials].
 struct FwdWs {
-  size_t t_bytes, part_bytes, total;
+  size_t t_bytes, part_bytes, flag_bytes, total;
 };
 FwdWs fwd_ws(int64_t M, int64_t K, int64_t N, int r) {
   (void)N;
   FwdWs w;
   w.t_bytes = round_up((size_t)M * r * 2);
   w.part_bytes = round_up(lora_skinny_ws(M, K, r));
-  w.total = w.t_bytes + w.part_bytes;
+  w.flag_bytes = qgemv_fused_ok(M, K, r) ? round_up(qgemv_fused_sync_bytes(M, r)) : 0;
+  w.total = w.t_bytes + w.part_bytes + w.flag_bytes;
   return w;
+}
+
+// Epochs of the decode forward's flags and T records: never the same twice in a
+// process (nor in their low 32 bits, never 0), and started at a value that no
+// earlier process is likely to have left in reused memory.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> ctr{[] {
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return (t * 0x9E3779B97F4A7C15ull) ^ ((uint64_t)getpid() << 40) ^ (uint64_t)(uintptr_t)&ctr;
+  }()};
+  uint64_t e;
+  do e = ctr.fetch_add(1, std::memory_order_relaxed);
+  while ((uint32_t)e == 0);
+  return e;
+}
+
+// Polls of the decode forward's wait for its slices before a wave forms them
+// itself.  QLORA_DECODE_T_SPINS overrides it (a test sets 0 to exercise the
+// wave's own path).
+uint32_t decode_spins() {
+  const char* e = std::getenv("QLORA_DECODE_T_SPINS");
+  if (e && *e) return (uint32_t)std::strtoul(e, nullptr, 10);
+  return 1u << 12;
 }
 
 // Backward: [T (recomputed when NULL)][G (M x r bf16)][fp32 partials, reused by each step].
@@ -425,6 +454,13 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const u
   char* ws = (char*)workspace;
   uint16_t* T = T_out ? T_out : (uint16_t*)ws;
   float* part = (float*)(ws + w.t_bytes);
+  if (qgemv_fused_ok(M, K, r) && decode_t_ok(M, K, X, L1)) {
+    // decode, small X: the slices of T = X L1 formed, added and rounded in the decode launch itself
+    void* sync = ws + w.t_bytes + w.part_bytes;
+    QL_TRY(launch_qgemv_fwd_fused(X, M, K, N, codes, c2, c1, L1, r, part, sync, next_epoch(), decode_spins(),
+                                  T_out, L2, lora_scale, Y, s));
+    return QL_OK;
+  }
   if (M <= 16 && (r % 4) == 0 && decode_t_ok(M, K, X, L1)) {
     // decode: the slices of T = X L1, added and rounded inside the decode kernel
     QL_TRY(launch_lora_part(X, M, K, L1, r, part, s));

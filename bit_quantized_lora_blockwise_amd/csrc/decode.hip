@@ -26,6 +26,7 @@
 // global memory together with the step's codes.
 #include "dequant.h"
 #include "kernels.h"
+#include "tpart.h"
 
 namespace {
 
@@ -56,6 +57,71 @@ struct Step {
   u32x4 xa[kXLds ? 1 : 8];
 };
 
+// kFuse: T is formed in this grid, in three roles by work-group index.
+//  - The first nprod = S ceil(r / 16) work groups each form one (slice, column
+//    tile) of the slices with tpart::slice_tile (the arithmetic of the
+//    stand-alone partial-sum kernel), store it to `part` and publish it by
+//    writing `epoch` to its flag with release semantics at agent scope.
+//  - The next ceil(r / 16) ("summers", one wave each) wait for the S flags of
+//    their column tile, read the slices with agent-coherent (sc1) loads, which
+//    bypass the other XCDs' non-coherent L2 copies, add them in order s = 0 ..
+//    S-1, round T once to bf16, write T_out and publish T as 64-bit records
+//    rec[m][c / 2] = {T[m][c], T[m][c + 1], low 32 bits of epoch}, each stored
+//    by one single-copy-atomic 64-bit store.
+//  - The rest take the 16-row tiles.  A tile's waves request their two records
+//    before converting their last step and check the epoch of each at the end,
+//    so no ordering between loads is needed and the round trip overlaps the
+//    conversion.
+// Every wait (a summer's for its flags, a tile's for its records) is bounded by
+// `spins` polls: past it the wave forms the slices itself (tpart::slice_wave,
+// same bits), so no work group ever depends on another being scheduled.  Flags
+// and records carry the epoch of the call that wrote them (never repeated by
+// the host), so they need no clearing between calls.
+struct TFuse {
+  const uint16_t* L1;
+  int64_t rows;              // rows of K per slice (multiple of 32)
+  int nprod;                 // slice work groups (S ceil(r / 16))
+  float* part;               // [S][M][r] fp32 slices
+  uint64_t* flags;           // [nprod]
+  uint64_t* rec;             // [M][r / 2] T records
+  uint64_t epoch;            // its low 32 bits are never 0
+  uint32_t spins;
+};
+
+// T fragment of lane (g, col) of a wave working on column tile ct: the S slices
+// of rows m = col, ranks 16 ct + 4 g .. + 3, added in order s = 0 .. S-1 (read
+// once the S producers of the tile have published them, else formed here).
+__device__ __forceinline__ f32x4 fused_t_sum(const TFuse& fz, const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                             int r, int S, int ct, bool t_ok, uint32_t off, f32x4* slot) {
+  const int l = threadIdx.x & 63;
+  const int ctiles = (r + 15) / 16;
+  bool ready = false;
+  for (uint32_t it = 0;; ++it) {
+    const uint64_t f = l < S ? __hip_atomic_load(fz.flags + l * ctiles + ct, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : fz.epoch;
+    ready = __all(f == fz.epoch);
+    if (ready || it >= fz.spins) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  asm volatile("" ::: "memory");             // the slices are requested after the flags have been seen
+  f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (ready) {
+    const __amdgpu_buffer_rsrc_t rp = rsrc(fz.part, 4 * (uint64_t)S * M * r);
+    f32x4 pv[kDecodeTSlices];
+#pragma unroll
+    for (int s = 0; s < kDecodeTSlices; ++s)
+      pv[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rp, (t_ok && s < S) ? off + (uint32_t)(4 * s * M * r) : kOOB, 0,
+                                            16 /* sc1: agent-coherent */));
+#pragma unroll
+    for (int s = 0; s < kDecodeTSlices; ++s)
+      if (s < S) sum += pv[s];
+  } else {
+    for (int s = 0; s < S; ++s) sum += tpart::slice_wave(X, M, K, fz.L1, r, fz.rows, ct, s, slot);
+  }
+  return sum;
+}
+
 // kTPart: T is not given but formed here from the S fp32 slices Tp[s][m][c]
 // (added in order s = 0 .. S-1, rounded once), and written to T (if not null)
 // by work group 0.
@@ -68,7 +134,7 @@ struct Step {
 // Eight-wave work groups are held to six waves per SIMD (three work groups per
 // CU, at most 80 VGPRs): given the registers, the compiler would otherwise keep
 // more values live and fit only two.
-template <bool kXLds, int kWv, int kXPer, bool kTPart>
+template <bool kXLds, int kWv, int kXPer, bool kTPart, bool kFuse>
 __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         int64_t N, int64_t ld, const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ c2,
@@ -76,17 +142,52 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
                                                         uint16_t* __restrict__ T, const float* __restrict__ Tp, int S,
                                                         const uint16_t* __restrict__ L2, int r, float scale,
                                                         uint16_t* __restrict__ Y, Nf4Params p, int seg_tiles,
-                                                        int64_t l2ld) {
+                                                        int64_t l2ld, TFuse fz) {
+  static_assert(!kFuse || (kXLds && kTPart), "slices formed in the grid: X staged in LDS, T from slices");
   constexpr int kThr = 64 * kWv;
   __shared__ __attribute__((aligned(16))) uint8_t lds[(kXLds ? kXBytes + kZeroBytes : 0) + kWv * 64 * 16];
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
   const int g = l >> 4, col = l & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * kRows;
+  if constexpr (kFuse) {
+    if ((int)blockIdx.x < fz.nprod) {
+      // producer: one (slice, column tile) of T's slices, then its flag
+      const int ctiles = (r + 15) / 16;
+      tpart::slice_tile<kWv, 2>(X, M, K, fz.L1, r, fz.rows, fz.part, (int)blockIdx.x % ctiles,
+                                (int)blockIdx.x / ctiles, (f32x4*)lds);
+      if (t == 0) __hip_atomic_store(fz.flags + blockIdx.x, fz.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    if ((int)blockIdx.x < fz.nprod + (r + 15) / 16) {
+      // summer of column tile ct (wave 0): T's records for ranks 16 ct .. 16 ct + 15
+      if (w != 0) return;
+      const int ct = (int)blockIdx.x - fz.nprod;
+      const int rb = 16 * ct + 4 * g;
+      const bool ok = rb < r && col < M;
+      const int S_ = S;
+      const f32x4 sum = fused_t_sum(fz, X, M, K, r, S_, ct, ok, (uint32_t)(4 * (col * r + rb)), (f32x4*)lds);
+      uint32_t vt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vt[j] = qk::f32_to_bf16(sum[j]);
+      if (ok) {
+        if (T) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) T[col * r + rb + j] = (uint16_t)vt[j];
+        }
+        const uint64_t tag = (uint64_t)(uint32_t)fz.epoch << 32;
+        uint64_t* rp = fz.rec + (col * r + rb) / 2;
+        __hip_atomic_store(rp, tag | vt[0] | (vt[1] << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(rp + 1, tag | vt[2] | (vt[3] << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
+    }
+  }
+  const uint32_t tile = kFuse ? blockIdx.x - (uint32_t)(fz.nprod + (r + 15) / 16) : blockIdx.x;
+  const int64_t n0 = (int64_t)tile * kRows;
   const int64_t nrow = n0 + col;
-  const uint32_t sg = blockIdx.x / (uint32_t)seg_tiles;          // segment of this work group
+  const uint32_t sg = tile / (uint32_t)seg_tiles;               // segment of this work group
   const int64_t nloc = nrow - (int64_t)sg * seg_tiles * kRows;  // its row within the segment
-  const bool seg_first = blockIdx.x == sg * (uint32_t)seg_tiles;
+  const bool seg_first = tile == sg * (uint32_t)seg_tiles;
   if (T) T += (int64_t)sg * M * r;                  // a null T (no T to write) stays null
   if (kTPart) Tp += (int64_t)sg * S * M * r;
   L2 += (int64_t)sg * r * l2ld;
@@ -133,7 +234,7 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
   const int rb = 16 * w + 4 * g;                   // first of this lane's four LoRA ranks
   const bool t_ok = rb < r && m_ok;                // r % 4 == 0 with kTPart: the four ranks are all in or all out
   f32x4 ps[kTPart ? kDecodeTSlices : 1];
-  if (kTPart) {
+  if (kTPart && !kFuse) {
     const __amdgpu_buffer_rsrc_t rp = rsrc(Tp, 4 * (uint64_t)S * M * r);
 #pragma unroll
     for (int s = 0; s < kDecodeTSlices; ++s)
@@ -187,7 +288,7 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
   uint32_t lt[2];
   {
     uint32_t vt[4];
-    if (kTPart) {
+    if (kTPart && !kFuse) {
       // the slices added in order s = 0 .. S-1, rounded once
       f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -220,6 +321,18 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
     __syncthreads();
   }
 
+  // kFuse: T's two records of this lane (see TFuse), requested before the last
+  // step is converted: ra_ in the last pair, rb_ before an odd last step (or
+  // when the wave has no steps)
+  const __amdgpu_buffer_rsrc_t rrec = rsrc(kFuse ? (const void*)fz.rec : (const void*)Y, 4 * (uint64_t)M * r);
+  const uint32_t rec_off = t_ok ? (uint32_t)(4 * (col * r + rb)) : kOOB;
+  u32x2 ra0 = {0, 0}, ra1 = {0, 0}, rb0 = {0, 0}, rb1 = {0, 0};
+  auto load_recs = [&](bool on, u32x2& v0, u32x2& v1) {
+    const uint32_t o = on ? rec_off : kOOB;
+    v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rrec, o, 0, 16 /* sc1 */));
+    v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rrec, o + 8, 0, 16 /* sc1 */));
+  };
+
   f32x4 acc = {0, 0, 0, 0};
   auto compute_step = [&](uint32_t i, const Step<kXLds>& st) {
     const uint32_t kb = kb0 + i * kbstep;
@@ -246,7 +359,7 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
   // converted (no exit between the halves: the compiler's wait before each
   // conversion then covers exactly that step), then the odd last step
   uint32_t i = 0;
-  for (; i + 2 <= nst; i += 2) {
+  for (; kFuse ? i + 2 < nst : i + 2 <= nst; i += 2) {
     load_step(i + 1, sb);
     __builtin_amdgcn_sched_barrier(0);
     compute_step(i, sa);
@@ -254,7 +367,25 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
     __builtin_amdgcn_sched_barrier(0);
     compute_step(i + 1, sb);
   }
-  if (i < nst) compute_step(i, sa);
+  if constexpr (kFuse) {
+    // the last pair, with the records requested before its second step (a
+    // reload in every pair would make each pair wait for the previous one)
+    if (i + 2 == nst) {
+      load_step(i + 1, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_step(i, sa);
+      load_recs(true, ra0, ra1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_step(i + 1, sb);
+    } else {
+      // an odd last step (or none): the records requested before it
+      load_recs(true, rb0, rb1);
+      if (i < nst) compute_step(i, sa);
+    }
+  } else {
+    if (i < nst) compute_step(i, sa);
+  }
+  const bool recs_late = (nst & 1u) != 0 || nst == 0;     // uniform
 
   {
     // the L2 (and given T) values are first used here: the empty volatile asm
@@ -269,6 +400,32 @@ __global__ __launch_bounds__(64 * kWv, kWv == 8 ? 6 : 1) void k_qgemv_fwd(const 
       asm volatile("" : "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));
       lt[0] = __builtin_amdgcn_perm(b1, b0, 0x05040100u);
       lt[1] = __builtin_amdgcn_perm(b3, b2, 0x05040100u);
+    }
+    if constexpr (kFuse) {
+      // T from the records published by this grid's summers (see TFuse)
+      const uint32_t tag = (uint32_t)fz.epoch;
+      u32x2 v0 = recs_late ? rb0 : ra0, v1 = recs_late ? rb1 : ra1;
+      bool ok = !t_ok || (v0[1] == tag && v1[1] == tag);
+      for (uint32_t it = 0; !__all(ok) && it < fz.spins; ++it) {
+        __builtin_amdgcn_s_sleep(2);
+        load_recs(true, v0, v1);
+        ok = !t_ok || (v0[1] == tag && v1[1] == tag);
+      }
+      if (__all(ok)) {
+        lt[0] = t_ok ? v0[0] : 0u;
+        lt[1] = t_ok ? v1[0] : 0u;
+      } else {
+        // not published within the bound: the slices formed and added here (same bits)
+        f32x4* slot = (f32x4*)(lds + (kXLds ? kXBytes + kZeroBytes : 0)) + w * 64;
+        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (16 * w < r)
+          for (int s = 0; s < S; ++s) sum += tpart::slice_wave(X, M, K, fz.L1, r, fz.rows, w, s, slot);
+        uint32_t vt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vt[j] = qk::f32_to_bf16(sum[j]);
+        lt[0] = t_ok ? (vt[0] | (vt[1] << 16)) : 0u;
+        lt[1] = t_ok ? (vt[2] | (vt[3] << 16)) : 0u;
+      }
     }
     f32x4 zl = {0, 0, 0, 0};
     zl = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{lt[0], lt[1]}),
@@ -758,6 +915,7 @@ struct QgemvArgs {
   uint16_t* Y;
   int seg_tiles = 0x7fffffff;   // 16-row tiles per stacked segment (one linear: more than any grid)
   int64_t l2ld = 0;             // row stride of each segment's L2 (0: ld)
+  TFuse fz = {};                // slices of T formed in the grid (k_qgemv_fwd only)
 };
 
 template <bool kTPart>
@@ -777,22 +935,22 @@ hipError_t launch_slices(int kt, unsigned grid, int64_t ksl, hipStream_t s, cons
   return hipGetLastError();
 }
 
-template <bool kXLds, int kWv, int kXPer, bool kTPart>
+template <bool kXLds, int kWv, int kXPer, bool kTPart, bool kFuse = false>
 hipError_t launch_one(dim3 grid, hipStream_t s, const QgemvArgs& a) {
-  hipLaunchKernelGGL((k_qgemv_fwd<kXLds, kWv, kXPer, kTPart>), grid, dim3(64 * kWv), 0, s, a.X, a.M, a.K, a.rows,
-                     a.ld, a.codes, a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params(), a.seg_tiles,
-                     a.l2ld ? a.l2ld : a.ld);
+  hipLaunchKernelGGL((k_qgemv_fwd<kXLds, kWv, kXPer, kTPart, kFuse>), grid, dim3(64 * kWv), 0, s, a.X, a.M, a.K,
+                     a.rows, a.ld, a.codes, a.c2, a.c1, a.T, a.Tp, a.S, a.L2, a.r, a.scale, a.Y, nf4_params(),
+                     a.seg_tiles, a.l2ld ? a.l2ld : a.ld, a.fz);
   return hipGetLastError();
 }
 
 // Small-X variant for kWv waves: the fewest X loads per thread (1, 2 or 4)
 // that cover M * K * 2 bytes.
-template <int kWv, bool kTPart>
+template <int kWv, bool kTPart, bool kFuse = false>
 hipError_t launch_lds(dim3 grid, hipStream_t s, const QgemvArgs& a) {
   const int64_t per = (a.M * a.K * 2 + 16 * 64 * kWv - 1) / (16 * 64 * kWv);
-  if (per <= 1) return launch_one<true, kWv, 1, kTPart>(grid, s, a);
-  if (per <= 2) return launch_one<true, kWv, 2, kTPart>(grid, s, a);
-  return launch_one<true, kWv, 4, kTPart>(grid, s, a);
+  if (per <= 1) return launch_one<true, kWv, 1, kTPart, kFuse>(grid, s, a);
+  if (per <= 2) return launch_one<true, kWv, 2, kTPart, kFuse>(grid, s, a);
+  return launch_one<true, kWv, 4, kTPart, kFuse>(grid, s, a);
 }
 
 template <bool kTPart>
@@ -846,6 +1004,30 @@ hipError_t launch_qgemv_fwd_tpart(const uint16_t* X, int64_t M, int64_t K, int64
   if (S < 1 || S > kDecodeTSlices || (r % 4) != 0 || ((uintptr_t)Tpart & 15) != 0) return hipErrorInvalidValue;
   const QgemvArgs a{X, M, K, 0, N, codes, c2, c1, T_out, Tpart, S, L2, r, scale, Y};
   return launch_shape<true>(a, N, s);
+}
+
+bool qgemv_fused_ok(int64_t M, int64_t K, int r) {
+  return M >= 1 && M <= 16 && M * K * 2 <= kXBytes && (K % 64) == 0 && r >= 4 && r <= 64 && (r % 4) == 0;
+}
+
+size_t qgemv_fused_sync_bytes(int64_t M, int r) {
+  return 8 * (size_t)kDecodeTSlices * ((r + 15) / 16) + 4 * (size_t)M * r;
+}
+
+hipError_t launch_qgemv_fwd_fused(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                                  const uint8_t* c2, const float* c1, const uint16_t* L1, int r, float* part,
+                                  void* sync, uint64_t epoch, uint32_t spins, uint16_t* T_out,
+                                  const uint16_t* L2, float scale, uint16_t* Y, hipStream_t s) {
+  if (!qgemv_fused_ok(M, K, r) || ((uintptr_t)part & 15) != 0 || ((uintptr_t)sync & 15) != 0 ||
+      (uint32_t)epoch == 0 || N * (K / 2) >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  const int S = decode_t_slices(K);
+  const int ctiles = (r + 15) / 16;
+  QgemvArgs a{X, M, K, N, N, codes, c2, c1, T_out, part, S, L2, r, scale, Y};
+  uint64_t* flags = (uint64_t*)sync;
+  a.fz = TFuse{L1, decode_t_rows(K), S * ctiles, part, flags, flags + (size_t)kDecodeTSlices * ctiles, epoch, spins};
+  const int64_t wgs = (N + kRows - 1) / kRows;
+  return launch_lds<8, true, true>(dim3((unsigned)(a.fz.nprod + ctiles + wgs)), s, a);
 }
 
 bool qgemv_group_ok(int64_t M, int64_t K, int64_t N, int G) {

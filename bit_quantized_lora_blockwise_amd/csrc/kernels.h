@@ -60,6 +60,7 @@ size_t lora_skinny_ws(int64_t M, int64_t R, int r);
 // part + g S M r (one launch for all).
 constexpr int kDecodeTSlices = 8;
 int decode_t_slices(int64_t K);
+int64_t decode_t_rows(int64_t K);   // rows of K per slice (a multiple of 32)
 bool decode_t_ok(int64_t M, int64_t K, const void* X, const void* L1);
 hipError_t launch_lora_part(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float* part,
                             hipStream_t s, int G = 1);
@@ -111,6 +112,19 @@ hipError_t launch_qgemv_group_tpart(const uint16_t* X, int64_t M, int64_t K, int
 hipError_t launch_qgemv_fwd_tpart(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
                                   const uint8_t* c2, const float* c1, const float* Tpart, int S, uint16_t* T_out,
                                   const uint16_t* L2, int r, float scale, uint16_t* Y, hipStream_t s);
+// The same decode forward with T formed inside the one launch (no separate
+// partial-sum launch): M * K * 2 <= 32 KB, r % 4 == 0, r <= 64.  part: S M r
+// fp32 (16-byte aligned); sync: qgemv_fused_sync_bytes(M, r) bytes (16-byte
+// aligned) of flags and T records, holding anything but data tagged with
+// `epoch`, which must differ from every earlier call's epoch on the same memory
+// (in its low 32 bits too, which must not be 0); spins bounds each wave's wait
+// (past it the wave forms T's slices itself, same bits).
+bool qgemv_fused_ok(int64_t M, int64_t K, int r);
+size_t qgemv_fused_sync_bytes(int64_t M, int r);
+hipError_t launch_qgemv_fwd_fused(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* codes,
+                                  const uint8_t* c2, const float* c1, const uint16_t* L1, int r, float* part,
+                                  void* sync, uint64_t epoch, uint32_t spins, uint16_t* T_out,
+                                  const uint16_t* L2, float scale, uint16_t* Y, hipStream_t s);
 // Large-tile (256 x 256) versions of both GEMMs: dx = false computes the forward
 // (A = X, LA = T, LB = L2, C = Y), dx = true the dX product (A = dY, LA = G,
 // LB = L1, C = dX).  qgemm_big_ok says whether the shapes qualify.  nseg > 1:

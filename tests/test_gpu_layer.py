@@ -387,3 +387,45 @@ def test_group_backward_second_stream_matches_segments():
         _, dL1, dL2 = q.qlora_linear_bwd(X, dY[:, g * N:(g + 1) * N].contiguous(), *sg, L1[g], L2[g], 0.5, dX=None)
         torch.cuda.synchronize()
         assert torch.equal(gdL1.view(G, K, r)[g], dL1) and torch.equal(gdL2.view(G, r, N)[g], dL2)
+
+
+# the decode forward at small X forms T's slices in the first work groups of its
+# own launch; a tile's waves wait for them (bounded) or form them themselves.
+# QLORA_DECODE_T_SPINS=0 cuts every wait to one poll, so that waves take their
+# own path whenever the slices are not yet there: Y and T must be the same bits
+# either way, and the same bits as T by the stand-alone product + Y by the stage
+# entry point.  Ranks 8 (half of one column tile), 20 (a partial second tile)
+# and 64; M = 1, 3 and 8; K down to one slice; ragged N.
+DECODE_FUSED_T = [(1, 4096, 11008, 64), (3, 2880, 620, 8), (8, 2048, 1000, 20), (1, 448, 33, 64),
+                  (4, 4096, 4096, 64)]
+
+
+@pytest.mark.parametrize("M,K,N,r", DECODE_FUSED_T)
+def test_decode_fused_T_own_path_same_bits(M, K, N, r, monkeypatch):
+    import os
+    q = qlib()
+    print(f"[layer] decode fused T M={M} K={K} N={N} r={r}", flush=True)
+    inp = WL.layer_inputs(N, K, M, r, seed_base=M * 7 + K + N + r, l2_std=0.3)
+    gq, rq = quantize_both(inp["W"])
+    X, L1, L2 = (inp[k].to(DEV) for k in ("X", "L1", "L2"))
+    Ya, Ta = q.qlora_linear_fwd(X, *gq, N, L1, L2, 0.7, T_out=True)
+    torch.cuda.synchronize()
+    outs = []
+    monkeypatch.setenv("QLORA_DECODE_T_SPINS", "0")
+    for _ in range(3):
+        Yb, Tb = q.qlora_linear_fwd(X, *gq, N, L1, L2, 0.7, T_out=True)
+        torch.cuda.synchronize()
+        outs.append((Yb, Tb))
+    monkeypatch.delenv("QLORA_DECODE_T_SPINS")
+    Ts = q.qlora_lora_down(X, L1)
+    Ys = q.qlora_linear_fwd_t(X, *gq, N, Ts, L2, 0.7)
+    torch.cuda.synchronize()
+    for Yb, Tb in outs:
+        assert_bitexact(bits(Tb), bits(Ta), "T, own path vs waited")
+        assert_bitexact(bits(Yb), bits(Ya), "Y, own path vs waited")
+    assert_bitexact(bits(Ta), bits(Ts), "T, in-launch slices vs stand-alone product")
+    assert_bitexact(bits(Ya), bits(Ys), "Y, one launch vs stage entry point")
+    Wq = O.nf4_dequantize(*rq, N, K)
+    rY, rT = O.qlora_forward(bits(inp["X"]), Wq, bits(inp["L1"]), bits(inp["L2"]), 0.7)
+    assert_close(bits(Ta), rT, f"decode fused T: T M={M} K={K} r={r}")
+    assert_close(bits(Ya), rY, f"decode fused T: Y M={M} K={K} r={r}")
