@@ -73,6 +73,13 @@ uint64_t next_epoch() {
   return e;
 }
 
+// Whether work issued to `s` is being captured into a graph (an error in the
+// query counts as capturing: the caller then gets the path that is safe to replay).
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+}
+
 // Polls of the decode forward's wait for its slices before a wave forms them
 // itself.  QLORA_DECODE_T_SPINS overrides it (a test sets 0 to exercise the
 // wave's own path).
@@ -454,8 +461,10 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const u
   char* ws = (char*)workspace;
   uint16_t* T = T_out ? T_out : (uint16_t*)ws;
   float* part = (float*)(ws + w.t_bytes);
-  if (qgemv_fused_ok(M, K, r) && decode_t_ok(M, K, X, L1)) {
+  if (qgemv_fused_ok(M, K, r) && decode_t_ok(M, K, X, L1) && !capturing(s)) {
     // decode, small X: the slices of T = X L1 formed, added and rounded in the decode launch itself
+    // (not under graph capture: a replay would reuse this call's epoch and could take an earlier
+    // replay's T; the two launches below are safe to replay)
     void* sync = ws + w.t_bytes + w.part_bytes;
     QL_TRY(launch_qgemv_fwd_fused(X, M, K, N, codes, c2, c1, L1, r, part, sync, next_epoch(), decode_spins(),
                                   T_out, L2, lora_scale, Y, s));

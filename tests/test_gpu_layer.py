@@ -429,3 +429,39 @@ def test_decode_fused_T_own_path_same_bits(M, K, N, r, monkeypatch):
     rY, rT = O.qlora_forward(bits(inp["X"]), Wq, bits(inp["L1"]), bits(inp["L2"]), 0.7)
     assert_close(bits(Ta), rT, f"decode fused T: T M={M} K={K} r={r}")
     assert_close(bits(Ya), rY, f"decode fused T: Y M={M} K={K} r={r}")
+
+
+def test_decode_graph_replay_follows_new_inputs():
+    """A decode forward captured once and replayed after X and L1 change in place
+    (as a serving loop does) gives the eager call's Y and T on the new inputs,
+    bit for bit, on every replay."""
+    q = qlib()
+    M, K, N, r = 1, 4096, 2000, 64
+    inp = WL.layer_inputs(N, K, M, r, seed_base=777)
+    gq, _ = quantize_both(inp["W"])
+    X, L1, L2 = (inp[k].to(DEV) for k in ("X", "L1", "L2"))
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    T = torch.empty((M, r), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty((q.qlora_linear_fwd_workspace(M, K, N, r),), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q.qlora_linear_fwd(X, *gq, N, L1, L2, 1.0, Y=Y, T_out=T, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.qlora_linear_fwd(X, *gq, N, L1, L2, 1.0, Y=Y, T_out=T, workspace=ws)
+    gen = torch.Generator().manual_seed(99)
+    for rep in range(4):
+        X.copy_(torch.randn((M, K), generator=gen).to(torch.bfloat16))
+        if rep % 2:
+            L1.copy_((torch.randn((K, r), generator=gen) / 64).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        Ye, Te = q.qlora_linear_fwd(X, *gq, N, L1, L2, 1.0, T_out=True)     # eager (one launch)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(T.view(torch.int16), Te.view(torch.int16)), rep
+        assert torch.equal(Y.view(torch.int16), Ye.view(torch.int16)), rep
+    del g
