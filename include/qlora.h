@@ -117,7 +117,18 @@ size_t qlora_linear_fwd_workspace(int64_t M, int64_t K, int64_t N, int r);
  * (N K / 2 bytes) must each stay below 2^31 bytes (split larger batches).
  * Outputs: Y [M, N] bf16; T_out [M, r] bf16 when non-NULL (keep it
  * for the backward). workspace: ws_bytes >= qlora_linear_fwd_workspace(...),
- * contents need no initialisation and are clobbered.                          */
+ * contents need no initialisation and are clobbered; calls that overlap in
+ * time must not share a workspace.
+ * Decode sizes with small X (M <= 16, 2 M K <= 32 KB, r % 4 == 0) run as ONE
+ * kernel launch that also forms T: its first work groups compute T's slices
+ * and publish them behind flags and T records tagged with a per-call epoch,
+ * which the other work groups wait for (bounded; past the bound a wave forms
+ * them itself, with the same bits). Under stream capture the call issues the
+ * two-launch form instead (T's slices, then the decode kernel), because a
+ * replayed graph would repeat the epoch; both forms give the same bits. The
+ * environment variable QLORA_DECODE_T_SPINS, read at each call, sets the
+ * bound in polls (default 4096; 0 makes waves take their own path whenever
+ * the slices are not yet there, for testing).                                  */
 int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
                      const uint8_t* codes, const uint8_t* c2, const float* c1,
                      const uint16_t* L1, const uint16_t* L2, int r, float lora_scale,
